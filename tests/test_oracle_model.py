@@ -1,0 +1,169 @@
+"""Pins for the whole-model oracle (CPU only, float64).
+
+* central finite differences along random directions of every tensor;
+* an independent torch float64 autograd model built from library routines
+  (rms_norm, scaled_dot_product_attention, cross_entropy, complex rotation);
+* causality, uniform logits, batch linearity, init-loss and ReLU² sparsity
+  invariants;
+* the page-stated depth dial and parameter count (tests/golden/depth_dial.txt).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import ops
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+TINY = oracle.derive_config(2, vocab=512, seq_len=64, d_model=128, n_heads=2, head_dim=64, d_ff=512)
+MICRO = oracle.derive_config(2, vocab=40, seq_len=8, d_model=32, n_heads=2, head_dim=16, d_ff=64)
+
+
+def make(cfg, B, seed=0, std=0.02):
+    p = synth.weights(oracle.param_shapes(cfg), seed=seed, std=std)
+    tok, tgt = synth.uniform_tokens(B, cfg.seq_len, cfg.vocab, seed=seed)
+    return {k: v.astype(np.float64) for k, v in p.items()}, tok, tgt
+
+
+# ---------------------------------------------------------------- golden: depth dial
+def read_golden(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            out[k] = float(v)
+    return out
+
+
+def test_depth_dial_and_param_count():
+    g = read_golden("depth_dial.txt")
+    for depth in (20, 26):
+        c = oracle.derive_config(depth, vocab=int(g["vocab"]))
+        assert c.d_model == depth * g["rule_d_model_per_depth"]
+        assert c.head_dim == g["rule_head_dim"]
+        assert c.n_heads * c.head_dim == c.d_model
+        assert c.d_ff == g["rule_ffn_mult"] * c.d_model
+    c20 = oracle.derive_config(20)
+    assert (c20.d_model, c20.n_heads, c20.d_ff) == (1280, 10, 5120)
+    n = oracle.param_count(c20)
+    assert n == 560_988_160
+    assert abs(n / (g["approx_params_millions"] * 1e6) - 1) < g["approx_params_rel_tol"]
+    assert 2 ** 16 == g["vocab"]
+
+
+# ---------------------------------------------------------------- finite differences
+@pytest.mark.parametrize("cfg,B", [(MICRO, 2), (TINY, 2)])
+def test_grads_central_finite_differences(cfg, B):
+    # larger weights than init so every path carries signal
+    params, tok, tgt = make(cfg, B, seed=3, std=0.2)
+    loss, grads = oracle.forward_backward(cfg, params, tok, tgt)
+    rng = np.random.default_rng(7)
+    h = 1e-5
+    for name, _ in oracle.param_shapes(cfg):
+        d = rng.standard_normal(params[name].shape)
+        if name == "E":  # only rows that occur carry gradient
+            d *= np.isin(np.arange(cfg.vocab), tok)[:, None]
+        d /= np.linalg.norm(d)
+        pp = dict(params); pm = dict(params)
+        pp[name] = params[name] + h * d
+        pm[name] = params[name] - h * d
+        fd = (oracle.forward(cfg, pp, tok, tgt) - oracle.forward(cfg, pm, tok, tgt)) / (2 * h)
+        an = float(np.sum(grads[name] * d))
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
+
+
+# ---------------------------------------------------------------- torch float64 autograd
+def torch_model_loss(cfg, P, tok, tgt):
+    """The same model written with torch library routines; autograd gives grads."""
+    B, T = tok.shape
+    H, hd = cfg.n_heads, cfg.head_dim
+    d = cfg.d_model
+    x = F.embedding(tok, P["E"])
+    theta = cfg.rope_base ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    rot = torch.polar(torch.ones(T, hd // 2, dtype=torch.float64),
+                      torch.arange(T, dtype=torch.float64)[:, None] * theta)
+
+    def rotate(u):  # u [B, H, T, hd], split-half pairs as a complex number
+        c = torch.complex(u[..., : hd // 2], u[..., hd // 2:]) * rot
+        return torch.cat([c.real, c.imag], -1)
+
+    for l in range(cfg.depth):
+        a = F.rms_norm(x, (d,), eps=cfg.eps)
+        qkv = F.linear(a, P[f"layers.{l}.W_qkv"]).view(B, T, 3, H, hd).permute(2, 0, 3, 1, 4)
+        q = rotate(F.rms_norm(qkv[0], (hd,), eps=cfg.eps))
+        k = rotate(F.rms_norm(qkv[1], (hd,), eps=cfg.eps))
+        o = F.scaled_dot_product_attention(q, k, qkv[2], is_causal=True)
+        x = x + F.linear(o.transpose(1, 2).reshape(B, T, H * hd), P[f"layers.{l}.W_o"])
+        m = F.rms_norm(x, (d,), eps=cfg.eps)
+        x = x + F.linear(F.relu(F.linear(m, P[f"layers.{l}.W_1"])).square(), P[f"layers.{l}.W_2"])
+    logits = F.linear(F.rms_norm(x, (d,), eps=cfg.eps), P["W_lm"])
+    return F.cross_entropy(logits.reshape(-1, cfg.vocab), tgt.reshape(-1))
+
+
+def test_matches_torch_float64_autograd_tiny():
+    params, tok, tgt = make(TINY, 2, seed=0)
+    loss, grads = oracle.forward_backward(TINY, params, tok, tgt)
+    P = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in params.items()}
+    lt = torch_model_loss(TINY, P, torch.from_numpy(tok).long(), torch.from_numpy(tgt).long())
+    lt.backward()
+    assert abs(loss - lt.item()) <= 1e-12 * abs(loss)
+    for k, v in grads.items():
+        ref = P[k].grad.numpy()
+        err = np.linalg.norm(v - ref) / np.linalg.norm(ref)
+        assert err <= 1e-10, (k, err)
+
+
+# ---------------------------------------------------------------- invariants
+def test_causality_bitwise():
+    params, tok, tgt = make(TINY, 1, seed=1)
+    t0 = 30
+    l1 = oracle.forward_logits(TINY, params, tok)
+    tok2 = tok.copy()
+    tok2[:, t0 + 1:] = (tok2[:, t0 + 1:] + 17) % TINY.vocab
+    l2 = oracle.forward_logits(TINY, params, tok2)
+    assert np.array_equal(l1[:, : t0 + 1], l2[:, : t0 + 1])
+    assert not np.array_equal(l1[:, t0 + 1:], l2[:, t0 + 1:])
+
+
+def test_uniform_logits_loss_is_ln_v():
+    params, tok, tgt = make(TINY, 2, seed=2)
+    params["W_lm"] = np.zeros_like(params["W_lm"])
+    assert oracle.forward(TINY, params, tok, tgt) == pytest.approx(math.log(512), abs=1e-12)
+    assert math.log(512) == pytest.approx(6.238324625039508, abs=1e-15)
+
+
+def test_batch_linearity():
+    params, tok, tgt = make(TINY, 2, seed=4)
+    loss, grads = oracle.forward_backward(TINY, params, tok, tgt)
+    l0, g0 = oracle.forward_backward(TINY, params, tok[:1], tgt[:1])
+    l1, g1 = oracle.forward_backward(TINY, params, tok[1:], tgt[1:])
+    assert loss == pytest.approx((l0 + l1) / 2, rel=1e-13)
+    for k in grads:
+        np.testing.assert_allclose(grads[k], (g0[k] + g1[k]) / 2, rtol=1e-9, atol=1e-15)
+
+
+def test_init_loss_and_relu2_sparsity():
+    params, tok, tgt = make(TINY, 2, seed=5)
+    loss = oracle.forward(TINY, params, tok, tgt)
+    sigma2 = 0.02 ** 2 * TINY.d_model  # logit variance with an rms-1 input
+    assert abs(loss - (math.log(TINY.vocab) + sigma2 / 2)) < 0.05
+    # g = relu2(u) is exactly zero for about half of the pre-activations
+    x = ops.embedding(params["E"], tok)
+    m, _ = ops.rmsnorm(x, TINY.eps)
+    g = ops.relu2(m @ params["layers.0.W_1"].T)
+    assert 0.45 < np.mean(g == 0.0) < 0.55
+
+
+def test_embedding_grad_conservation_full_model():
+    params, tok, tgt = make(TINY, 2, seed=6)
+    _, grads = oracle.forward_backward(TINY, params, tok, tgt)
+    absent = np.setdiff1d(np.arange(TINY.vocab), tok)
+    assert absent.size > 0 and np.all(grads["E"][absent] == 0.0)
