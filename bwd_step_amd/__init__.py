@@ -1,0 +1,115 @@
+"""MI355X (gfx950) training-step library: Python binding over the C ABI.
+
+The functions below only marshal arguments: torch tensors provide device
+memory and the current HIP stream, and every step of the computation runs in
+the HIP kernels of ``libnc.so`` (see include/nc.h).  Nothing here computes on
+the host, and nothing falls back to PyTorch: a missing library raises.
+"""
+
+import ctypes
+
+from . import _nc
+from ._nc import NC_BF16, NC_FP32, NcConfig, NcError, NcTensorDesc, check, lib
+
+__all__ = ["Model", "NC_BF16", "NC_FP32", "NcError", "lib", "ops"]
+
+
+def _dtype_code(dtype):
+    if dtype in ("bf16", NC_BF16):
+        return NC_BF16
+    if dtype in ("fp32", "f32", NC_FP32):
+        return NC_FP32
+    raise ValueError(f"dtype must be 'bf16' or 'fp32', got {dtype!r}")
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class Model:
+    """One nc context: configuration, parameter layout and workspace.
+
+    depth drives d_model = 64*depth, n_heads = d_model/128, head_dim = 128 and
+    d_ff = 4*d_model unless overridden.
+    """
+
+    def __init__(self, depth, vocab=65536, seq_len=2048, max_batch=1, dtype="bf16", d_model=0,
+                 n_heads=0, head_dim=0, d_ff=0, rope_base=10000.0, eps=1e-6, stream=None):
+        cfg = NcConfig(depth, d_model, n_heads, head_dim, d_ff, vocab, seq_len, max_batch,
+                       rope_base, eps, _dtype_code(dtype))
+        h = ctypes.c_void_p()
+        s = stream if stream is not None else None
+        check(lib().nc_init(ctypes.byref(cfg), s, ctypes.byref(h)), "nc_init")
+        self._h = h
+        self._ws = None
+        out = NcConfig()
+        check(lib().nc_get_config(h, ctypes.byref(out)), "nc_get_config")
+        self.config = {f: getattr(out, f) for f, _ in NcConfig._fields_}
+        self.dtype = out.dtype
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            try:
+                lib().nc_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    @property
+    def param_count(self):
+        return int(lib().nc_param_count(self._h))
+
+    def layout(self):
+        n = lib().nc_param_layout(self._h, None, 0)
+        arr = (NcTensorDesc * n)()
+        lib().nc_param_layout(self._h, arr, n)
+        return [(a.name.decode(), int(a.offset), int(a.rows), int(a.cols)) for a in arr]
+
+    def workspace_bytes(self, batch):
+        return int(lib().nc_workspace_bytes(self._h, batch))
+
+    def set_stream(self, stream=None):
+        check(lib().nc_set_stream(self._h, _stream(stream)), "nc_set_stream")
+
+    def ensure_workspace(self, batch):
+        """Allocate (with torch) a workspace large enough for `batch` sequences."""
+        import torch
+        need = self.workspace_bytes(batch)
+        if need == 0:
+            raise ValueError(f"invalid batch {batch}")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = None
+            self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            self.set_stream()
+            check(lib().nc_set_workspace(self._h, _ptr(self._ws), need), "nc_set_workspace")
+        return self._ws
+
+    def forward_backward(self, params, tokens, targets, loss, grads, accumulate=False):
+        batch = tokens.shape[0]
+        self.ensure_workspace(batch)
+        self.set_stream()
+        check(lib().nc_forward_backward(self._h, _ptr(params), _ptr(tokens), _ptr(targets), batch,
+                                        _ptr(loss), _ptr(grads), int(bool(accumulate))),
+              "nc_forward_backward")
+
+    def forward_logits(self, params, tokens, logits):
+        batch = tokens.shape[0]
+        self.ensure_workspace(batch)
+        self.set_stream()
+        check(lib().nc_forward_logits(self._h, _ptr(params), _ptr(tokens), batch, _ptr(logits)),
+              "nc_forward_logits")
+
+    def check(self):
+        """Synchronise and return the device status code (0 = ok)."""
+        return int(lib().nc_check(self._h))
+
+
+from . import ops  # noqa: E402,F401

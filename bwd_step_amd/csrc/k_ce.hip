@@ -1,0 +1,113 @@
+// Next-token softmax cross-entropy over one chunk of logits ("nanochat
+// explainer", The Full Pipeline -> Pretraining: cross-entropy between the
+// predicted logits and the actual next tokens).
+//
+// Per row n of the chunk: lse = log sum_v exp(l_nv) (max-subtracted, fp32),
+// loss_n = lse - l_{n, y_n}, and the gradient of the mean loss
+// G_nv = (exp(l_nv - lse) - [v == y_n]) / N_total, written in the GEMM
+// operand type so that dz = G W and dW = G^T z follow directly.  A
+// workgroup owns a row: pass 1 keeps a per-thread online (max, sum), merged
+// across the workgroup; pass 2 re-reads the row (now L2/MALL-resident) and
+// writes G.  The mean loss is reduced over all rows in a fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+
+__device__ __forceinline__ void online_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  m = mn;
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) ce_row_kernel(const float* __restrict__ logits, long ldl,
+                                                     const int32_t* __restrict__ tgt, T* __restrict__ G, long ldg,
+                                                     float* __restrict__ loss_rows, int V, float inv_n,
+                                                     int* __restrict__ status) {
+  const int row = blockIdx.x;
+  const float* l = logits + (size_t)row * ldl;
+  float m = -INFINITY, s = 0.f;
+  for (int c = threadIdx.x * 4; c < V; c += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(l + c);
+    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    const float mn = fmaxf(m, mx);
+    s = s * expf(m - mn) + expf(v.x - mn) + expf(v.y - mn) + expf(v.z - mn) + expf(v.w - mn);
+    m = mn;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    online_merge(m, s, m2, s2);
+  }
+  __shared__ float sm[4], ss[4];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[wv] = m; ss[wv] = s; }
+  __syncthreads();
+  m = sm[0]; s = ss[0];
+  for (int w = 1; w < 4; ++w) online_merge(m, s, sm[w], ss[w]);
+  const float lse = m + logf(s);
+  int y = tgt[row];
+  if (y < 0 || y >= V) {
+    if (threadIdx.x == 0) atomicOr(status, kStatusTokenRange);
+    y = y < 0 ? 0 : V - 1;
+  }
+  if (threadIdx.x == 0) loss_rows[row] = lse - l[y];
+  T* gr = G + (size_t)row * ldg;
+  for (int c = threadIdx.x * 4; c < V; c += 1024) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(l + c);
+    float g0 = expf(v.x - lse), g1 = expf(v.y - lse), g2 = expf(v.z - lse), g3 = expf(v.w - lse);
+    if (y >= c && y < c + 4) {
+      const int q = y - c;
+      g0 -= q == 0; g1 -= q == 1; g2 -= q == 2; g3 -= q == 3;
+    }
+    if constexpr (sizeof(T) == 2) {
+      u32x2 w;
+      w.x = pack_bf16x2(g0 * inv_n, g1 * inv_n);
+      w.y = pack_bf16x2(g2 * inv_n, g3 * inv_n);
+      *reinterpret_cast<u32x2*>(gr + c) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(gr + c) = f32x4{g0 * inv_n, g1 * inv_n, g2 * inv_n, g3 * inv_n};
+    }
+  }
+}
+
+int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
+                   int V, int n_total, int dtype, int* status, hipStream_t s) {
+  if (rows == 0) return 0;
+  const float inv_n = 1.0f / (float)n_total;
+  if (dtype == 0)
+    ce_row_kernel<bf16><<<rows, 256, 0, s>>>(logits, ldl, tgt, (bf16*)G, ldg, loss_rows, V, inv_n, status);
+  else
+    ce_row_kernel<float><<<rows, 256, 0, s>>>(logits, ldl, tgt, (float*)G, ldg, loss_rows, V, inv_n, status);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+// Mean of n values in a fixed order (one workgroup), non-finite -> status.
+__global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ v, int n, float* __restrict__ out,
+                                                    int* __restrict__ status) {
+  __shared__ double part[1024];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 1024) s += (double)v[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 512; off >= 1; off >>= 1) {
+    if ((int)threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float r = n > 0 ? (float)(part[0] / n) : 0.f;
+    *out = r;
+    if (!isfinite(r)) atomicOr(status, kStatusNonFinite);
+  }
+}
+
+int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s) {
+  mean_kernel<<<1, 1024, 0, s>>>(v, n, out, status);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+}  // namespace nc

@@ -1,0 +1,296 @@
+// RMSNorm and QK-norm + RoPE kernels (forward and backward).
+//
+// RMSNorm, parameter-free ("nanochat explainer", Modern architecture
+// choices): y = x * r with r = 1/sqrt(mean(x^2) + eps); backward
+// dx = r * (dy - y * mean(dy * y)).  One wavefront per row; the row's sum of
+// squares is a wavefront butterfly reduction; statistics stay in fp32.
+//
+// QK-norm then RoPE ("nanochat explainer", Modern architecture choices;
+// Architecture Choices -> RoPE Intuition): each head vector u of length hd is
+// RMS-normalised and element i is paired with i + hd/2 and rotated by
+// t * base^(-2i/hd), t being the position inside the sequence.  A lane owns
+// one (i, i + hd/2) pair, so the rotation needs no data exchange and the norm
+// is a reduction over hd/2 lanes.
+#include "common.h"
+#include "kernels.h"
+
+namespace nc {
+
+// --------------------------------------------------------------- RMSNorm
+template <class T>
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                          float* __restrict__ r, int N, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)row * d);
+  const int nc4 = d >> 2;
+  float ss = 0.f;
+  for (int c = lane; c < nc4; c += 64) {
+    f32x4 v = xr[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / (float)d + eps);
+  if (lane == 0) r[row] = rr;
+  T* yr = y + (size_t)row * d;
+  for (int c = lane; c < nc4; c += 64) {
+    f32x4 v = xr[c];
+    if constexpr (sizeof(T) == 2) {
+      u32x2 w;
+      w.x = pack_bf16x2(v.x * rr, v.y * rr);
+      w.y = pack_bf16x2(v.z * rr, v.w * rr);
+      *reinterpret_cast<u32x2*>(yr + 4 * c) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(yr + 4 * c) = v * rr;
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ f32x4 load4(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2 w;
+    w.x = pack_bf16x2(v.x, v.y);
+    w.y = pack_bf16x2(v.z, v.w);
+    *reinterpret_cast<u32x2*>(p) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+                                                          const float* __restrict__ r, float* __restrict__ dx,
+                                                          T* __restrict__ dx_lp, int N, int d, int accumulate) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const size_t base = (size_t)row * d;
+  const int nc4 = d >> 2;
+  float dot = 0.f;
+  for (int c = lane; c < nc4; c += 64) {
+    f32x4 g = *reinterpret_cast<const f32x4*>(dy + base + 4 * c);
+    f32x4 v = load4(y + base + 4 * c);
+    dot += g.x * v.x + g.y * v.y + g.z * v.z + g.w * v.w;
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float rr = r[row];
+  for (int c = lane; c < nc4; c += 64) {
+    f32x4 g = *reinterpret_cast<const f32x4*>(dy + base + 4 * c);
+    f32x4 v = load4(y + base + 4 * c);
+    f32x4 o = (g - v * dot) * rr;
+    f32x4* dp = reinterpret_cast<f32x4*>(dx + base + 4 * c);
+    if (accumulate) o += *dp;
+    *dp = o;
+    if (dx_lp) store4(dx_lp + base + 4 * c, o);
+  }
+}
+
+template <class T>
+int rmsnorm_fwd_t(const float* x, void* y, float* r, int N, int d, float eps, hipStream_t s) {
+  if (N == 0) return 0;
+  rmsnorm_fwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(x, (T*)y, r, N, d, eps);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, hipStream_t s) {
+  return dtype == 0 ? rmsnorm_fwd_t<bf16>(x, y, r, N, d, eps, s) : rmsnorm_fwd_t<float>(x, y, r, N, d, eps, s);
+}
+
+template <class T>
+int rmsnorm_bwd_t(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d, int acc,
+                  hipStream_t s) {
+  if (N == 0) return 0;
+  rmsnorm_bwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(dy, (const T*)y, r, dx, (T*)dx_lp, N, d, acc);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
+                       int accumulate, int dtype, hipStream_t s) {
+  return dtype == 0 ? rmsnorm_bwd_t<bf16>(dy, y, r, dx, dx_lp, N, d, accumulate, s)
+                    : rmsnorm_bwd_t<float>(dy, y, r, dx, dx_lp, N, d, accumulate, s);
+}
+
+// --------------------------------------------------------------- RoPE table
+// cos/sin of t * base^(-2i/hd) for t < T, i < hd/2, evaluated in double so
+// that large angles (t up to thousands of radians) keep full fp32 accuracy.
+__global__ void rope_table_kernel(float* __restrict__ cs, int T, int half, double log2_base, int hd) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int t = idx / half, i = idx - t * half;
+  const double theta = exp2(-(2.0 * i / hd) * log2_base);
+  double sn, c;
+  sincos((double)t * theta, &sn, &c);
+  cs[2 * idx] = (float)c;
+  cs[2 * idx + 1] = (float)sn;
+}
+
+int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s) {
+  const int half = hd / 2;
+  const int n = T * half;
+  if (n == 0) return 0;
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(cs, T, half, log2((double)base), hd);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+// --------------------------------------------------------------- QK-norm + RoPE
+// Vectors are (token n, head h) of one tensor; `which` (blockIdx.y) selects
+// the q or the k tensor.  Element (n, h, e) of tensor w lives at
+// ptr[w][n * ld[w] + h * hd + e].
+struct QkArgs {
+  const void* in[2];
+  void* out[2];
+  int ld_in[2];
+  int ld_out[2];
+  float* r[2];  // [N, H]
+};
+
+template <class T, int HALF>
+__global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(QkArgs a, const float* __restrict__ cs, int N, int H,
+                                                              int Tseq, float eps) {
+  constexpr int VPW = 64 / HALF;  // vectors per wavefront
+  const int w = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / HALF;
+  const int i = lane % HALF;
+  const bool ok = vec < N * H;
+  const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
+  const T* src = (const T*)a.in[w] + (size_t)n * a.ld_in[w] + h * (2 * HALF);
+  float u0 = ok ? to_f32(src[i]) : 0.f, u1 = ok ? to_f32(src[i + HALF]) : 0.f;
+  float ss = u0 * u0 + u1 * u1;
+#pragma unroll
+  for (int o = HALF / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float rr = 1.0f / sqrtf(ss / (float)(2 * HALF) + eps);
+  if (!ok) return;
+  const int t = n % Tseq;
+  const float c = cs[2 * (t * HALF + i)], sn = cs[2 * (t * HALF + i) + 1];
+  const float y0 = u0 * rr, y1 = u1 * rr;
+  T* dst = (T*)a.out[w] + (size_t)n * a.ld_out[w] + h * (2 * HALF);
+  dst[i] = from_f32<T>(y0 * c - y1 * sn);
+  dst[i + HALF] = from_f32<T>(y0 * sn + y1 * c);
+  if (i == 0) a.r[w][vec] = rr;
+}
+
+// Backward: dv (fp32, gradient w.r.t. the rotated normalised vector), v the
+// saved rotated normalised vector, r its saved 1/rms.  du = r (dy - y mean(dy y))
+// with dy = R^T dv and y = R^T v.
+struct QkBwdArgs {
+  const float* dv[2];
+  int ld_dv[2];
+  const void* v[2];
+  int ld_v[2];
+  const float* r[2];
+  void* du[2];
+  int ld_du[2];
+};
+
+template <class T, int HALF>
+__global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const float* __restrict__ cs, int N,
+                                                              int H, int Tseq) {
+  constexpr int VPW = 64 / HALF;
+  const int w = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / HALF;
+  const int i = lane % HALF;
+  const bool ok = vec < N * H;
+  const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
+  const int t = n % Tseq;
+  const float c = cs[2 * (t * HALF + i)], sn = cs[2 * (t * HALF + i) + 1];
+  const float* g = a.dv[w] + (size_t)n * a.ld_dv[w] + h * (2 * HALF);
+  const T* vv = (const T*)a.v[w] + (size_t)n * a.ld_v[w] + h * (2 * HALF);
+  float g0 = ok ? g[i] : 0.f, g1 = ok ? g[i + HALF] : 0.f;
+  float v0 = ok ? to_f32(vv[i]) : 0.f, v1 = ok ? to_f32(vv[i + HALF]) : 0.f;
+  // R^T: rotation by -phi
+  const float dy0 = g0 * c + g1 * sn, dy1 = -g0 * sn + g1 * c;
+  const float y0 = v0 * c + v1 * sn, y1 = -v0 * sn + v1 * c;
+  float dot = dy0 * y0 + dy1 * y1;
+#pragma unroll
+  for (int o = HALF / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+  dot /= (float)(2 * HALF);
+  if (!ok) return;
+  const float rr = a.r[w][vec];
+  T* out = (T*)a.du[w] + (size_t)n * a.ld_du[w] + h * (2 * HALF);
+  out[i] = from_f32<T>(rr * (dy0 - y0 * dot));
+  out[i + HALF] = from_f32<T>(rr * (dy1 - y1 * dot));
+}
+
+template <class T>
+static int qk_fwd_dispatch(const QkArgs& a, const float* cs, int N, int H, int hd, int Tseq, float eps,
+                           hipStream_t s) {
+  const int vecs = N * H;
+  if (vecs == 0) return 0;
+  const int half = hd / 2;
+  const int vpb = 4 * (64 / half);
+  dim3 grid((vecs + vpb - 1) / vpb, 2);
+  switch (half) {
+    case 64: qknorm_rope_fwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, eps); break;
+    case 32: qknorm_rope_fwd_kernel<T, 32><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, eps); break;
+    case 16: qknorm_rope_fwd_kernel<T, 16><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, eps); break;
+    case 8: qknorm_rope_fwd_kernel<T, 8><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, eps); break;
+    default: return 7;
+  }
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+template <class T>
+static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, int hd, int Tseq, hipStream_t s) {
+  const int vecs = N * H;
+  if (vecs == 0) return 0;
+  const int half = hd / 2;
+  const int vpb = 4 * (64 / half);
+  dim3 grid((vecs + vpb - 1) / vpb, 2);
+  switch (half) {
+    case 64: qknorm_rope_bwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
+    case 32: qknorm_rope_bwd_kernel<T, 32><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
+    case 16: qknorm_rope_bwd_kernel<T, 16><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
+    case 8: qknorm_rope_bwd_kernel<T, 8><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
+    default: return 7;
+  }
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
+                           void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
+                           int T, float eps, int dtype, hipStream_t s) {
+  QkArgs a;
+  a.in[0] = q_in; a.in[1] = k_in;
+  a.out[0] = q_out; a.out[1] = k_out;
+  a.ld_in[0] = ldq_in; a.ld_in[1] = ldk_in;
+  a.ld_out[0] = ldq_out; a.ld_out[1] = ldk_out;
+  a.r[0] = rq; a.r[1] = rk;
+  return dtype == 0 ? qk_fwd_dispatch<bf16>(a, cs, N, H, hd, T, eps, s)
+                    : qk_fwd_dispatch<float>(a, cs, N, H, hd, T, eps, s);
+}
+
+int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
+                           const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
+                           void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
+                           hipStream_t s) {
+  QkBwdArgs a;
+  a.dv[0] = dq; a.dv[1] = dk;
+  a.ld_dv[0] = lddq; a.ld_dv[1] = lddk;
+  a.v[0] = qh; a.v[1] = kh;
+  a.ld_v[0] = ldq; a.ld_v[1] = ldk;
+  a.r[0] = rq; a.r[1] = rk;
+  a.du[0] = dq_out; a.du[1] = dk_out;
+  a.ld_du[0] = ldq_out; a.ld_du[1] = ldk_out;
+  return dtype == 0 ? qk_bwd_dispatch<bf16>(a, cs, N, H, hd, T, s) : qk_bwd_dispatch<float>(a, cs, N, H, hd, T, s);
+}
+
+}  // namespace nc

@@ -1,0 +1,86 @@
+// Internal launch API between the host runtime (nc.cpp) and the kernels.
+// Every launcher enqueues on stream `s` and returns 0 or an nc_status code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nc {
+
+// ---- GEMM epilogues
+enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4 };
+
+struct EpiArgs {
+  float* c32 = nullptr;  // EPI_F32 (beta selects store / accumulate), EPI_RESID
+  long ldc = 0;
+  int beta = 0;
+  long split_stride = 0;    // elements between split-K partial slices
+  void* c_lp = nullptr;     // EPI_LP / EPI_RELU2 (u) / EPI_DRELU2 (du)
+  void* c_lp2 = nullptr;    // EPI_RELU2 (g)
+  long ld_lp = 0;
+  const void* aux = nullptr;  // EPI_DRELU2: u
+  long ld_aux = 0;
+};
+
+struct GemmCall {
+  const void* A = nullptr;
+  long lda = 0;
+  bool a_k = true;
+  const void* B = nullptr;
+  long ldb = 0;
+  bool b_k = true;
+  int M = 0, N = 0, K = 0;
+  int epi = EPI_F32;
+  EpiArgs e;
+  int dtype = 0;
+  float* splitk_ws = nullptr;  // fp32 partials for split-K (EPI_F32 only); may be null
+};
+
+int launch_gemm(const GemmCall& g, hipStream_t s);
+int gemm_splits(int M, int N, int K, int dtype);
+uint64_t gemm_ws_bytes(int M, int N, int K, int dtype);
+
+// ---- norms
+int launch_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, hipStream_t s);
+int launch_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
+                       int accumulate, int dtype, hipStream_t s);
+int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s);
+int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
+                           void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
+                           int T, float eps, int dtype, hipStream_t s);
+int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
+                           const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
+                           void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
+                           hipStream_t s);
+
+// ---- embedding
+int launch_embed_fwd(const void* E, const int32_t* tok, float* x, int N, int d, int V, int dtype, int* status,
+                     hipStream_t s);
+uint64_t embed_bwd_ws_bytes(int N, int d, int V);
+int launch_embed_bwd(const float* dx, const int32_t* tok, float* dE, int N, int d, int V, int accumulate, void* ws,
+                     hipStream_t s);
+
+// ---- attention.  Element (b, t, h, e) of tensor X is X[(b*T + t) * ldX + h*hd + e].
+struct AttnArgs {
+  const void* q = nullptr; long ldq = 0;
+  const void* k = nullptr; long ldk = 0;
+  const void* v = nullptr; long ldv = 0;
+  void* o = nullptr; long ldo = 0;          // forward output (read by the backward)
+  const void* dout = nullptr; long lddo = 0;
+  float* lse = nullptr;                     // [B*H][T], natural log
+  float* Dbuf = nullptr;                    // [B*H][T]
+  float* dq32 = nullptr; long lddq = 0;     // fp32 grads w.r.t. the rotated q, k
+  float* dk32 = nullptr; long lddk = 0;
+  void* dv = nullptr; long lddv = 0;        // grad w.r.t. v, element type
+  int B = 0, H = 0, T = 0;
+  float scale = 0.f, scale_log2 = 0.f;      // set by the launchers
+};
+int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s);
+int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s);
+
+// ---- cross-entropy
+int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
+                   int V, int n_total, int dtype, int* status, hipStream_t s);
+int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s);
+
+}  // namespace nc

@@ -1,0 +1,630 @@
+// Host runtime behind include/nc.h: configuration and depth dial, flat
+// parameter layout, workspace plan, and the forward/backward launch schedule
+// of one training step.  No device memory is allocated here; every buffer is
+// a slice of the caller's workspace.
+//
+// Model ("nanochat explainer", Modern architecture choices; The 'One Dial'
+// Design -> How dimensions are derived; The Full Pipeline -> Pretraining):
+//   x = E[tok]; per layer: a = rho(x); qkv = a W_qkv^T; qh, kh = RoPE(rho_hd(q, k));
+//   o = causal attention; x += o W_o^T; m = rho(x); u = m W_1^T; g = relu(u)^2;
+//   x += g W_2^T;  finally z = rho(x), logits = z W_lm^T, mean cross-entropy.
+// Residual stream and every gradient are fp32; GEMM operands and saved
+// activations use the configured element type.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/nc.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace nc;
+
+namespace {
+
+constexpr int kCeChunk = 8192;  // tokens per LM-head chunk
+
+inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Desc {
+  std::string name;
+  uint64_t offset;
+  int rows, cols;
+};
+
+struct Plan {
+  int batch = 0;
+  size_t status = 0;
+  // per-layer saved activations: offsets inside layer 0, plus the layer stride
+  size_t a1, r1, qkv, rq, rk, O, lse, m, r2, u, g, layer_stride;
+  size_t layers_base;
+  // step-global buffers
+  size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, Dbuf, rope, logits, G, loss_rows, splitk, embed_ws;
+  size_t total;
+};
+
+}  // namespace
+
+struct nc_ctx {
+  nc_config cfg;
+  hipStream_t stream;
+  std::vector<Desc> layout;
+  uint64_t nparams;
+  char* ws = nullptr;
+  uint64_t ws_bytes = 0;
+};
+
+namespace {
+
+int validate(nc_config* c) {
+  if (c->depth < 1) return NC_ERR_CONFIG;
+  if (c->d_model == 0) c->d_model = 64 * c->depth;
+  if (c->head_dim == 0) c->head_dim = 128;
+  if (c->n_heads == 0) c->n_heads = c->d_model / c->head_dim;
+  if (c->d_ff == 0) c->d_ff = 4 * c->d_model;
+  if (c->rope_base == 0.f) c->rope_base = 10000.f;
+  if (c->norm_eps == 0.f) c->norm_eps = 1e-6f;
+  if (c->d_model <= 0 || c->d_model % 64) return NC_ERR_CONFIG;
+  if (c->d_ff <= 0 || c->d_ff % 64) return NC_ERR_CONFIG;
+  if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return NC_ERR_CONFIG;
+  if (c->n_heads < 1) return NC_ERR_CONFIG;
+  if (c->vocab < 64 || c->vocab % 64) return NC_ERR_CONFIG;
+  if (c->seq_len < 1 || c->max_batch < 1) return NC_ERR_CONFIG;
+  if (!(c->rope_base > 1.f) || !(c->norm_eps > 0.f)) return NC_ERR_CONFIG;
+  if (c->dtype != NC_BF16 && c->dtype != NC_FP32) return NC_ERR_CONFIG;
+  if ((uint64_t)c->max_batch * c->seq_len > (1ull << 30)) return NC_ERR_CONFIG;
+  if (c->dtype == NC_BF16 && c->head_dim != 64 && c->head_dim != 128) return NC_ERR_UNSUPPORTED;
+  return NC_OK;
+}
+
+Plan make_plan(const nc_config& c, int batch) {
+  Plan p;
+  p.batch = batch;
+  const size_t N = (size_t)batch * c.seq_len;
+  const size_t d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff, V = c.vocab, H = c.n_heads;
+  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o += al(bytes); return r; };
+  p.status = take(256);
+  p.x = take(N * d * 4);
+  p.z = take(N * d * es);
+  p.rf = take(N * 4);
+  p.dx = take(N * d * 4);
+  p.dx_lp = take(N * d * es);
+  p.tmp_d = take(N * d * 4);
+  p.du = take(N * F * es);
+  p.dO = take(N * hh * es);
+  p.dqkv = take(N * 3 * hh * es);
+  p.dqk32 = take(N * 2 * hh * 4);
+  p.Dbuf = take(N * H * 4);
+  p.rope = take((size_t)c.seq_len * c.head_dim * 4);
+  const size_t chunk = std::min<size_t>(N, kCeChunk);
+  p.logits = take(chunk * V * 4);
+  p.G = take(chunk * V * es);
+  p.loss_rows = take(N * 4);
+  uint64_t sk = 0;
+  const int n = (int)N;
+  sk = std::max(sk, gemm_ws_bytes(3 * (int)hh, (int)d, n, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)d, (int)hh, n, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)F, (int)d, n, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)d, (int)F, n, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)chunk, (int)d, (int)V, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)V, (int)d, (int)chunk, c.dtype));
+  p.splitk = take(sk);
+  p.embed_ws = take(embed_bwd_ws_bytes(n, (int)d, (int)V));
+  // per-layer saved activations
+  p.layers_base = o;
+  size_t lo = 0;
+  auto ltake = [&](size_t bytes) { size_t r = lo; lo += al(bytes); return r; };
+  p.a1 = ltake(N * d * es);
+  p.r1 = ltake(N * 4);
+  p.qkv = ltake(N * 3 * hh * es);
+  p.rq = ltake(N * H * 4);
+  p.rk = ltake(N * H * 4);
+  p.O = ltake(N * hh * es);
+  p.lse = ltake(N * H * 4);
+  p.m = ltake(N * d * es);
+  p.r2 = ltake(N * 4);
+  p.u = ltake(N * F * es);
+  p.g = ltake(N * F * es);
+  p.layer_stride = lo;
+  o += lo * c.depth;
+  p.total = o;
+  return p;
+}
+
+void build_layout(nc_ctx* x) {
+  const nc_config& c = x->cfg;
+  const uint64_t d = c.d_model, hh = (uint64_t)c.n_heads * c.head_dim, F = c.d_ff, V = c.vocab;
+  uint64_t off = 0;
+  auto add = [&](const std::string& n, uint64_t r, uint64_t cl) {
+    x->layout.push_back({n, off, (int)r, (int)cl});
+    off += r * cl;
+  };
+  add("E", V, d);
+  for (int l = 0; l < c.depth; ++l) {
+    const std::string p = "layers." + std::to_string(l) + ".";
+    add(p + "W_qkv", 3 * hh, d);
+    add(p + "W_o", d, hh);
+    add(p + "W_1", F, d);
+    add(p + "W_2", d, F);
+  }
+  add("W_lm", V, d);
+  x->nparams = off;
+}
+
+__global__ void clear_status_kernel(int* s) { *s = 0; }
+
+int clear_status(void* ws, hipStream_t s) {
+  clear_status_kernel<<<1, 1, 0, s>>>((int*)ws);
+  return hipGetLastError() == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+
+int read_status(void* ws, hipStream_t s) {
+  int v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return NC_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return NC_ERR_HIP;
+  if (clear_status(ws, s) != NC_OK) return NC_ERR_HIP;
+  if (v & nc::kStatusTokenRange) return NC_ERR_TOKEN_RANGE;
+  if (v & nc::kStatusNonFinite) return NC_ERR_NONFINITE;
+  return NC_OK;
+}
+
+#define TRY(x)                   \
+  do {                           \
+    int rc_ = (x);               \
+    if (rc_) return rc_;         \
+  } while (0)
+
+GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, int M, int N, int K, int dtype) {
+  GemmCall g;
+  g.A = A; g.lda = lda; g.a_k = ak;
+  g.B = B; g.ldb = ldb; g.b_k = bk;
+  g.M = M; g.N = N; g.K = K;
+  g.dtype = dtype;
+  return g;
+}
+
+// LM head + cross-entropy over tokens in chunks: loss_rows, dz (fp32, [N,d]),
+// dW (fp32 [V,d]; overwritten or accumulated).  G and logits are chunk-sized.
+int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss_rows, float* dz,
+              float* dW, int accumulate, int dtype, float* logits, void* G, float* splitk, int* status, hipStream_t s) {
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  for (int c0 = 0; c0 < N; c0 += kCeChunk) {
+    const int rows = std::min(kCeChunk, N - c0);
+    const char* zc = (const char*)z + (size_t)c0 * d * es;
+    GemmCall lg = mk(zc, d, true, W, d, true, rows, V, d, dtype);
+    lg.epi = EPI_F32; lg.e.c32 = logits; lg.e.ldc = V; lg.e.beta = 0;
+    TRY(launch_gemm(lg, s));
+    TRY(launch_ce_rows(logits, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
+    GemmCall gw = mk(G, V, false, zc, d, false, V, d, rows, dtype);
+    gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
+    gw.splitk_ws = splitk;
+    TRY(launch_gemm(gw, s));
+    GemmCall gz = mk(G, V, true, W, d, false, rows, d, V, dtype);
+    gz.epi = EPI_F32; gz.e.c32 = dz + (size_t)c0 * d; gz.e.ldc = d; gz.e.beta = 0;
+    gz.splitk_ws = splitk;
+    TRY(launch_gemm(gz, s));
+  }
+  return NC_OK;
+}
+
+int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* tokens, int batch) {
+  const nc_config& c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  char* W = ctx->ws;
+  const int N = batch * c.seq_len, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
+  const int V = c.vocab, dt = c.dtype;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  const char* prm = (const char*)params;
+  int* status = (int*)(W + P.status);
+  float* x = (float*)(W + P.x);
+  float* cs = (float*)(W + P.rope);
+
+  TRY(launch_embed_fwd(prm, tokens, x, N, d, V, dt, status, s));
+  TRY(launch_rope_table(cs, c.seq_len, hd, c.rope_base, s));
+  for (int l = 0; l < c.depth; ++l) {
+    char* L = W + P.layers_base + (size_t)l * P.layer_stride;
+    const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
+    const char* Wo = prm + ctx->layout[2 + 4 * l].offset * es;
+    const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
+    const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
+    void* a1 = L + P.a1;
+    char* qkv = L + P.qkv;
+    TRY(launch_rmsnorm_fwd(x, a1, (float*)(L + P.r1), N, d, c.norm_eps, dt, s));
+    GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, 3 * hh, d, dt);
+    g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
+    TRY(launch_gemm(g1, s));
+    TRY(launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
+                               (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, c.seq_len, c.norm_eps, dt, s));
+    AttnArgs a;
+    a.q = qkv; a.ldq = 3 * hh;
+    a.k = qkv + hh * es; a.ldk = 3 * hh;
+    a.v = qkv + 2 * hh * es; a.ldv = 3 * hh;
+    a.o = L + P.O; a.ldo = hh;
+    a.lse = (float*)(L + P.lse);
+    a.B = batch; a.H = H; a.T = c.seq_len;
+    TRY(launch_attn_fwd(a, hd, dt, s));
+    GemmCall g2 = mk(L + P.O, hh, true, Wo, hh, true, N, d, hh, dt);
+    g2.epi = EPI_RESID; g2.e.c32 = x; g2.e.ldc = d;
+    TRY(launch_gemm(g2, s));
+    TRY(launch_rmsnorm_fwd(x, L + P.m, (float*)(L + P.r2), N, d, c.norm_eps, dt, s));
+    GemmCall g3 = mk(L + P.m, d, true, W1, d, true, N, F, d, dt);
+    g3.epi = EPI_RELU2; g3.e.c_lp = L + P.u; g3.e.c_lp2 = L + P.g; g3.e.ld_lp = F;
+    TRY(launch_gemm(g3, s));
+    GemmCall g4 = mk(L + P.g, F, true, W2, F, true, N, d, F, dt);
+    g4.epi = EPI_RESID; g4.e.c32 = x; g4.e.ldc = d;
+    TRY(launch_gemm(g4, s));
+  }
+  TRY(launch_rmsnorm_fwd(x, W + P.z, (float*)(W + P.rf), N, d, c.norm_eps, dt, s));
+  return NC_OK;
+}
+
+int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* tokens, const int32_t* targets,
+                 int batch, float* loss, float* grads, int accumulate) {
+  const nc_config& c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  char* W = ctx->ws;
+  const int N = batch * c.seq_len, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
+  const int V = c.vocab, dt = c.dtype;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  const char* prm = (const char*)params;
+  int* status = (int*)(W + P.status);
+  float* dx = (float*)(W + P.dx);
+  void* dx_lp = W + P.dx_lp;
+  float* tmp = (float*)(W + P.tmp_d);
+  float* splitk = P.splitk ? (float*)(W + P.splitk) : nullptr;
+  float* cs = (float*)(W + P.rope);
+  const Desc& lm = ctx->layout.back();
+
+  TRY(lmhead_ce(W + P.z, prm + lm.offset * es, targets, N, d, V, (float*)(W + P.loss_rows), tmp,
+                grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, status, s));
+  TRY(launch_mean((float*)(W + P.loss_rows), N, loss, status, s));
+  TRY(launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
+
+  for (int l = c.depth - 1; l >= 0; --l) {
+    char* L = W + P.layers_base + (size_t)l * P.layer_stride;
+    const Desc& dqkv_d = ctx->layout[1 + 4 * l];
+    const Desc& do_d = ctx->layout[2 + 4 * l];
+    const Desc& d1_d = ctx->layout[3 + 4 * l];
+    const Desc& d2_d = ctx->layout[4 + 4 * l];
+    const char* Wqkv = prm + dqkv_d.offset * es;
+    const char* Wo = prm + do_d.offset * es;
+    const char* W1 = prm + d1_d.offset * es;
+    const char* W2 = prm + d2_d.offset * es;
+    const int beta = accumulate ? 1 : 0;
+    char* qkv = L + P.qkv;
+    char* dqkv = W + P.dqkv;
+    float* dqk32 = (float*)(W + P.dqk32);
+
+    // MLP: du = (dx W_2) * 2 relu(u); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
+    GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
+    b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.u; b1.e.ld_aux = F;
+    TRY(launch_gemm(b1, s));
+    GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
+    b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk;
+    TRY(launch_gemm(b2, s));
+    GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
+    b3.epi = EPI_F32; b3.e.c32 = tmp; b3.e.ldc = d;
+    TRY(launch_gemm(b3, s));
+    GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
+    b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk;
+    TRY(launch_gemm(b4, s));
+    TRY(launch_rmsnorm_bwd(tmp, L + P.m, (float*)(L + P.r2), dx, dx_lp, N, d, 1, dt, s));
+
+    // attention output projection: dO = dx W_o; dW_o = dx^T O
+    GemmCall b5 = mk(dx_lp, d, true, Wo, hh, false, N, hh, d, dt);
+    b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
+    TRY(launch_gemm(b5, s));
+    GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
+    b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk;
+    TRY(launch_gemm(b6, s));
+
+    AttnArgs a;
+    a.q = qkv; a.ldq = 3 * hh;
+    a.k = qkv + hh * es; a.ldk = 3 * hh;
+    a.v = qkv + 2 * hh * es; a.ldv = 3 * hh;
+    a.o = L + P.O; a.ldo = hh;
+    a.dout = W + P.dO; a.lddo = hh;
+    a.lse = (float*)(L + P.lse);
+    a.Dbuf = (float*)(W + P.Dbuf);
+    a.dq32 = dqk32; a.lddq = 2 * hh;
+    a.dk32 = dqk32 + hh; a.lddk = 2 * hh;
+    a.dv = dqkv + 2 * hh * es; a.lddv = 3 * hh;
+    a.B = batch; a.H = H; a.T = c.seq_len;
+    TRY(launch_attn_bwd(a, hd, dt, s));
+    TRY(launch_qknorm_rope_bwd(dqk32, 2 * hh, dqk32 + hh, 2 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
+                               (float*)(L + P.rq), (float*)(L + P.rk), dqkv, 3 * hh, dqkv + hh * es, 3 * hh, cs, N, H,
+                               hd, c.seq_len, dt, s));
+
+    // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
+    GemmCall b7 = mk(dqkv, 3 * hh, true, Wqkv, d, false, N, d, 3 * hh, dt);
+    b7.epi = EPI_F32; b7.e.c32 = tmp; b7.e.ldc = d;
+    TRY(launch_gemm(b7, s));
+    GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
+    b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk;
+    TRY(launch_gemm(b8, s));
+    TRY(launch_rmsnorm_bwd(tmp, L + P.a1, (float*)(L + P.r1), dx, dx_lp, N, d, 1, dt, s));
+  }
+  TRY(launch_embed_bwd(dx, tokens, grads, N, d, V, accumulate, W + P.embed_ws, s));
+  return NC_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* nc_strerror(int st) {
+  switch (st) {
+    case NC_OK: return "ok";
+    case NC_ERR_CONFIG: return "invalid configuration";
+    case NC_ERR_NULL: return "null pointer argument";
+    case NC_ERR_WORKSPACE: return "workspace missing or too small";
+    case NC_ERR_TOKEN_RANGE: return "token or target id outside [0, vocab)";
+    case NC_ERR_NONFINITE: return "non-finite loss";
+    case NC_ERR_HIP: return "HIP runtime error";
+    case NC_ERR_UNSUPPORTED: return "unsupported shape for the GPU kernels";
+    case NC_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int nc_init(const nc_config* cfg, void* stream, nc_ctx** out) {
+  if (!cfg || !out) return NC_ERR_NULL;
+  *out = nullptr;
+  nc_config c = *cfg;
+  const int rc = validate(&c);
+  if (rc) return rc;
+  nc_ctx* x = new nc_ctx();
+  x->cfg = c;
+  x->stream = (hipStream_t)stream;
+  build_layout(x);
+  *out = x;
+  return NC_OK;
+}
+
+void nc_destroy(nc_ctx* ctx) { delete ctx; }
+
+int nc_get_config(const nc_ctx* ctx, nc_config* out) {
+  if (!ctx || !out) return NC_ERR_NULL;
+  *out = ctx->cfg;
+  return NC_OK;
+}
+
+int nc_set_stream(nc_ctx* ctx, void* stream) {
+  if (!ctx) return NC_ERR_NULL;
+  ctx->stream = (hipStream_t)stream;
+  return NC_OK;
+}
+
+uint64_t nc_param_count(const nc_ctx* ctx) { return ctx ? ctx->nparams : 0; }
+
+int nc_param_layout(const nc_ctx* ctx, nc_tensor_desc* out, int cap) {
+  if (!ctx) return -NC_ERR_NULL;
+  const int n = (int)ctx->layout.size();
+  for (int i = 0; i < n && i < cap && out; ++i) {
+    memset(&out[i], 0, sizeof(nc_tensor_desc));
+    strncpy(out[i].name, ctx->layout[i].name.c_str(), sizeof(out[i].name) - 1);
+    out[i].offset = ctx->layout[i].offset;
+    out[i].rows = ctx->layout[i].rows;
+    out[i].cols = ctx->layout[i].cols;
+  }
+  return n;
+}
+
+uint64_t nc_workspace_bytes(const nc_ctx* ctx, int batch) {
+  if (!ctx || batch < 1 || batch > ctx->cfg.max_batch) return 0;
+  return make_plan(ctx->cfg, batch).total;
+}
+
+int nc_set_workspace(nc_ctx* ctx, void* dev_ptr, uint64_t bytes) {
+  if (!ctx || !dev_ptr) return NC_ERR_NULL;
+  if ((uintptr_t)dev_ptr & 255) return NC_ERR_ARG;
+  ctx->ws = (char*)dev_ptr;
+  ctx->ws_bytes = bytes;
+  return clear_status(dev_ptr, ctx->stream);
+}
+
+int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* targets, int batch,
+                        float* loss, float* grads, int accumulate) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !targets || !loss || !grads) return NC_ERR_NULL;
+  if (batch < 1 || batch > ctx->cfg.max_batch || (accumulate != 0 && accumulate != 1)) return NC_ERR_ARG;
+  if (!ctx->ws) return NC_ERR_WORKSPACE;
+  const Plan P = make_plan(ctx->cfg, batch);
+  if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  TRY(run_forward(ctx, P, params, tokens, batch));
+  return run_backward(ctx, P, params, tokens, targets, batch, loss, grads, accumulate);
+}
+
+int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, int batch, float* logits) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !logits) return NC_ERR_NULL;
+  if (batch < 1 || batch > ctx->cfg.max_batch) return NC_ERR_ARG;
+  if (!ctx->ws) return NC_ERR_WORKSPACE;
+  const Plan P = make_plan(ctx->cfg, batch);
+  if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  TRY(run_forward(ctx, P, params, tokens, batch));
+  const nc_config& c = ctx->cfg;
+  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+  const int N = batch * c.seq_len;
+  GemmCall lg = mk(ctx->ws + P.z, c.d_model, true, (const char*)params + ctx->layout.back().offset * es, c.d_model,
+                   true, N, c.vocab, c.d_model, c.dtype);
+  lg.epi = EPI_F32; lg.e.c32 = logits; lg.e.ldc = c.vocab; lg.e.beta = 0;
+  return launch_gemm(lg, ctx->stream);
+}
+
+int nc_check(nc_ctx* ctx) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!ctx->ws) return NC_ERR_WORKSPACE;
+  return read_status(ctx->ws, ctx->stream);
+}
+
+int nc_op_status(void* workspace, void* stream) {
+  if (!workspace) return NC_ERR_NULL;
+  return read_status(workspace, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------- ops
+static size_t attn_ws_parts(int B, int H, int T, int hd, int dtype, size_t* off) {
+  const size_t N = (size_t)B * T, hh = (size_t)H * hd;
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
+  off[0] = take(256);            // status
+  off[1] = take(N * hh * es);    // qh
+  off[2] = take(N * hh * es);    // kh
+  off[3] = take(N * H * 4);      // rq
+  off[4] = take(N * H * 4);      // rk
+  off[5] = take(N * H * 4);      // lse
+  off[6] = take(N * H * 4);      // D
+  off[7] = take(N * hh * 4);     // dqh fp32
+  off[8] = take(N * hh * 4);     // dkh fp32
+  off[9] = take((size_t)T * hd * 4);  // rope table
+  return o;
+}
+
+uint64_t nc_attention_workspace_bytes(int B, int H, int T, int hd, int dtype) {
+  if (B < 1 || H < 1 || T < 1 || (hd != 16 && hd != 32 && hd != 64 && hd != 128)) return 0;
+  size_t off[10];
+  return attn_ws_parts(B, H, T, hd, dtype, off);
+}
+
+int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void* dout, void* out, void* dq, void* dk,
+                         void* dv, int B, int H, int T, int hd, float rope_base, float eps, int dtype, void* workspace,
+                         uint64_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !dout || !out || !dq || !dk || !dv || !workspace) return NC_ERR_NULL;
+  if (B < 1 || H < 1 || T < 1 || (hd != 16 && hd != 32 && hd != 64 && hd != 128) || !(rope_base > 1.f) ||
+      !(eps > 0.f))
+    return NC_ERR_ARG;
+  if (dtype != NC_BF16 && dtype != NC_FP32) return NC_ERR_ARG;
+  if (dtype == NC_BF16 && hd != 64 && hd != 128) return NC_ERR_UNSUPPORTED;
+  size_t off[10];
+  if (ws_bytes < attn_ws_parts(B, H, T, hd, dtype, off)) return NC_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)workspace;
+  const int N = B * T, hh = H * hd;
+  float* cs = (float*)(w + off[9]);
+  TRY(launch_rope_table(cs, T, hd, rope_base, s));
+  TRY(launch_qknorm_rope_fwd(q, hh, k, hh, w + off[1], hh, w + off[2], hh, (float*)(w + off[3]), (float*)(w + off[4]),
+                             cs, N, H, hd, T, eps, dtype, s));
+  AttnArgs a;
+  a.q = w + off[1]; a.ldq = hh;
+  a.k = w + off[2]; a.ldk = hh;
+  a.v = v; a.ldv = hh;
+  a.o = out; a.ldo = hh;
+  a.dout = dout; a.lddo = hh;
+  a.lse = (float*)(w + off[5]);
+  a.Dbuf = (float*)(w + off[6]);
+  a.dq32 = (float*)(w + off[7]); a.lddq = hh;
+  a.dk32 = (float*)(w + off[8]); a.lddk = hh;
+  a.dv = dv; a.lddv = hh;
+  a.B = B; a.H = H; a.T = T;
+  TRY(launch_attn_fwd(a, hd, dtype, s));
+  TRY(launch_attn_bwd(a, hd, dtype, s));
+  return launch_qknorm_rope_bwd(a.dq32, hh, a.dk32, hh, w + off[1], hh, w + off[2], hh, (float*)(w + off[3]),
+                                (float*)(w + off[4]), dq, hh, dk, hh, cs, N, H, hd, T, dtype, s);
+}
+
+static size_t ce_ws_parts(int N, int d, int V, int dtype, size_t* off) {
+  const size_t chunk = std::min<size_t>(N, kCeChunk);
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
+  off[0] = take(256);
+  off[1] = take(chunk * V * 4);
+  off[2] = take(chunk * V * es);
+  off[3] = take((size_t)N * 4);
+  off[4] = take(std::max(gemm_ws_bytes((int)chunk, d, V, dtype), gemm_ws_bytes(V, d, (int)chunk, dtype)));
+  return o;
+}
+
+uint64_t nc_lmhead_ce_workspace_bytes(int N, int d, int V, int dtype) {
+  if (N < 1 || d < 8 || d % 8 || V < 8 || V % 8) return 0;
+  size_t off[5];
+  return ce_ws_parts(N, d, V, dtype, off);
+}
+
+int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss, float* dz,
+                         float* dW, int dtype, void* workspace, uint64_t ws_bytes, void* stream) {
+  if (!z || !W || !y || !loss || !dz || !dW || !workspace) return NC_ERR_NULL;
+  if (N < 1 || d < 8 || d % 8 || V < 8 || V % 8) return NC_ERR_ARG;
+  if (dtype != NC_BF16 && dtype != NC_FP32) return NC_ERR_ARG;
+  size_t off[5];
+  if (ws_bytes < ce_ws_parts(N, d, V, dtype, off)) return NC_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)workspace;
+  int* status = (int*)w;
+  const uint64_t sk_bytes = std::max(gemm_ws_bytes(std::min(N, kCeChunk), d, V, dtype),
+                                     gemm_ws_bytes(V, d, std::min(N, kCeChunk), dtype));
+  float* sk = sk_bytes ? (float*)(w + off[4]) : nullptr;
+  TRY(lmhead_ce(z, W, y, N, d, V, (float*)(w + off[3]), dz, dW, 0, dtype, (float*)(w + off[1]), w + off[2], sk,
+                status, s));
+  return launch_mean((float*)(w + off[3]), N, loss, status, s);
+}
+
+int nc_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, void* stream) {
+  if (N == 0) return NC_OK;
+  if (!x || !y || !r) return NC_ERR_NULL;
+  if (N < 0 || d < 4 || d % 4 || !(eps > 0.f) || (dtype != NC_BF16 && dtype != NC_FP32)) return NC_ERR_ARG;
+  return launch_rmsnorm_fwd(x, y, r, N, d, eps, dtype, (hipStream_t)stream);
+}
+
+int nc_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
+                   int accumulate, int dtype, void* stream) {
+  if (N == 0) return NC_OK;
+  if (!dy || !y || !r || !dx) return NC_ERR_NULL;
+  if (N < 0 || d < 4 || d % 4 || (accumulate != 0 && accumulate != 1) || (dtype != NC_BF16 && dtype != NC_FP32))
+    return NC_ERR_ARG;
+  return launch_rmsnorm_bwd(dy, y, r, dx, dx_lp, N, d, accumulate, dtype, (hipStream_t)stream);
+}
+
+int nc_embedding_fwd(const void* E, const int32_t* tokens, float* x, int N, int d, int V, int dtype, void* workspace,
+                     void* stream) {
+  if (N == 0) return NC_OK;
+  if (!E || !tokens || !x || !workspace) return NC_ERR_NULL;
+  if (N < 0 || d < 4 || d % 4 || V < 1 || (dtype != NC_BF16 && dtype != NC_FP32)) return NC_ERR_ARG;
+  return launch_embed_fwd(E, tokens, x, N, d, V, dtype, (int*)workspace, (hipStream_t)stream);
+}
+
+uint64_t nc_embedding_bwd_workspace_bytes(int N, int d, int V) {
+  if (N < 0 || d < 4 || d % 4 || V < 1) return 0;
+  return embed_bwd_ws_bytes(N, d, V);
+}
+
+int nc_embedding_bwd(const float* dx, const int32_t* tokens, float* dE, int N, int d, int V, int accumulate,
+                     void* workspace, uint64_t ws_bytes, void* stream) {
+  if (!dE || (N > 0 && (!dx || !tokens || !workspace))) return NC_ERR_NULL;
+  if (N < 0 || d < 4 || d % 4 || V < 1 || (accumulate != 0 && accumulate != 1)) return NC_ERR_ARG;
+  if (ws_bytes < embed_bwd_ws_bytes(N, d, V)) return NC_ERR_WORKSPACE;
+  return launch_embed_bwd(dx, tokens, dE, N, d, V, accumulate, workspace, (hipStream_t)stream);
+}
+
+uint64_t nc_gemm_workspace_bytes(int M, int N, int K, int dtype) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return gemm_ws_bytes(M, N, K, dtype);
+}
+
+int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb, int b_kmajor, float* C, int ldc, int M,
+            int N, int K, int beta, int dtype, void* workspace, uint64_t ws_bytes, void* stream) {
+  if (!A || !B || !C) return NC_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || (beta != 0 && beta != 1) || (dtype != NC_BF16 && dtype != NC_FP32)) return NC_ERR_ARG;
+  if (a_kmajor != 0 && a_kmajor != 1) return NC_ERR_ARG;
+  if (b_kmajor != 0 && b_kmajor != 1) return NC_ERR_ARG;
+  // the contiguous dimension of each operand must be a multiple of 8 (16-byte loads)
+  if ((a_kmajor ? K : M) % 8 || (b_kmajor ? K : N) % 8 || N % 4) return NC_ERR_ARG;
+  if (lda < (a_kmajor ? K : M) || ldb < (b_kmajor ? K : N) || ldc < N || lda % 8 || ldb % 8 || ldc % 4)
+    return NC_ERR_ARG;
+  GemmCall g = mk(A, lda, a_kmajor, B, ldb, b_kmajor, M, N, K, dtype);
+  g.epi = EPI_F32; g.e.c32 = C; g.e.ldc = ldc; g.e.beta = beta;
+  const uint64_t need = gemm_ws_bytes(M, N, K, dtype);
+  if (need && workspace && ws_bytes >= need) g.splitk_ws = (float*)workspace;
+  return launch_gemm(g, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,261 @@
+/*
+ * nc.h -- C ABI of the MI355X (gfx950) training-step library.
+ *
+ * The library computes one forward + backward pass of a small decoder-only
+ * GPT on one GPU: token embedding, parameter-free RMSNorm, causal multi-head
+ * attention with QK-norm and RoPE, a ReLU-squared MLP, an untied LM head and
+ * the mean next-token softmax cross-entropy.  Sources, cited by page and
+ * section (the nanochat pages):
+ *   - "nanochat explainer" (cloudtoid LLM book), Modern architecture choices:
+ *     RoPE, RMSNorm, ReLU-squared, QK-norm, untied embeddings;
+ *   - same page, Architecture Choices -> RoPE Intuition and ReLU² Sparsity;
+ *   - same page, The 'One Dial' Design -> How dimensions are derived:
+ *     d_model = 64*depth, heads = d_model/128, head_dim = 128, FFN = 4*d_model;
+ *   - same page, The Full Pipeline -> Pretraining: causal next-token
+ *     prediction, cross-entropy loss; Tokenizer Training: V = 65,536.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are plain addresses of GPU memory the CALLER owns
+ *     (allocated e.g. by torch).  The library never allocates device memory;
+ *     scratch space is a caller-provided workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without synchronising;
+ *     results are valid once the stream has been synchronised.
+ *   - Return value: NC_OK or an nc_status code; no exception crosses the ABI.
+ *     Argument and configuration errors are detected on the host before any
+ *     GPU work is enqueued, and nothing is enqueued in that case.
+ *   - Data-dependent errors (a token or target id outside [0, vocab), a
+ *     non-finite loss) set a device status word instead; nc_check() reports
+ *     it.  An out-of-range id is clamped so that no access leaves its buffer.
+ *   - Element types: NC_BF16 stores weights and activations as bfloat16 and
+ *     accumulates in fp32; NC_FP32 (debug path) stores everything as fp32.
+ *     Gradients, losses and logits are always fp32.
+ *   - Matrices are row-major.  Weights are [out, in] (y = x W^T).
+ */
+#ifndef NC_H
+#define NC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NC_OK = 0,
+  NC_ERR_CONFIG = 1,      /* invalid or inconsistent configuration */
+  NC_ERR_NULL = 2,        /* a required pointer is NULL */
+  NC_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  NC_ERR_TOKEN_RANGE = 4, /* (device) an id was outside [0, vocab) */
+  NC_ERR_NONFINITE = 5,   /* (device) the loss was NaN or infinite */
+  NC_ERR_HIP = 6,         /* a HIP runtime call failed */
+  NC_ERR_UNSUPPORTED = 7, /* valid request outside what the kernels handle */
+  NC_ERR_ARG = 8          /* invalid size or flag argument */
+} nc_status;
+
+typedef enum { NC_BF16 = 0, NC_FP32 = 1 } nc_dtype;
+
+/*
+ * Model configuration.  A zero in d_model / n_heads / head_dim / d_ff is
+ * derived from `depth` by the depth dial ("nanochat explainer", How
+ * dimensions are derived); a nonzero value overrides it.  Zero rope_base
+ * means 10000, zero norm_eps means 1e-6.
+ * Constraints: depth >= 1; head_dim in {16, 32, 64, 128} (the bf16 path:
+ * 64 or 128); d_model, d_ff multiples of 64; vocab >= 64 and a multiple of
+ * 64; seq_len >= 1; max_batch >= 1.
+ */
+typedef struct {
+  int32_t depth;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t d_ff;
+  int32_t vocab;
+  int32_t seq_len;
+  int32_t max_batch;
+  float rope_base;
+  float norm_eps;
+  int32_t dtype; /* nc_dtype */
+} nc_config;
+
+typedef struct nc_ctx nc_ctx;
+
+/* One parameter tensor inside the flat parameter / gradient buffers. */
+typedef struct {
+  char name[48];   /* "E", "layers.<l>.W_qkv", "layers.<l>.W_o",
+                      "layers.<l>.W_1", "layers.<l>.W_2", "W_lm" */
+  uint64_t offset; /* in elements from the start of the flat buffer */
+  int32_t rows;    /* out features (vocab for E and W_lm) */
+  int32_t cols;    /* in features */
+} nc_tensor_desc;
+
+/* Human-readable text for a status code.  Never NULL. */
+const char* nc_strerror(int status);
+
+/*
+ * Validate `cfg`, apply the depth dial and plan the parameter layout and the
+ * workspace.  Host only: makes no HIP call, so it also works without a GPU.
+ * On success *out is a new context bound to `stream`.
+ * Errors: NC_ERR_NULL (cfg or out NULL), NC_ERR_CONFIG.
+ */
+int nc_init(const nc_config* cfg, void* stream, nc_ctx** out);
+
+/* Free the host context (the caller's device buffers are untouched). */
+void nc_destroy(nc_ctx* ctx);
+
+/* Copy the resolved configuration (derived fields filled in). */
+int nc_get_config(const nc_ctx* ctx, nc_config* out);
+
+/* Rebind the context to another stream. */
+int nc_set_stream(nc_ctx* ctx, void* stream);
+
+/*
+ * Flat parameter layout: E [V,d]; then per layer l: W_qkv [3*H*hd, d]
+ * (all q rows, then k, then v; head h owns rows h*hd..h*hd+hd-1 of each),
+ * W_o [d, H*hd], W_1 [d_ff, d], W_2 [d, d_ff]; then W_lm [V, d].  Tensors are
+ * packed back to back with no padding.  The gradient buffer uses the same
+ * layout in fp32.
+ */
+uint64_t nc_param_count(const nc_ctx* ctx);
+/* Writes min(cap, n) descriptors; returns n (the number of tensors). */
+int nc_param_layout(const nc_ctx* ctx, nc_tensor_desc* out, int cap);
+
+/* Workspace bytes needed by nc_forward_backward / nc_forward_logits for
+ * `batch` sequences (batch <= max_batch). 0 for an invalid batch. */
+uint64_t nc_workspace_bytes(const nc_ctx* ctx, int batch);
+
+/* Attach caller-owned device workspace (256-byte aligned). */
+int nc_set_workspace(nc_ctx* ctx, void* dev_ptr, uint64_t bytes);
+
+/*
+ * One training step's forward and backward pass.
+ *   params  : device, flat layout above, element type cfg.dtype.
+ *   tokens  : device int32 [batch, seq_len]; targets: device int32 [batch, seq_len]
+ *             (targets[b][t] is the id that follows tokens[b][t]).
+ *   loss    : device fp32 scalar; the mean cross-entropy over batch*seq_len
+ *             positions, in nats.
+ *   grads   : device fp32, flat layout; accumulate = 0 overwrites it,
+ *             accumulate = 1 adds this step's gradient to it.
+ * Saved activations live in the workspace, which must hold
+ * nc_workspace_bytes(ctx, batch) bytes.  Not re-entrant: one context per stream.
+ */
+int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens,
+                        const int32_t* targets, int batch, float* loss,
+                        float* grads, int accumulate);
+
+/* Forward pass only; logits: device fp32 [batch, seq_len, vocab]. */
+int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
+                      int batch, float* logits);
+
+/*
+ * Synchronise the context's stream, then read and clear the device status
+ * word.  Returns NC_OK, NC_ERR_TOKEN_RANGE, NC_ERR_NONFINITE or NC_ERR_HIP.
+ */
+int nc_check(nc_ctx* ctx);
+
+/* ------------------------------------------------------------------------
+ * Operation entry points (stateless).  Each takes its own workspace; the
+ * matching *_workspace_bytes() gives its size.  `dtype` is an nc_dtype and
+ * sets the element type of the non-fp32 arguments marked "(dt)".
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Causal attention with QK-norm and RoPE, forward and backward
+ * ("nanochat explainer", Modern architecture choices; RoPE Intuition):
+ *   qh = R_t rho(q), kh = R_t rho(k)  (rho: RMSNorm over head_dim, eps),
+ *   out = softmax_{j<=t}(qh kh^T / sqrt(hd)) v,
+ * and, for the upstream gradient dout, the gradients dq, dk, dv w.r.t. the
+ * pre-norm q, k and v.  RoPE pairs element i with i + hd/2 and rotates by
+ * t * rope_base^(-2i/hd), t = position within the sequence.
+ * Layout of q, k, v, dout, out, dq, dk, dv: (dt) [B, T, H, hd] contiguous.
+ * hd must be 16, 32, 64 or 128.  Errors: NC_ERR_NULL, NC_ERR_ARG (sizes),
+ * NC_ERR_UNSUPPORTED (hd not in {64, 128} on the bf16 path), NC_ERR_WORKSPACE.
+ */
+uint64_t nc_attention_workspace_bytes(int B, int H, int T, int hd, int dtype);
+int nc_attention_fwd_bwd(const void* q, const void* k, const void* v,
+                         const void* dout, void* out, void* dq, void* dk,
+                         void* dv, int B, int H, int T, int hd,
+                         float rope_base, float eps, int dtype,
+                         void* workspace, uint64_t ws_bytes, void* stream);
+
+/*
+ * Fused LM head + softmax cross-entropy, forward and backward ("nanochat
+ * explainer", Pretraining: next-token cross-entropy), processed in chunks of
+ * tokens so that the full [N, V] logits never exist:
+ *   l = z W^T; loss = mean_n [logsumexp(l_n) - l_{n,y_n}];
+ *   G = (softmax(l) - onehot(y)) / N;  dz = G W;  dW = G^T z.
+ * z: (dt) [N, d]; W: (dt) [V, d]; y: int32 [N]; loss: fp32 scalar;
+ * dz: fp32 [N, d] (overwritten); dW: fp32 [V, d] (overwritten).
+ * Errors: NC_ERR_NULL, NC_ERR_ARG, NC_ERR_WORKSPACE.  Ids outside [0, V)
+ * set the device status word read by nc_op_status().
+ */
+uint64_t nc_lmhead_ce_workspace_bytes(int N, int d, int V, int dtype);
+int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y,
+                         int N, int d, int V, float* loss, float* dz,
+                         float* dW, int dtype, void* workspace,
+                         uint64_t ws_bytes, void* stream);
+
+/*
+ * Read and clear the device status word at the start of an operation
+ * workspace (synchronises `stream`).  Same codes as nc_check().
+ */
+int nc_op_status(void* workspace, void* stream);
+
+/*
+ * Row RMSNorm ("nanochat explainer", Modern architecture choices: RMSNorm),
+ * parameter-free: y = x / sqrt(mean(x^2) + eps), r = 1/sqrt(mean(x^2) + eps).
+ * x: fp32 [N, d]; y: (dt) [N, d]; r: fp32 [N].  d must be a multiple of 4;
+ * N = 0 is a no-op.
+ */
+int nc_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps,
+                   int dtype, void* stream);
+/*
+ * Backward: dx (+)= r * (dy - y * mean(dy * y)).  dy: fp32 [N, d];
+ * y: (dt) [N, d]; r: fp32 [N]; dx: fp32 [N, d], overwritten when
+ * accumulate = 0 and added to when 1; dx_lp: optional (dt) copy of the
+ * resulting dx (may be NULL).
+ */
+int nc_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx,
+                   void* dx_lp, int N, int d, int accumulate, int dtype,
+                   void* stream);
+
+/*
+ * Token embedding ("nanochat explainer", Modern architecture choices:
+ * untied embeddings).  Forward: x[n] = E[tokens[n]]; E: (dt) [V, d];
+ * x: fp32 [N, d].  Uses the first 256 bytes of `workspace` for the status
+ * word (nc_op_status reads it).
+ */
+int nc_embedding_fwd(const void* E, const int32_t* tokens, float* x, int N,
+                     int d, int V, int dtype, void* workspace, void* stream);
+/*
+ * Backward without floating-point atomics: dE[v] = sum over the positions n
+ * with tokens[n] == v, in increasing n, of dx[n]; rows of ids that do not
+ * occur are 0 (accumulate = 0) or unchanged (accumulate = 1).
+ * dx: fp32 [N, d]; dE: fp32 [V, d].  Deterministic run to run.
+ */
+uint64_t nc_embedding_bwd_workspace_bytes(int N, int d, int V);
+int nc_embedding_bwd(const float* dx, const int32_t* tokens, float* dE, int N,
+                     int d, int V, int accumulate, void* workspace,
+                     uint64_t ws_bytes, void* stream);
+
+/*
+ * Matrix product with fp32 accumulation, the building block of every linear
+ * layer (y = x W^T), its input gradient (dx = dy W) and weight gradient
+ * (dW = dy^T x):   C[i, j] (+)= sum_k A(i, k) * B(j, k),
+ * for i < M, j < N, k < K.  a_kmajor = 1: A(i,k) = A[i*lda + k], else
+ * A(i,k) = A[k*lda + i]; likewise b_kmajor for B(j,k) = B[j*ldb + k] or
+ * B[k*ldb + j].  A, B: (dt); C: fp32 [M, N] with row stride ldc,
+ * overwritten (beta = 0) or added to (beta = 1).  The contiguous dimension
+ * of A and B must be a multiple of 8.
+ */
+uint64_t nc_gemm_workspace_bytes(int M, int N, int K, int dtype);
+int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb,
+            int b_kmajor, float* C, int ldc, int M, int N, int K, int beta,
+            int dtype, void* workspace, uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NC_H */

@@ -29,10 +29,11 @@ def bf16_round(x):
     NaN and infinities are not expected in synthetic inputs and are not handled.
     """
     a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    r = ((u + bias) >> 16) << 16
-    return (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(a.shape)
 
 
 def normal(shape, seed, stream, std=1.0):

@@ -1,0 +1,173 @@
+"""GPU parity of the whole training step (nc_forward_backward, nc_forward_logits)
+against the float64 oracle.
+
+Tolerances: loss within 1e-2 relative and every gradient tensor within 3e-2
+relative L2 on the bf16 path; both within 1e-4 on the fp32 debug path.
+The tiny model is checked in full, ragged shapes exercise partial tiles, the
+depth-20 and depth-26 widths are checked at two layers and one sequence of
+2048, and the full depth-20 bench configuration is checked through properties
+that hold at any size plus oracle losses of sampled sequences.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import banner, pack, prep, rel_l2, to_dev, to_np, unpack
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bwd_step_amd  # noqa: E402
+
+TOL = {"bf16": (1e-2, 3e-2), "fp32": (1e-4, 1e-4)}
+
+
+def setup(cfg, B, dt, seed=0, zipf=False):
+    shapes = oracle.param_shapes(cfg)
+    params = synth.weights(shapes, seed=seed, bf16=(dt == "bf16"))
+    if zipf:
+        tok, tgt = synth.zipf_tokens(B, cfg.seq_len, cfg.vocab, seed=seed)
+    else:
+        tok, tgt = synth.uniform_tokens(B, cfg.seq_len, cfg.vocab, seed=seed)
+    model = bwd_step_amd.Model(cfg.depth, vocab=cfg.vocab, seq_len=cfg.seq_len, max_batch=B, dtype=dt,
+                               d_model=cfg.d_model, n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ff=cfg.d_ff)
+    flat = to_dev(pack(params, shapes), dt)
+    return model, shapes, params, flat, to_dev(tok), to_dev(tgt), tok, tgt
+
+
+def run_step(model, flat, tok_d, tgt_d, accumulate=False, grads=None):
+    loss = torch.empty((), dtype=torch.float32, device="cuda")
+    if grads is None:
+        grads = torch.empty(model.param_count, dtype=torch.float32, device="cuda")
+    model.forward_backward(flat, tok_d, tgt_d, loss, grads, accumulate=accumulate)
+    assert model.check() == 0
+    return loss, grads
+
+
+def compare(cfg, dt, loss, grads, shapes, ref_loss, ref_grads):
+    tl, tg = TOL[dt]
+    assert abs(loss - ref_loss) / abs(ref_loss) < tl, (loss, ref_loss)
+    g = unpack(grads, shapes)
+    worst = []
+    for name, _ in shapes:
+        e = rel_l2(g[name], ref_grads[name])
+        worst.append((e, name))
+        assert e < tg, (name, e)
+    return max(worst)
+
+
+TINY = oracle.derive_config(2, vocab=512, seq_len=64, d_model=128, n_heads=2, head_dim=64, d_ff=512)
+RAGGED = oracle.derive_config(3, vocab=576, seq_len=100, d_model=192, n_heads=3, head_dim=64, d_ff=320)
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3)])
+def test_step_matches_oracle_small(dt, which, B):
+    cfg = TINY if which == "tiny" else RAGGED
+    banner(f"step {which} {dt} B={B}")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, dt)
+    loss, grads = run_step(model, flat, tok_d, tgt_d)
+    ref_loss, ref_grads = oracle.forward_backward(cfg, params, tok, tgt)
+    worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, ref_loss, ref_grads)
+    print(f"worst rel-L2 {worst}", flush=True)
+
+
+def test_step_deterministic_and_accumulate():
+    banner("step determinism + accumulate (tiny, bf16)")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(TINY, 2, "bf16", seed=1)
+    l1, g1 = run_step(model, flat, tok_d, tgt_d)
+    l2, g2 = run_step(model, flat, tok_d, tgt_d)
+    assert l1.item() == l2.item()
+    assert torch.equal(g1, g2)  # bitwise: no floating-point atomics anywhere
+    g3 = g1.clone()
+    run_step(model, flat, tok_d, tgt_d, accumulate=True, grads=g3)
+    assert torch.allclose(g3, 2 * g1, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_forward_logits_and_causality(dt):
+    banner(f"forward_logits {dt}")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(TINY, 2, dt, seed=2)
+    logits = torch.empty(2, TINY.seq_len, TINY.vocab, dtype=torch.float32, device="cuda")
+    model.forward_logits(flat, tok_d, logits)
+    assert model.check() == 0
+    ref = oracle.forward_logits(TINY, params, tok)
+    assert rel_l2(to_np(logits), ref) < (1e-4 if dt == "fp32" else 2e-2)
+    # changing tokens after position t0 leaves logits at positions <= t0 bitwise unchanged
+    t0 = 37
+    tok2 = tok.copy()
+    tok2[:, t0 + 1:] = (tok2[:, t0 + 1:] + 11) % TINY.vocab
+    logits2 = torch.empty_like(logits)
+    model.forward_logits(flat, to_dev(tok2), logits2)
+    assert torch.equal(logits[:, : t0 + 1], logits2[:, : t0 + 1])
+    assert not torch.equal(logits[:, t0 + 1:], logits2[:, t0 + 1:])
+
+
+def test_token_range_status():
+    banner("step with an out-of-range token")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(TINY, 1, "bf16", seed=3)
+    bad = tok.copy()
+    bad[0, 5] = TINY.vocab + 3
+    loss = torch.empty((), dtype=torch.float32, device="cuda")
+    grads = torch.empty(model.param_count, dtype=torch.float32, device="cuda")
+    model.forward_backward(flat, to_dev(bad), tgt_d, loss, grads)
+    assert model.check() == 4
+    assert model.check() == 0
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("depth_widths,zipf", [(20, False), (26, True)])
+def test_step_real_widths_two_layers(dt, depth_widths, zipf):
+    # depth-20 / depth-26 widths (d 1280 / 1664, 128-wide heads, V 65536), two layers, one sequence of 2048
+    full = oracle.derive_config(depth_widths)
+    cfg = oracle.derive_config(2, d_model=full.d_model, n_heads=full.n_heads, d_ff=full.d_ff)
+    banner(f"step widths of depth {depth_widths}, 2 layers, B=1, {dt}, zipf={zipf}")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, 1, dt, seed=4, zipf=zipf)
+    loss, grads = run_step(model, flat, tok_d, tgt_d)
+    g = to_np(grads)
+    ref_loss, ref_grads = oracle.forward_backward(cfg, params, tok, tgt)
+    worst = compare(cfg, dt, loss.item(), g, shapes, ref_loss, ref_grads)
+    print(f"worst rel-L2 {worst}", flush=True)
+
+
+def test_full_depth20_bench_config_properties():
+    """Depth 20, d 1280, V 65536, B 32 x T 2048 (the bench workload).
+
+    The oracle cannot run a whole step at this size, so: (a) the batch loss is
+    the mean of the 32 per-sequence losses and the batch gradient the mean of
+    per-sequence gradients (batch linearity, holding at any size); (b) two
+    sampled per-sequence losses match the oracle's forward; (c) the init loss
+    is near ln V + sigma^2/2 for logits of variance 0.02^2 * d.
+    """
+    cfg = oracle.derive_config(20)
+    B = 32
+    banner("full depth-20 step B=32 (bench configuration)")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, "bf16", seed=0)
+    loss, grads = run_step(model, flat, tok_d, tgt_d)
+    L = loss.item()
+    assert math.isfinite(L)
+    assert abs(L - (math.log(cfg.vocab) + 0.02 ** 2 * cfg.d_model / 2)) < 0.05
+    acc = torch.zeros_like(grads)
+    per = []
+    one = bwd_step_amd.Model(20, max_batch=1, dtype="bf16")
+    for b in range(B):
+        lb, _ = run_step(one, flat, tok_d[b:b + 1].contiguous(), tgt_d[b:b + 1].contiguous(),
+                         accumulate=(b > 0), grads=acc)
+        per.append(lb.item())
+    assert abs(L - float(np.mean(per))) / L < 1e-5
+    acc /= B
+    gn = unpack(to_np(grads), shapes)
+    an = unpack(to_np(acc), shapes)
+    for name, _ in shapes:
+        assert rel_l2(gn[name], an[name]) < 1e-4, name
+    p64 = {k: v.astype(np.float64) for k, v in params.items()}
+    for b in (0, 31):
+        ref = oracle.forward(cfg, p64, tok[b:b + 1], tgt[b:b + 1])
+        assert abs(per[b] - ref) / ref < 1e-2, (b, per[b], ref)

@@ -222,3 +222,15 @@ def test_embedding_bwd_brute_force_and_conservation():
     np.testing.assert_allclose(dE, brute, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(dE.sum(0), dx.sum(0), rtol=1e-12)
     assert np.all(dE[V - 3:] == 0.0)
+
+
+# ---------------------------------------------------------------- input rounding
+def test_bf16_round_is_rne():
+    import synth
+    # halfway cases go to the even neighbour
+    assert synth.bf16_round(np.float32([1.0 + 2 ** -8]))[0] == 1.0
+    assert synth.bf16_round(np.float32([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+    assert synth.bf16_round(np.float32([1.0 + 2 ** -8 + 2 ** -20]))[0] == 1.0 + 2 ** -7
+    x = R.standard_normal(100000).astype(np.float32) * 7
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(synth.bf16_round(x), ref)
