@@ -107,6 +107,19 @@ class Model:
         check(lib().nc_forward_logits(self._h, _ptr(params), _ptr(tokens), batch, _ptr(logits)),
               "nc_forward_logits")
 
+    def profile(self, on=True):
+        """Enable (and clear) or disable per-kernel-class event timing."""
+        check(lib().nc_profile_enable(self._h, int(bool(on))), "nc_profile_enable")
+
+    def profile_read(self):
+        """Dict class -> (launches, ms, flops, bytes) accumulated since enabling."""
+        n = lib().nc_profile_read(self._h, None, 0)
+        if n < 0:
+            raise NcError(-n, "nc_profile_read")
+        arr = (_nc.NcProfEntry * n)()
+        lib().nc_profile_read(self._h, arr, n)
+        return {a.name.decode(): (int(a.launches), a.ms, a.flops, a.bytes) for a in arr}
+
     def check(self):
         """Synchronise and return the device status code (0 = ok)."""
         return int(lib().nc_check(self._h))

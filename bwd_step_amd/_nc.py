@@ -38,6 +38,11 @@ class NcTensorDesc(ctypes.Structure):
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
 
 
+class NcProfEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
 SIGNATURES = {
     "nc_strerror": (ctypes.c_char_p, [_i]),
     "nc_init": (_i, [ctypes.POINTER(NcConfig), _vp, ctypes.POINTER(_vp)]),
@@ -51,6 +56,8 @@ SIGNATURES = {
     "nc_forward_backward": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i]),
     "nc_forward_logits": (_i, [_vp, _vp, _vp, _i, _vp]),
     "nc_check": (_i, [_vp]),
+    "nc_profile_enable": (_i, [_vp, _i]),
+    "nc_profile_read": (_i, [_vp, ctypes.POINTER(NcProfEntry), _i]),
     "nc_attention_workspace_bytes": (_u64, [_i, _i, _i, _i, _i]),
     "nc_attention_fwd_bwd": (_i, [_vp] * 8 + [_i, _i, _i, _i, _f, _f, _i, _vp, _u64, _vp]),
     "nc_lmhead_ce_workspace_bytes": (_u64, [_i, _i, _i, _i]),

@@ -49,6 +49,44 @@ struct Plan {
 
 }  // namespace
 
+// Per-kernel-class GPU timing: HIP events recorded on the launch stream
+// around each launcher call, with the algorithmic FLOPs / HBM bytes of that
+// call.  Off by default.
+enum ProfClass {
+  PC_GEMM, PC_ATTN_FWD, PC_ATTN_BWD, PC_RMS_FWD, PC_RMS_BWD, PC_QK_FWD, PC_QK_BWD,
+  PC_EMB_FWD, PC_EMB_BWD, PC_CE, PC_OTHER, PC_COUNT
+};
+static const char* kProfNames[PC_COUNT] = {"gemm", "attn_fwd", "attn_bwd", "rmsnorm_fwd", "rmsnorm_bwd",
+                                           "qknorm_rope_fwd", "qknorm_rope_bwd", "embed_fwd", "embed_bwd",
+                                           "ce_rows", "other"};
+
+struct Prof {
+  bool on = false;
+  struct Rec {
+    int cls;
+    hipEvent_t a, b;
+    double flops, bytes;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t get() {
+    if (used < pool.size()) return pool[used++];
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    pool.push_back(e);
+    ++used;
+    return e;
+  }
+  void clear() {
+    recs.clear();
+    used = 0;
+  }
+  ~Prof() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
 struct nc_ctx {
   nc_config cfg;
   hipStream_t stream;
@@ -56,6 +94,7 @@ struct nc_ctx {
   uint64_t nparams;
   char* ws = nullptr;
   uint64_t ws_bytes = 0;
+  Prof prof;
 };
 
 namespace {
@@ -180,6 +219,24 @@ int read_status(void* ws, hipStream_t s) {
     if (rc_) return rc_;         \
   } while (0)
 
+// Run a launcher call; when profiling, bracket it with events on stream s.
+#define PROF(P, cls, fl, by, call)                                         \
+  do {                                                                     \
+    Prof* p_ = (P);                                                        \
+    hipEvent_t e0_ = nullptr;                                              \
+    if (p_ && p_->on && (e0_ = p_->get())) (void)hipEventRecord(e0_, s);   \
+    TRY(call);                                                             \
+    if (e0_) {                                                             \
+      hipEvent_t e1_ = p_->get();                                          \
+      if (e1_) {                                                           \
+        (void)hipEventRecord(e1_, s);                                      \
+        p_->recs.push_back({(cls), e0_, e1_, (double)(fl), (double)(by)}); \
+      }                                                                    \
+    }                                                                      \
+  } while (0)
+
+inline double gflops(const GemmCall& g) { return 2.0 * g.M * (double)g.N * g.K; }
+
 GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, int M, int N, int K, int dtype) {
   GemmCall g;
   g.A = A; g.lda = lda; g.a_k = ak;
@@ -192,23 +249,24 @@ GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, 
 // LM head + cross-entropy over tokens in chunks: loss_rows, dz (fp32, [N,d]),
 // dW (fp32 [V,d]; overwritten or accumulated).  G and logits are chunk-sized.
 int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss_rows, float* dz,
-              float* dW, int accumulate, int dtype, float* logits, void* G, float* splitk, int* status, hipStream_t s) {
+              float* dW, int accumulate, int dtype, float* logits, void* G, float* splitk, int* status, hipStream_t s,
+              Prof* pf) {
   const size_t es = dtype == NC_BF16 ? 2 : 4;
   for (int c0 = 0; c0 < N; c0 += kCeChunk) {
     const int rows = std::min(kCeChunk, N - c0);
     const char* zc = (const char*)z + (size_t)c0 * d * es;
     GemmCall lg = mk(zc, d, true, W, d, true, rows, V, d, dtype);
     lg.epi = EPI_F32; lg.e.c32 = logits; lg.e.ldc = V; lg.e.beta = 0;
-    TRY(launch_gemm(lg, s));
-    TRY(launch_ce_rows(logits, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
+    PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
+    PROF(pf, PC_CE, 0, (double)rows * V * (4 + es), launch_ce_rows(logits, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
     GemmCall gw = mk(G, V, false, zc, d, false, V, d, rows, dtype);
     gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
     gw.splitk_ws = splitk;
-    TRY(launch_gemm(gw, s));
+    PROF(pf, PC_GEMM, gflops(gw), 0, launch_gemm(gw, s));
     GemmCall gz = mk(G, V, true, W, d, false, rows, d, V, dtype);
     gz.epi = EPI_F32; gz.e.c32 = dz + (size_t)c0 * d; gz.e.ldc = d; gz.e.beta = 0;
     gz.splitk_ws = splitk;
-    TRY(launch_gemm(gz, s));
+    PROF(pf, PC_GEMM, gflops(gz), 0, launch_gemm(gz, s));
   }
   return NC_OK;
 }
@@ -225,8 +283,10 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   float* x = (float*)(W + P.x);
   float* cs = (float*)(W + P.rope);
 
-  TRY(launch_embed_fwd(prm, tokens, x, N, d, V, dt, status, s));
-  TRY(launch_rope_table(cs, c.seq_len, hd, c.rope_base, s));
+  Prof* pf = &ctx->prof;
+  const double pairs = (double)batch * H * c.seq_len * (c.seq_len + 1) / 2.0;  // causal (query, key) pairs
+  PROF(pf, PC_EMB_FWD, 0, (double)N * d * (es + 4) + N * 4.0, launch_embed_fwd(prm, tokens, x, N, d, V, dt, status, s));
+  PROF(pf, PC_OTHER, 0, 0, launch_rope_table(cs, c.seq_len, hd, c.rope_base, s));
   for (int l = 0; l < c.depth; ++l) {
     char* L = W + P.layers_base + (size_t)l * P.layer_stride;
     const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
@@ -235,11 +295,12 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
     void* a1 = L + P.a1;
     char* qkv = L + P.qkv;
-    TRY(launch_rmsnorm_fwd(x, a1, (float*)(L + P.r1), N, d, c.norm_eps, dt, s));
+    PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
+         launch_rmsnorm_fwd(x, a1, (float*)(L + P.r1), N, d, c.norm_eps, dt, s));
     GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, 3 * hh, d, dt);
     g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
-    TRY(launch_gemm(g1, s));
-    TRY(launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
+    PROF(pf, PC_GEMM, gflops(g1), 0, launch_gemm(g1, s));
+    PROF(pf, PC_QK_FWD, 0, 4.0 * N * hh * es + 2.0 * N * H * 4, launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
                                (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, c.seq_len, c.norm_eps, dt, s));
     AttnArgs a;
     a.q = qkv; a.ldq = 3 * hh;
@@ -248,19 +309,21 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     a.o = L + P.O; a.ldo = hh;
     a.lse = (float*)(L + P.lse);
     a.B = batch; a.H = H; a.T = c.seq_len;
-    TRY(launch_attn_fwd(a, hd, dt, s));
+    PROF(pf, PC_ATTN_FWD, 4.0 * hd * pairs, 0, launch_attn_fwd(a, hd, dt, s));
     GemmCall g2 = mk(L + P.O, hh, true, Wo, hh, true, N, d, hh, dt);
     g2.epi = EPI_RESID; g2.e.c32 = x; g2.e.ldc = d;
-    TRY(launch_gemm(g2, s));
-    TRY(launch_rmsnorm_fwd(x, L + P.m, (float*)(L + P.r2), N, d, c.norm_eps, dt, s));
+    PROF(pf, PC_GEMM, gflops(g2), 0, launch_gemm(g2, s));
+    PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
+         launch_rmsnorm_fwd(x, L + P.m, (float*)(L + P.r2), N, d, c.norm_eps, dt, s));
     GemmCall g3 = mk(L + P.m, d, true, W1, d, true, N, F, d, dt);
     g3.epi = EPI_RELU2; g3.e.c_lp = L + P.u; g3.e.c_lp2 = L + P.g; g3.e.ld_lp = F;
-    TRY(launch_gemm(g3, s));
+    PROF(pf, PC_GEMM, gflops(g3), 0, launch_gemm(g3, s));
     GemmCall g4 = mk(L + P.g, F, true, W2, F, true, N, d, F, dt);
     g4.epi = EPI_RESID; g4.e.c32 = x; g4.e.ldc = d;
-    TRY(launch_gemm(g4, s));
+    PROF(pf, PC_GEMM, gflops(g4), 0, launch_gemm(g4, s));
   }
-  TRY(launch_rmsnorm_fwd(x, W + P.z, (float*)(W + P.rf), N, d, c.norm_eps, dt, s));
+  PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
+       launch_rmsnorm_fwd(x, W + P.z, (float*)(W + P.rf), N, d, c.norm_eps, dt, s));
   return NC_OK;
 }
 
@@ -281,10 +344,14 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   float* cs = (float*)(W + P.rope);
   const Desc& lm = ctx->layout.back();
 
+  Prof* pf = &ctx->prof;
+  const double pairs = (double)batch * H * c.seq_len * (c.seq_len + 1) / 2.0;
+  const double rms_bwd_bytes = (double)N * d * (4 + es + 4 + 4 + es) + N * 4.0;
   TRY(lmhead_ce(W + P.z, prm + lm.offset * es, targets, N, d, V, (float*)(W + P.loss_rows), tmp,
-                grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, status, s));
-  TRY(launch_mean((float*)(W + P.loss_rows), N, loss, status, s));
-  TRY(launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
+                grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, status, s, pf));
+  PROF(pf, PC_OTHER, 0, 0, launch_mean((float*)(W + P.loss_rows), N, loss, status, s));
+  PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 4,
+       launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
 
   for (int l = c.depth - 1; l >= 0; --l) {
     char* L = W + P.layers_base + (size_t)l * P.layer_stride;
@@ -304,25 +371,25 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     // MLP: du = (dx W_2) * 2 relu(u); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.u; b1.e.ld_aux = F;
-    TRY(launch_gemm(b1, s));
+    PROF(pf, PC_GEMM, gflops(b1), 0, launch_gemm(b1, s));
     GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
     b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk;
-    TRY(launch_gemm(b2, s));
+    PROF(pf, PC_GEMM, gflops(b2), 0, launch_gemm(b2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
     b3.epi = EPI_F32; b3.e.c32 = tmp; b3.e.ldc = d;
-    TRY(launch_gemm(b3, s));
+    PROF(pf, PC_GEMM, gflops(b3), 0, launch_gemm(b3, s));
     GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
     b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk;
-    TRY(launch_gemm(b4, s));
-    TRY(launch_rmsnorm_bwd(tmp, L + P.m, (float*)(L + P.r2), dx, dx_lp, N, d, 1, dt, s));
+    PROF(pf, PC_GEMM, gflops(b4), 0, launch_gemm(b4, s));
+    PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.m, (float*)(L + P.r2), dx, dx_lp, N, d, 1, dt, s));
 
     // attention output projection: dO = dx W_o; dW_o = dx^T O
     GemmCall b5 = mk(dx_lp, d, true, Wo, hh, false, N, hh, d, dt);
     b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
-    TRY(launch_gemm(b5, s));
+    PROF(pf, PC_GEMM, gflops(b5), 0, launch_gemm(b5, s));
     GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
     b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk;
-    TRY(launch_gemm(b6, s));
+    PROF(pf, PC_GEMM, gflops(b6), 0, launch_gemm(b6, s));
 
     AttnArgs a;
     a.q = qkv; a.ldq = 3 * hh;
@@ -336,21 +403,22 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     a.dk32 = dqk32 + hh; a.lddk = 2 * hh;
     a.dv = dqkv + 2 * hh * es; a.lddv = 3 * hh;
     a.B = batch; a.H = H; a.T = c.seq_len;
-    TRY(launch_attn_bwd(a, hd, dt, s));
-    TRY(launch_qknorm_rope_bwd(dqk32, 2 * hh, dqk32 + hh, 2 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
+    PROF(pf, PC_ATTN_BWD, 8.0 * hd * pairs, 0, launch_attn_bwd(a, hd, dt, s));
+    PROF(pf, PC_QK_BWD, 0, 2.0 * N * hh * (4 + 2 * es) + 2.0 * N * H * 4, launch_qknorm_rope_bwd(dqk32, 2 * hh, dqk32 + hh, 2 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
                                (float*)(L + P.rq), (float*)(L + P.rk), dqkv, 3 * hh, dqkv + hh * es, 3 * hh, cs, N, H,
                                hd, c.seq_len, dt, s));
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
     GemmCall b7 = mk(dqkv, 3 * hh, true, Wqkv, d, false, N, d, 3 * hh, dt);
     b7.epi = EPI_F32; b7.e.c32 = tmp; b7.e.ldc = d;
-    TRY(launch_gemm(b7, s));
+    PROF(pf, PC_GEMM, gflops(b7), 0, launch_gemm(b7, s));
     GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
     b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk;
-    TRY(launch_gemm(b8, s));
-    TRY(launch_rmsnorm_bwd(tmp, L + P.a1, (float*)(L + P.r1), dx, dx_lp, N, d, 1, dt, s));
+    PROF(pf, PC_GEMM, gflops(b8), 0, launch_gemm(b8, s));
+    PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.a1, (float*)(L + P.r1), dx, dx_lp, N, d, 1, dt, s));
   }
-  TRY(launch_embed_bwd(dx, tokens, grads, N, d, V, accumulate, W + P.embed_ws, s));
+  PROF(pf, PC_EMB_BWD, 0, (double)N * d * 4 + (double)V * d * 4 * (accumulate ? 2 : 1) + N * 4.0,
+       launch_embed_bwd(dx, tokens, grads, N, d, V, accumulate, W + P.embed_ws, s));
   return NC_OK;
 }
 
@@ -465,6 +533,39 @@ int nc_check(nc_ctx* ctx) {
   return read_status(ctx->ws, ctx->stream);
 }
 
+int nc_profile_enable(nc_ctx* ctx, int on) {
+  if (!ctx) return NC_ERR_NULL;
+  if (on != 0 && on != 1) return NC_ERR_ARG;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) return NC_ERR_HIP;
+  ctx->prof.clear();
+  ctx->prof.on = on != 0;
+  return NC_OK;
+}
+
+int nc_profile_read(nc_ctx* ctx, nc_prof_entry* out, int cap) {
+  if (!ctx) return -NC_ERR_NULL;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess) return -NC_ERR_HIP;
+  double ms[PC_COUNT] = {}, fl[PC_COUNT] = {}, by[PC_COUNT] = {};
+  int64_t n[PC_COUNT] = {};
+  for (const auto& r : ctx->prof.recs) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return -NC_ERR_HIP;
+    ms[r.cls] += t;
+    fl[r.cls] += r.flops;
+    by[r.cls] += r.bytes;
+    n[r.cls] += 1;
+  }
+  for (int i = 0; i < PC_COUNT && i < cap && out; ++i) {
+    memset(&out[i], 0, sizeof(nc_prof_entry));
+    strncpy(out[i].name, kProfNames[i], sizeof(out[i].name) - 1);
+    out[i].launches = n[i];
+    out[i].ms = ms[i];
+    out[i].flops = fl[i];
+    out[i].bytes = by[i];
+  }
+  return PC_COUNT;
+}
+
 int nc_op_status(void* workspace, void* stream) {
   if (!workspace) return NC_ERR_NULL;
   return read_status(workspace, (hipStream_t)stream);
@@ -564,7 +665,7 @@ int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, 
                                      gemm_ws_bytes(V, d, std::min(N, kCeChunk), dtype));
   float* sk = sk_bytes ? (float*)(w + off[4]) : nullptr;
   TRY(lmhead_ce(z, W, y, N, d, V, (float*)(w + off[3]), dz, dW, 0, dtype, (float*)(w + off[1]), w + off[2], sk,
-                status, s));
+                status, s, nullptr));
   return launch_mean((float*)(w + off[3]), N, loss, status, s);
 }
 

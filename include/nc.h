@@ -154,6 +154,28 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
  */
 int nc_check(nc_ctx* ctx);
 
+/*
+ * Tracing: per-kernel-class GPU time.  When enabled, every launch made by
+ * nc_forward_backward / nc_forward_logits is bracketed by HIP events on the
+ * context's stream and credited to its class ("gemm", "attn_fwd",
+ * "attn_bwd", "rmsnorm_fwd", "rmsnorm_bwd", "qknorm_rope_fwd",
+ * "qknorm_rope_bwd", "embed_fwd", "embed_bwd", "ce_rows", "other") with the
+ * call's algorithmic FLOPs (GEMMs: 2MNK; attention: causal model FLOPs) or
+ * HBM bytes (bandwidth-bound kernels: each input read once, each output
+ * written once).  nc_profile_enable synchronises the stream and clears the
+ * records.  nc_profile_read synchronises, writes min(cap, n) entries and
+ * returns n (negative nc_status on error).
+ */
+typedef struct {
+  char name[32];
+  int64_t launches;
+  double ms;
+  double flops;
+  double bytes;
+} nc_prof_entry;
+int nc_profile_enable(nc_ctx* ctx, int on);
+int nc_profile_read(nc_ctx* ctx, nc_prof_entry* out, int cap);
+
 /* ------------------------------------------------------------------------
  * Operation entry points (stateless).  Each takes its own workspace; the
  * matching *_workspace_bytes() gives its size.  `dtype` is an nc_dtype and

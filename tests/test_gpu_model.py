@@ -140,17 +140,23 @@ def test_step_real_widths_two_layers(dt, depth_widths, zipf):
 def test_full_depth20_bench_config_properties():
     """Depth 20, d 1280, V 65536, B 32 x T 2048 (the bench workload).
 
-    The oracle cannot run a whole step at this size, so: (a) the batch loss is
-    the mean of the 32 per-sequence losses and the batch gradient the mean of
-    per-sequence gradients (batch linearity, holding at any size); (b) two
-    sampled per-sequence losses match the oracle's forward; (c) the init loss
-    is near ln V + sigma^2/2 for logits of variance 0.02^2 * d.
+    The oracle cannot run a whole step at this size, so: (a) two runs give
+    bitwise-identical gradients; (b) the batch loss is the mean of the 32
+    per-sequence losses (fp32 sums only, 1e-5) and the batch gradient the
+    mean of the per-sequence gradients to the bf16 tolerance (the B=32 and B=1
+    runs sum in different fp32 orders, after which the two runs' bf16
+    roundings decorrelate); (c) a sampled sequence's loss matches the oracle's
+    forward; (d) the init loss is near ln V + sigma^2/2 for logits of variance
+    0.02^2 * d.
     """
     cfg = oracle.derive_config(20)
     B = 32
     banner("full depth-20 step B=32 (bench configuration)")
     model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, "bf16", seed=0)
     loss, grads = run_step(model, flat, tok_d, tgt_d)
+    loss2, grads2 = run_step(model, flat, tok_d, tgt_d)
+    assert torch.equal(grads, grads2) and loss.item() == loss2.item()
+    del grads2
     L = loss.item()
     assert math.isfinite(L)
     assert abs(L - (math.log(cfg.vocab) + 0.02 ** 2 * cfg.d_model / 2)) < 0.05
@@ -165,9 +171,39 @@ def test_full_depth20_bench_config_properties():
     acc /= B
     gn = unpack(to_np(grads), shapes)
     an = unpack(to_np(acc), shapes)
-    for name, _ in shapes:
-        assert rel_l2(gn[name], an[name]) < 1e-4, name
+    errs = {name: rel_l2(gn[name], an[name]) for name, _ in shapes}
+    print("batch-linearity rel-L2: max %.2e (%s)" % max((v, k) for k, v in errs.items()), flush=True)
+    assert max(errs.values()) < 3e-2
     p64 = {k: v.astype(np.float64) for k, v in params.items()}
-    for b in (0, 31):
-        ref = oracle.forward(cfg, p64, tok[b:b + 1], tgt[b:b + 1])
-        assert abs(per[b] - ref) / ref < 1e-2, (b, per[b], ref)
+    ref = oracle.forward(cfg, p64, tok[31:32], tgt[31:32])
+    assert abs(per[31] - ref) / ref < 1e-2, (per[31], ref)
+
+
+_FULL = {}
+
+
+def _full_depth20_reference():
+    """Oracle loss and gradients of one 2048-token sequence at full depth 20 (computed once)."""
+    if not _FULL:
+        cfg = oracle.derive_config(20)
+        shapes = oracle.param_shapes(cfg)
+        params = synth.weights(shapes, seed=5, bf16=True)  # bf16-representable: feeds both paths exactly
+        tok, tgt = synth.uniform_tokens(1, cfg.seq_len, cfg.vocab, seed=5)
+        p64 = {k: v.astype(np.float64) for k, v in params.items()}
+        ref_loss, ref_grads = oracle.forward_backward(cfg, p64, tok, tgt)
+        _FULL.update(cfg=cfg, shapes=shapes, params=params, tok=tok, tgt=tgt, loss=ref_loss, grads=ref_grads)
+    return _FULL
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_full_depth20_one_sequence_matches_oracle(dt):
+    """All 20 layers at the real widths, one sequence of 2048: every gradient tensor."""
+    banner(f"full depth-20, B=1, {dt}, against the oracle")
+    R = _full_depth20_reference()
+    cfg, shapes = R["cfg"], R["shapes"]
+    model = bwd_step_amd.Model(20, max_batch=1, dtype=dt)
+    flat = to_dev(pack(R["params"], shapes), dt)
+    loss, grads = run_step(model, flat, to_dev(R["tok"]), to_dev(R["tgt"]))
+    worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, R["loss"], R["grads"])
+    print(f"worst rel-L2 {worst}", flush=True)
