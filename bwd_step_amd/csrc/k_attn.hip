@@ -35,6 +35,10 @@ namespace nc {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// 2^x with the hardware instruction (no range fix-up; results below the
+// smallest normal flush to zero, which is harmless for softmax weights).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Tile staging: a [64 rows][HD] bf16 tile is read in 4-row x 8-column blocks
 // (four 16-byte loads).  The same registers can be stored row-major
 // (row stride HD + 8) and/or transposed (row stride 64 + 4).
@@ -220,6 +224,508 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
       *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
     }
   if (g == 0) p.lse[(size_t)bh * T + qi] = (mx + log2f(ltot)) * kLn2;
+}
+
+// ------------------------------------------------------------------ forward, head_dim 128
+// K and V tiles ([64 keys][128], 16 KB each) are staged with LDS-direct buffer
+// loads into two stages (separate LDS objects, so the compiler does not wait
+// on the in-flight stage).  K fragments for S^T = K Q^T are 16-byte reads of
+// an XOR-swizzled tile (chunk ^= key & 15).  V^T fragments for O^T = V^T P^T
+// come straight from the row-major V tile through ds_read_b64_tr_b16, whose
+// per-16-lane-group key offset is chosen to follow the key order that the
+// score accumulator already has; the V chunks are swizzled by sw_v(key & 3)
+// so that these reads are conflict free.  The kernel stays under 256
+// registers per lane so that two workgroups (eight wavefronts) share a
+// compute unit and one's softmax overlaps the other's MFMAs.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ int sw_v(int r) { return 4 * r + 2 * ((r >> 1) & 1); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 1 KB block (4 key rows of 128) of a [64][128] tile; V tiles use the
+// transposed-read swizzle, K tiles the row swizzle.
+template <bool VTILE>
+__device__ __forceinline__ void kv_dma(rsrc_t rs, long ld, long col0, int key0, int T, bf16* lds, int blk,
+                                       int lane) {
+  const int row = blk * 4 + (lane >> 4);
+  const int pc = lane & 15;
+  const int c = VTILE ? (pc ^ sw_v(row & 3)) : (pc ^ (row & 15));
+  const int key = key0 + row;
+  const uint32_t off = key < T ? (uint32_t)(((long)key * ld + col0 + c * 8) * 2) : kOOB;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + blk * 512), 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 k_frag(const bf16* Ks, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(Ks + row * 128 + ((chunk ^ (row & 15)) << 3));
+}
+
+// V^T fragment: hd rows x*32 + (lane & 31), keys kb + {4g .. 4g+3, 8+4g .. 8+4g+3}, g = lane / 32.
+__device__ __forceinline__ bf16x8 vt_frag(const bf16* Vs, int x, int kb, int lane) {
+  const int gi = lane >> 4, i = lane & 15;
+  const int r = i >> 2, q = i & 3;
+  const int chunk = (x * 4 + 2 * (gi & 1) + (q >> 1)) ^ sw_v(r);
+  const int col = (chunk << 3) + 4 * (q & 1);
+  const int k0 = kb + 4 * (gi >> 1) + r;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(Vs + k0 * 128 + col));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(Vs + (k0 + 8) * 128 + col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  __shared__ __attribute__((aligned(1024))) bf16 K0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 K1[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 V1[64 * HD];
+
+  const int T = p.T;
+  const int nqb = (T + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int q0 = qb * 128;
+  const int qi = q0 + wv * 32 + li;
+  const size_t tok0 = (size_t)b * T;
+  const uint32_t kbytes = (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2);
+  const uint32_t vbytes = (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2);
+  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk, kbytes);
+  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv, vbytes);
+  const long colk = (long)h * HD;
+
+  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
+
+  f32x16 oacc[HB];
+#pragma unroll
+  for (int x = 0; x < HB; ++x) oacc[x] = f32x16{};
+  float mx = -INFINITY, lsum = 0.f;
+  const float c = p.scale_log2;
+
+  const int q_last = min(T - 1, q0 + 127);
+  const int nkv = q_last / 64 + 1;
+  const int wq_min = q0 + wv * 32, wq_max = wq_min + 31;
+
+  // stage block 0
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kv_dma<false>(rk, p.ldk, colk, 0, T, K0, wv * 4 + i, lane);
+    kv_dma<true>(rv, p.ldv, colk, 0, T, V0, wv * 4 + i, lane);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  auto block = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn, int kb) {
+    const bool live = kb + 1 < nkv;
+    const int knext = (kb + 1) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kv_dma<false>(rk, p.ldk, colk, live ? knext : T, T, Kn, wv * 4 + i, lane);
+      kv_dma<true>(rv, p.ldv, colk, live ? knext : T, T, Vn, wv * 4 + i, lane);
+    }
+    const int kbase = kb * 64;
+    if (kbase <= wq_max) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        sacc[kk] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc[kk] = mfma(k_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], sacc[kk]);
+      }
+      const bool need_mask = (kbase + 63 > wq_min) || (kbase + 64 > T);
+      float lmax = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + kk * 32 + acc_row(r, g);
+            if (key > qi || key >= T) sacc[kk][r] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, sacc[kk][r]);
+      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+      // Running max in the scaled log2 domain.  It is raised (and O and the
+      // sum rescaled) only when a score exceeds it by more than 8, so the
+      // weights below stay <= 2^8 and the costly rescale is rare; the final
+      // normalisation by the sum makes the result independent of the choice.
+      const float mcand = fmaxf(mx, lmax * c);
+      if (mcand > mx + 8.f) {
+        const float alpha = ex2(mx - mcand);
+        lsum *= alpha;
+#pragma unroll
+        for (int x = 0; x < HB; ++x) oacc[x] *= alpha;
+        mx = mcand;
+      }
+      const float moff = mx == -INFINITY ? 0.f : -mx;
+      float ps = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = ex2(fmaf(sacc[kk][r], c, moff));
+          sacc[kk][r] = e;
+          ps += e;
+        }
+      lsum += ps;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 pf = pack8(sacc[kk], t);
+#pragma unroll
+          for (int x = 0; x < HB; ++x) oacc[x] = mfma(vt_frag(Vs, x, kk * 32 + t * 16, lane), pf, oacc[x]);
+        }
+    }
+  };
+
+  int kb = 0;
+  for (; kb + 1 < nkv; kb += 2) {
+    block(K0, V0, K1, V1, kb);
+    wait_vmem();
+    __syncthreads();
+    block(K1, V1, K0, V0, kb + 1);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (kb < nkv) block(K0, V0, K1, V1, kb);
+  wait_vmem();  // the tail's no-op loads still target LDS
+
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  if (qi >= T) return;
+  const float inv = 1.0f / ltot;
+  bf16* op = (bf16*)p.o + (tok0 + qi) * p.ldo + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 w;
+      w.x = pack_bf16x2(oacc[x][rg * 4 + 0] * inv, oacc[x][rg * 4 + 1] * inv);
+      w.y = pack_bf16x2(oacc[x][rg * 4 + 2] * inv, oacc[x][rg * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
+    }
+  if (g == 0) p.lse[(size_t)bh * T + qi] = (mx + log2f(ltot)) * kLn2;
+}
+
+// ------------------------------------------------------------------ backward, head_dim 128
+// Tiles of 64 rows x 128 that are read both ways -- 16-byte row fragments
+// (the A operand of S = Q K^T, dP = dO V^T and their transposes) and
+// transposed fragments through ds_read_b64_tr_b16 (the A operand of
+// dQ^T = K^T dS^T, dK^T = Q^T dS, dV^T = dO^T P) -- use one XOR swizzle of
+// the 16-byte chunk index, sw2(row), that is conflict free for both access
+// patterns (any 16 aligned rows see 16 distinct chunk slots; within every
+// aligned group of 4 rows bits 2-3 differ and bits 1-2 differ).
+__device__ __forceinline__ int sw2(int row) { return 4 * (row & 3) + (((row >> 2) & 3) ^ (2 * ((row >> 1) & 1))); }
+
+__device__ __forceinline__ void tile_dma(rsrc_t rs, long ld, long col0, int row0, int T, bf16* lds, int blk,
+                                         int lane) {
+  const int row = blk * 4 + (lane >> 4);
+  const int c = (lane & 15) ^ sw2(row);
+  const int t = row0 + row;
+  const uint32_t off = t < T ? (uint32_t)(((long)t * ld + col0 + c * 8) * 2) : kOOB;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + blk * 512), 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 row_frag(const bf16* S, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(S + row * 128 + ((chunk ^ sw2(row)) << 3));
+}
+
+// Transposed fragment: A-operand rows = columns x*32 + (lane & 31) of the
+// tile, reduction index = tile rows kb + {4g .. 4g+3, 8+4g .. 8+4g+3}.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* S, int x, int kb, int lane) {
+  const int gi = lane >> 4, i = lane & 15;
+  const int r = i >> 2, q = i & 3;
+  const int chunk = x * 4 + 2 * (gi & 1) + (q >> 1);
+  const int k0 = kb + 4 * (gi >> 1) + r;
+  const int sub = 4 * (q & 1);
+  const v4i16 lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(S + k0 * 128 + ((chunk ^ sw2(k0)) << 3) + sub));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_AS v4i16*)(S + (k0 + 8) * 128 + ((chunk ^ sw2(k0 + 8)) << 3) + sub));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// dQ: 128 queries per workgroup, 64-key blocks of K and V staged in LDS.
+__global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  __shared__ __attribute__((aligned(1024))) bf16 K0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 K1[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 V0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 V1[64 * HD];
+
+  const int T = p.T;
+  const int nqb = (T + 127) / 128;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int q0 = qb * 128;
+  const int qi = q0 + wv * 32 + li;
+  const size_t tok0 = (size_t)b * T;
+  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
+                              (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2));
+  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv,
+                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2));
+  const long col = (long)h * HD;
+
+  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
+  const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
+    df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
+  }
+  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] * kLog2e : 0.f;
+  const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
+  const float c = p.scale_log2;
+
+  f32x16 dq[HB];
+#pragma unroll
+  for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
+
+  const int q_last = min(T - 1, q0 + 127);
+  const int nkv = q_last / 64 + 1;
+  const int wq_min = q0 + wv * 32, wq_max = wq_min + 31;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tile_dma(rk, p.ldk, col, 0, T, K0, wv * 4 + i, lane);
+    tile_dma(rv, p.ldv, col, 0, T, V0, wv * 4 + i, lane);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  auto block = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn, int kb) {
+    const int knext = kb + 1 < nkv ? (kb + 1) * 64 : T;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile_dma(rk, p.ldk, col, knext, T, Kn, wv * 4 + i, lane);
+      tile_dma(rv, p.ldv, col, knext, T, Vn, wv * 4 + i, lane);
+    }
+    const int kbase = kb * 64;
+    if (kbase > wq_max) return;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      sacc[kk] = f32x16{};
+      pacc[kk] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sacc[kk] = mfma(row_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], sacc[kk]);
+        pacc[kk] = mfma(row_frag(Vs, kk * 32 + li, 2 * s + g), df[s], pacc[kk]);
+      }
+    }
+    const bool need_mask = (kbase + 63 > wq_min) || (kbase + 64 > T);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = ex2(fmaf(sacc[kk][r], c, nlse));
+        if (need_mask) {
+          const int key = kbase + kk * 32 + acc_row(r, g);
+          if (key > qi || key >= T) pr = 0.f;
+        }
+        pacc[kk][r] = pr * (pacc[kk][r] - Dl);  // dS^T
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 sf = pack8(pacc[kk], t);
+#pragma unroll
+        for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 32 + t * 16, lane), sf, dq[x]);
+      }
+  };
+
+  int kb = 0;
+  for (; kb + 1 < nkv; kb += 2) {
+    block(K0, V0, K1, V1, kb);
+    wait_vmem();
+    __syncthreads();
+    block(K1, V1, K0, V0, kb + 1);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (kb < nkv) block(K0, V0, K1, V1, kb);
+  wait_vmem();
+
+  if (qi >= T) return;
+  const float sc = p.scale;
+  float* dqp = p.dq32 + (tok0 + qi) * p.lddq + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      f32x4 w{dq[x][rg * 4 + 0] * sc, dq[x][rg * 4 + 1] * sc, dq[x][rg * 4 + 2] * sc, dq[x][rg * 4 + 3] * sc};
+      *reinterpret_cast<f32x4*>(dqp + x * 32 + 8 * rg + 4 * g) = w;
+    }
+}
+
+// dK, dV: 128 keys per workgroup (K and V fragments held in registers), 64-query
+// blocks of qh and dO staged in LDS, lse and D for the block in LDS.
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  __shared__ __attribute__((aligned(1024))) bf16 Q0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 Q1[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 O0[64 * HD];
+  __shared__ __attribute__((aligned(1024))) bf16 O1[64 * HD];
+  __shared__ float L0[64], L1[64], D0[64], D1[64];
+
+  const int T = p.T;
+  const int kbk = blockIdx.x;  // low key blocks have the most queries: launched first
+  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int k0 = kbk * 128;
+  const int kj = k0 + wv * 32 + li;
+  const size_t tok0 = (size_t)b * T;
+  const rsrc_t rq = make_rsrc((const bf16*)p.q + tok0 * p.ldq,
+                              (uint32_t)(((size_t)(T - 1) * p.ldq + (size_t)p.H * HD) * 2));
+  const rsrc_t ro = make_rsrc((const bf16*)p.dout + tok0 * p.lddo,
+                              (uint32_t)(((size_t)(T - 1) * p.lddo + (size_t)p.H * HD) * 2));
+  const long col = (long)h * HD;
+  const float* lsep = p.lse + (size_t)bh * T;
+  const float* Dp = p.Dbuf + (size_t)bh * T;
+
+  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
+  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(kp + (size_t)kj * p.ldk + s * 16 + g * 8) : bf16x8{};
+    vf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(vp + (size_t)kj * p.ldv + s * 16 + g * 8) : bf16x8{};
+  }
+  f32x16 dk[HB], dv[HB];
+#pragma unroll
+  for (int x = 0; x < HB; ++x) { dk[x] = f32x16{}; dv[x] = f32x16{}; }
+  const float c = p.scale_log2;
+
+  const int nqb = (T + 63) / 64;
+  const int qb0 = k0 / 64;
+  const int wk_min = k0 + wv * 32;
+  const int tid = threadIdx.x;
+
+  // stage the first query block
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tile_dma(rq, p.ldq, col, qb0 * 64, T, Q0, wv * 4 + i, lane);
+    tile_dma(ro, p.lddo, col, qb0 * 64, T, O0, wv * 4 + i, lane);
+  }
+  if (tid < 64) {
+    const int t = qb0 * 64 + tid;
+    L0[tid] = t < T ? lsep[t] * kLog2e : 0.f;
+    D0[tid] = t < T ? Dp[t] : 0.f;
+  }
+  wait_vmem();
+  __syncthreads();
+
+  auto block = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, bf16* Qn, bf16* On, float* Ln,
+                   float* Dn, int qb) {
+    const int qnext = qb + 1 < nqb ? (qb + 1) * 64 : T;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile_dma(rq, p.ldq, col, qnext, T, Qn, wv * 4 + i, lane);
+      tile_dma(ro, p.lddo, col, qnext, T, On, wv * 4 + i, lane);
+    }
+    float ln = 0.f, dn = 0.f;
+    if (tid < 64 && qnext + tid < T) {
+      ln = lsep[qnext + tid] * kLog2e;
+      dn = Dp[qnext + tid];
+    }
+    const int qbase = qb * 64;
+    if (qbase + 63 >= wk_min) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        sacc[mi] = f32x16{};
+        pacc[mi] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sacc[mi] = mfma(row_frag(Qs, mi * 32 + li, 2 * s + g), kf[s], sacc[mi]);
+          pacc[mi] = mfma(row_frag(Os, mi * 32 + li, 2 * s + g), vf[s], pacc[mi]);
+        }
+      }
+      const bool need_mask = (qbase < wk_min + 31) || (qbase + 64 > T);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = mi * 32 + acc_row(r, g);
+          float pr = ex2(fmaf(sacc[mi][r], c, -Ls[ql]));
+          if (need_mask) {
+            const int q = qbase + ql;
+            if (q < kj || q >= T) pr = 0.f;
+          }
+          sacc[mi][r] = pr;                             // P
+          pacc[mi][r] = pr * (pacc[mi][r] - Ds[ql]);    // dS
+        }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 pf = pack8(sacc[mi], t);
+          const bf16x8 sf = pack8(pacc[mi], t);
+#pragma unroll
+          for (int x = 0; x < HB; ++x) {
+            dv[x] = mfma(tr_frag(Os, x, mi * 32 + t * 16, lane), pf, dv[x]);
+            dk[x] = mfma(tr_frag(Qs, x, mi * 32 + t * 16, lane), sf, dk[x]);
+          }
+        }
+    }
+    if (tid < 64) {
+      Ln[tid] = ln;
+      Dn[tid] = dn;
+    }
+  };
+
+  int qb = qb0;
+  for (; qb + 1 < nqb; qb += 2) {
+    block(Q0, O0, L0, D0, Q1, O1, L1, D1, qb);
+    wait_vmem();
+    __syncthreads();
+    block(Q1, O1, L1, D1, Q0, O0, L0, D0, qb + 1);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (qb < nqb) block(Q0, O0, L0, D0, Q1, O1, L1, D1, qb);
+  wait_vmem();
+
+  if (kj >= T) return;
+  const float sc = p.scale;
+  float* dkp = p.dk32 + (tok0 + kj) * p.lddk + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      f32x4 w{dk[x][rg * 4 + 0] * sc, dk[x][rg * 4 + 1] * sc, dk[x][rg * 4 + 2] * sc, dk[x][rg * 4 + 3] * sc};
+      *reinterpret_cast<f32x4*>(dkp + x * 32 + 8 * rg + 4 * g) = w;
+    }
+  bf16* dvp = (bf16*)p.dv + (tok0 + kj) * p.lddv + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 w;
+      w.x = pack_bf16x2(dv[x][rg * 4 + 0], dv[x][rg * 4 + 1]);
+      w.y = pack_bf16x2(dv[x][rg * 4 + 2], dv[x][rg * 4 + 3]);
+      *reinterpret_cast<u32x2*>(dvp + x * 32 + 8 * rg + 4 * g) = w;
+    }
 }
 
 // ------------------------------------------------------------------ backward: D
@@ -577,7 +1083,7 @@ int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
   if (p.B * p.H * p.T == 0) return 0;
   if (dtype == 0) {
     dim3 grid((p.T + 127) / 128, p.B * p.H);
-    if (hd == 128) attn_fwd_mfma<128><<<grid, 256, 0, s>>>(p);
+    if (hd == 128) attn_fwd128<<<grid, 256, 0, s>>>(p);
     else if (hd == 64) attn_fwd_mfma<64><<<grid, 256, 0, s>>>(p);
     else return 7;
   } else {
@@ -598,8 +1104,8 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
     dim3 gk((p.T + 127) / 128, p.B * p.H);
     dim3 gq((p.T + 127) / 128, p.B * p.H);
     if (hd == 128) {
-      attn_bwd_dkdv_mfma<128><<<gk, 256, 0, s>>>(p);
-      attn_bwd_dq_mfma<128><<<gq, 256, 0, s>>>(p);
+      attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
+      attn_bwd_dq128<<<gq, 256, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_dkdv_mfma<64><<<gk, 256, 0, s>>>(p);
       attn_bwd_dq_mfma<64><<<gq, 256, 0, s>>>(p);

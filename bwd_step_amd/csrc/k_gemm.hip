@@ -296,6 +296,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   }
   if (kt < nk) {
     compute(As0, Bs0, As1, Bs1, kbeg + (kt + 1) * kBK, false);
+    wait_vmem();  // the tail's no-op loads still target LDS
   }
 
   // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so

@@ -159,29 +159,42 @@ struct QkArgs {
   float* r[2];  // [N, H]
 };
 
+// A lane owns 4 consecutive pairs (i .. i+3, i+HALF .. i+HALF+3), so a
+// vector of hd = 2*HALF elements takes HALF/4 lanes and loads are 8 bytes
+// (bf16) or 16 bytes (fp32) wide.
+template <int HALF>
+struct QkLanes {
+  static constexpr int LPV = HALF / 4;   // lanes per vector
+  static constexpr int VPW = 64 / LPV;   // vectors per wavefront
+};
+
 template <class T, int HALF>
 __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(QkArgs a, const float* __restrict__ cs, int N, int H,
                                                               int Tseq, float eps) {
-  constexpr int VPW = 64 / HALF;  // vectors per wavefront
+  constexpr int LPV = QkLanes<HALF>::LPV, VPW = QkLanes<HALF>::VPW;
   const int w = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / HALF;
-  const int i = lane % HALF;
+  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
+  const int i = (lane % LPV) * 4;
   const bool ok = vec < N * H;
   const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
   const T* src = (const T*)a.in[w] + (size_t)n * a.ld_in[w] + h * (2 * HALF);
-  float u0 = ok ? to_f32(src[i]) : 0.f, u1 = ok ? to_f32(src[i + HALF]) : 0.f;
-  float ss = u0 * u0 + u1 * u1;
+  f32x4 u0 = ok ? load4(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 u1 = ok ? load4(src + i + HALF) : f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = u0.x * u0.x + u0.y * u0.y + u0.z * u0.z + u0.w * u0.w + u1.x * u1.x + u1.y * u1.y + u1.z * u1.z +
+             u1.w * u1.w;
 #pragma unroll
-  for (int o = HALF / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  for (int o = LPV / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float rr = 1.0f / sqrtf(ss / (float)(2 * HALF) + eps);
   if (!ok) return;
   const int t = n % Tseq;
-  const float c = cs[2 * (t * HALF + i)], sn = cs[2 * (t * HALF + i) + 1];
-  const float y0 = u0 * rr, y1 = u1 * rr;
+  const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
+  const f32x4 cs01 = csp[0], cs23 = csp[1];  // (cos, sin) of pairs i, i+1 | i+2, i+3
+  const f32x4 c{cs01.x, cs01.z, cs23.x, cs23.z}, sn{cs01.y, cs01.w, cs23.y, cs23.w};
+  const f32x4 y0 = u0 * rr, y1 = u1 * rr;
   T* dst = (T*)a.out[w] + (size_t)n * a.ld_out[w] + h * (2 * HALF);
-  dst[i] = from_f32<T>(y0 * c - y1 * sn);
-  dst[i + HALF] = from_f32<T>(y0 * sn + y1 * c);
+  store4(dst + i, y0 * c - y1 * sn);
+  store4(dst + i + HALF, y0 * sn + y1 * c);
   if (i == 0) a.r[w][vec] = rr;
 }
 
@@ -201,31 +214,36 @@ struct QkBwdArgs {
 template <class T, int HALF>
 __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const float* __restrict__ cs, int N,
                                                               int H, int Tseq) {
-  constexpr int VPW = 64 / HALF;
+  constexpr int LPV = QkLanes<HALF>::LPV, VPW = QkLanes<HALF>::VPW;
   const int w = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / HALF;
-  const int i = lane % HALF;
+  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
+  const int i = (lane % LPV) * 4;
   const bool ok = vec < N * H;
   const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
   const int t = n % Tseq;
-  const float c = cs[2 * (t * HALF + i)], sn = cs[2 * (t * HALF + i) + 1];
-  const float* g = a.dv[w] + (size_t)n * a.ld_dv[w] + h * (2 * HALF);
+  const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
+  const f32x4 cs01 = csp[0], cs23 = csp[1];
+  const f32x4 c{cs01.x, cs01.z, cs23.x, cs23.z}, sn{cs01.y, cs01.w, cs23.y, cs23.w};
+  const float* gp = a.dv[w] + (size_t)n * a.ld_dv[w] + h * (2 * HALF);
   const T* vv = (const T*)a.v[w] + (size_t)n * a.ld_v[w] + h * (2 * HALF);
-  float g0 = ok ? g[i] : 0.f, g1 = ok ? g[i + HALF] : 0.f;
-  float v0 = ok ? to_f32(vv[i]) : 0.f, v1 = ok ? to_f32(vv[i + HALF]) : 0.f;
+  const f32x4 z{0.f, 0.f, 0.f, 0.f};
+  const f32x4 g0 = ok ? *reinterpret_cast<const f32x4*>(gp + i) : z;
+  const f32x4 g1 = ok ? *reinterpret_cast<const f32x4*>(gp + i + HALF) : z;
+  const f32x4 v0 = ok ? load4(vv + i) : z, v1 = ok ? load4(vv + i + HALF) : z;
   // R^T: rotation by -phi
-  const float dy0 = g0 * c + g1 * sn, dy1 = -g0 * sn + g1 * c;
-  const float y0 = v0 * c + v1 * sn, y1 = -v0 * sn + v1 * c;
-  float dot = dy0 * y0 + dy1 * y1;
+  const f32x4 dy0 = g0 * c + g1 * sn, dy1 = g1 * c - g0 * sn;
+  const f32x4 y0 = v0 * c + v1 * sn, y1 = v1 * c - v0 * sn;
+  const f32x4 pr = dy0 * y0 + dy1 * y1;
+  float dot = pr.x + pr.y + pr.z + pr.w;
 #pragma unroll
-  for (int o = HALF / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+  for (int o = LPV / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
   dot /= (float)(2 * HALF);
   if (!ok) return;
   const float rr = a.r[w][vec];
   T* out = (T*)a.du[w] + (size_t)n * a.ld_du[w] + h * (2 * HALF);
-  out[i] = from_f32<T>(rr * (dy0 - y0 * dot));
-  out[i + HALF] = from_f32<T>(rr * (dy1 - y1 * dot));
+  store4(out + i, (dy0 - y0 * dot) * rr);
+  store4(out + i + HALF, (dy1 - y1 * dot) * rr);
 }
 
 template <class T>
@@ -234,7 +252,7 @@ static int qk_fwd_dispatch(const QkArgs& a, const float* cs, int N, int H, int h
   const int vecs = N * H;
   if (vecs == 0) return 0;
   const int half = hd / 2;
-  const int vpb = 4 * (64 / half);
+  const int vpb = 4 * (64 / (half / 4));
   dim3 grid((vecs + vpb - 1) / vpb, 2);
   switch (half) {
     case 64: qknorm_rope_fwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, eps); break;
@@ -252,7 +270,7 @@ static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, in
   const int vecs = N * H;
   if (vecs == 0) return 0;
   const int half = hd / 2;
-  const int vpb = 4 * (64 / half);
+  const int vpb = 4 * (64 / (half / 4));
   dim3 grid((vecs + vpb - 1) / vpb, 2);
   switch (half) {
     case 64: qknorm_rope_bwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
