@@ -9,6 +9,11 @@ the roofline of the dominant kernel (the MFMA GEMM) measured live with HIP
 events, and the float64 oracle's throughput on this host (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--config d20|d26] [--no-cpu-baseline]
+
+--op attention | lmhead times one operation entry point instead of the step
+(the attention microbenchmark B16 x H10 x T2048 x hd128, or the fused LM head
++ cross-entropy on 32768 x 1280 x 65536); these lines are for profiling the
+kernels and carry their own metric, not the headline one.
 """
 
 import argparse
@@ -93,6 +98,44 @@ def cpu_baseline(cfg, seed=0):
     }
 
 
+def op_bench(args):
+    """Time nc_attention_fwd_bwd or nc_lmhead_ce_fwd_bwd on their benchmark shapes."""
+    import torch
+
+    from bwd_step_amd import ops
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    if args.op == "attention":
+        B, H, T, hd = 16, 10, 2048, 128
+        q, k, v, do = (torch.randn(B, T, H, hd, device=dev, generator=g).to(torch.bfloat16) for _ in range(4))
+        fn = lambda: ops.attention_fwd_bwd(q, k, v, do)  # noqa: E731
+        flops = 3 * 4.0 * hd * B * H * T * (T + 1) / 2  # causal model FLOPs, fwd + 2x bwd
+        name = "attention fwd+bwd (QK-norm, RoPE, causal) B16 H10 T2048 hd128"
+    else:
+        N, d, V = 32768, 1280, 65536
+        z = torch.randn(N, d, device=dev, generator=g).to(torch.bfloat16)
+        W = (0.02 * torch.randn(V, d, device=dev, generator=g)).to(torch.bfloat16)
+        y = torch.randint(0, V, (N,), device=dev, generator=g, dtype=torch.int32)
+        ws = ops.lmhead_ce_fwd_bwd(z, W, y)[3]
+        fn = lambda: ops.lmhead_ce_fwd_bwd(z, W, y, ws=ws)  # noqa: E731
+        flops = 3 * 2.0 * N * d * V
+        name = "LM head + softmax cross-entropy fwd+bwd N32768 d1280 V65536"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"metric": name + " model TFLOP/s", "value": round(flops / ms / 1e9, 1), "unit": "TFLOP/s",
+                      "ms_per_call": round(ms, 4), "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                      "data": "synthetic, seeded torch generator", "higher_is_better": True}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,11 +144,15 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--op", choices=["attention", "lmhead"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the data-parallel sharding across "
               "GPUs is described in DESIGN.md but not run", file=sys.stderr)
         sys.exit(2)
+    if args.op:
+        op_bench(args)
+        return
 
     import numpy as np
     import torch
