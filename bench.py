@@ -37,21 +37,23 @@ CONFIGS = {
 METRIC = "train tokens/sec + MFU (fwd+bwd) on 1 MI355X, depth-20 bf16 seq 2048"
 
 
-def model_flops_per_token(cfg):
+def model_flops_per_token(c):
     """Model FLOPs per token of one fwd+bwd (3x the forward matmul FLOPs).
 
     Matmuls: 6 * (L * (3*hh*d + d*hh + 2*F*d) + V*d).  Attention: per query
     t the causal row has t+1 keys; QK^T and PV cost 4*hd per (query, key)
     pair forward, 12*hd forward+backward, averaged over (T+1)/2 keys.
+    c: the resolved configuration dict of a bwd_step_amd.Model.
     """
-    d, H, hd, F, V, L, T = cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.d_ff, cfg.vocab, cfg.depth, cfg.seq_len
+    d, H, hd, F = c["d_model"], c["n_heads"], c["head_dim"], c["d_ff"]
+    V, L, T = c["vocab"], c["depth"], c["seq_len"]
     hh = H * hd
     mat = 6.0 * (L * (3 * hh * d + d * hh + 2 * F * d) + V * d)
     att = 12.0 * hd * H * L * (T + 1) / 2.0
     return mat + att
 
 
-def cpu_baseline(cfg, seed=0):
+def cpu_baseline(c, seed=0):
     """Time the float64 oracle on this host on a bounded sample of the workload.
 
     Sample: one sequence of 2048 tokens through the model at the workload's
@@ -65,6 +67,8 @@ def cpu_baseline(cfg, seed=0):
     import oracle
     import synth
 
+    cfg = oracle.derive_config(c["depth"], vocab=c["vocab"], seq_len=c["seq_len"], d_model=c["d_model"],
+                               n_heads=c["n_heads"], head_dim=c["head_dim"], d_ff=c["d_ff"])
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -75,12 +79,12 @@ def cpu_baseline(cfg, seed=0):
     times = []
     layers = [1, 2, 3]
     for L in layers:
-        c = oracle.derive_config(L, vocab=cfg.vocab, seq_len=cfg.seq_len, d_model=cfg.d_model,
-                                 n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ff=cfg.d_ff)
-        p = {k: v.astype(np.float64) for k, v in synth.weights(oracle.param_shapes(c), seed=seed, bf16=True).items()}
+        cl = oracle.derive_config(L, vocab=cfg.vocab, seq_len=cfg.seq_len, d_model=cfg.d_model,
+                                  n_heads=cfg.n_heads, head_dim=cfg.head_dim, d_ff=cfg.d_ff)
+        p = {k: v.astype(np.float64) for k, v in synth.weights(oracle.param_shapes(cl), seed=seed, bf16=True).items()}
         tok, tgt = synth.uniform_tokens(1, cfg.seq_len, cfg.vocab, seed=seed)
         t0 = time.perf_counter()
-        oracle.forward_backward(c, p, tok, tgt)
+        oracle.forward_backward(cl, p, tok, tgt)
         times.append(time.perf_counter() - t0)
         del p
     if limiter is not None:
@@ -158,15 +162,15 @@ def main():
     import torch
 
     import bwd_step_amd
-    import oracle
     import synth
 
     depth, B, dist = CONFIGS[args.config]
-    cfg = oracle.derive_config(depth)
-    T, V = cfg.seq_len, cfg.vocab
-    shapes = oracle.param_shapes(cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    model = bwd_step_amd.Model(depth, vocab=65536, seq_len=2048, max_batch=B, dtype="bf16")
+    cfg = model.config
+    T, V = cfg["seq_len"], cfg["vocab"]
+    shapes = [(name, (rows, cols)) for name, _, rows, cols in model.layout()]
 
     # seeded synthetic inputs: weights N(0, 0.02) rounded to bf16, ids uniform or Zipf(1.1)
     print(f"[bench] generating inputs ({args.config}: depth {depth}, B {B} x T {T})", file=sys.stderr, flush=True)
@@ -184,7 +188,6 @@ def main():
         tok, tgt = synth.zipf_tokens(B, T, V, seed=args.seed)
     tok_d, tgt_d = torch.from_numpy(tok).to(dev), torch.from_numpy(tgt).to(dev)
 
-    model = bwd_step_amd.Model(depth, vocab=V, seq_len=T, max_batch=B, dtype="bf16")
     loss = torch.empty((), dtype=torch.float32, device=dev)
     grads = torch.empty(model.param_count, dtype=torch.float32, device=dev)
     model.ensure_workspace(B)
@@ -249,8 +252,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded uniform token ids (Zipf(1.1) for d26), weights N(0,0.02) rounded to bf16",
         "config": {
-            "workload": (f"depth-{depth} fwd+bwd, d_model {cfg.d_model}, {cfg.n_heads}x{cfg.head_dim} heads, "
-                         f"MLP {cfg.d_ff} ReLU^2, untied vocab {V}, microbatch {B} x seq {T}"),
+            "workload": (f"depth-{depth} fwd+bwd, d_model {cfg['d_model']}, {cfg['n_heads']}x{cfg['head_dim']} heads, "
+                         f"MLP {cfg['d_ff']} ReLU^2, untied vocab {V}, microbatch {B} x seq {T}"),
             "global_batch": B,
             "seq_len": T,
             "depth": depth,
