@@ -20,6 +20,8 @@
 // Epilogues are fused so that each output is written once: fp32 store or
 // accumulate, bf16 store, residual add into the fp32 stream, ReLU² (stores
 // u and g = max(u,0)^2), and the ReLU² backward (du = dg * 2 max(u,0)).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,6 +34,7 @@ struct GemmParams {
   uint32_t a_bytes, b_bytes;  // extent of each operand (buffer bound; beyond it loads read 0)
   int M, N, K;
   int kchunk;  // K range per split (multiple of 64)
+  int splits;
   int tiles_m, tiles_n;
   EpiArgs e;
 };
@@ -60,11 +63,11 @@ __device__ __forceinline__ f32x4 load4(const T* p) {
   }
 }
 
-template <int EPI, class T>
+template <int EPI, class T = bf16>
 __device__ __forceinline__ void epi_apply4(const EpiArgs& e, int split, long i, long j, f32x4 v) {
-  if constexpr (EPI == EPI_F32) {
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
     f32x4* c = reinterpret_cast<f32x4*>(e.c32 + (size_t)split * e.split_stride + i * e.ldc + j);
-    if (e.beta) v += *c;
+    if constexpr (EPI == EPI_F32_ACC) v += *c;
     *c = v;
   } else if constexpr (EPI == EPI_RESID) {
     f32x4* c = reinterpret_cast<f32x4*>(e.c32 + i * e.ldc + j);
@@ -103,7 +106,8 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int split, long i, l
 }
 
 // ------------------------------------------------------------------ MFMA path
-constexpr int kBK = 64;
+constexpr int kBK = 32;  // K depth of one staged slice
+constexpr int kNS = 4;   // LDS stages: loads run three slices ahead of the MFMAs
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every operand: loads return 0
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -114,36 +118,31 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS element offset of the 16-byte chunk `kc` (0..7) of row `row` in a
-// k-contiguous [256][64] tile.  The chunk index is XOR-ed with
-// (row ^ row >> 3) & 7: any 8 consecutive rows get 8 different chunk slots of
-// a 128-byte bank window, and the even (and the odd) rows of any 16
-// consecutive rows get 8 different slots, so a 16-byte-per-lane fragment read
-// is conflict free whether the LDS serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ int swf(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int swz(int row, int kc) { return row * 64 + ((kc ^ swf(row)) << 3); }
+// k-contiguous slices are [256 rows][32 k] (64-byte rows of four 16-byte
+// chunks).  The chunk index is XOR-ed with ((row >> 1) ^ (row >> 3)) & 3, which
+// gives the 16-byte fragment reads of 8 (or 16) consecutive rows 8 (or 16)
+// different slots of a 128-byte (or 256-byte) bank window.
+__device__ __forceinline__ int swf(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz(int row, int kc) { return row * kBK + ((kc ^ swf(row)) << 3); }
 
-// m-contiguous tiles XOR the 16-byte chunk index with this function of (k & 3):
-// the four k-rows of a transposed read then land in four different 64-byte
-// quarters of a 256-byte bank window (bits 2-3) and, pairwise, in different
-// halves of a 128-byte window (bits 1-2), so the reads are conflict free
-// whether 16 or 32 lanes are served per cycle.
+// m-contiguous slices are [32 k][256 m]; the 16-byte chunk index is XOR-ed
+// with this function of (k & 3): the four k-rows of one transposed read land
+// in four different 64-byte quarters of a 256-byte bank window (bits 2-3)
+// and, pairwise, in different halves of a 128-byte window (bits 1-2).
 __device__ __forceinline__ int swk(int k) { const int r = k & 3; return 4 * r + 2 * ((r >> 1) & 1); }
 
-// Stage 1 KB (one wavefront instruction, 64 x 16 B) of a 64-deep K slice of a
+// Stage 1 KB (one wavefront instruction, 64 x 16 B) of a 32-deep slice of a
 // 256-row operand into LDS with an LDS-direct buffer load.  The LDS slots of
-// one instruction are consecutive, so every lane picks the global chunk that
-// belongs at its slot.  k-contiguous operands land as [256 rows][64 k] (chunk
-// swizzle swf); m-contiguous operands land as [64 k][256 m] (chunk swizzle
-// swk).  `b` (0..31, wave-uniform) selects the 1 KB block; `live` = false
-// turns the load into a no-op read of zeros.
+// one instruction are consecutive, so each lane picks the global chunk that
+// belongs at its slot.  `b` (0..15, wave-uniform) selects the block; `live`
+// = false turns the load into a read of zeros (an offset past the buffer).
 template <bool KMAJ>
 __device__ __forceinline__ void dma_block(rsrc_t rs, long ld, int row0, int k0, int rows_lim, int k_lim,
                                           bf16* lds, int b, int lane, bool live) {
   uint32_t off;
   if constexpr (KMAJ) {
-    const int row = b * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ swf(row);
+    const int row = b * 16 + (lane >> 2);
+    const int kc = (lane & 3) ^ swf(row);
     const int gr = row0 + row, gk = k0 + kc * 8;
     off = (live && gr < rows_lim && gk < k_lim) ? (uint32_t)(((long)gr * ld + gk) * 2) : kOOB;
   } else {
@@ -159,7 +158,7 @@ __device__ __forceinline__ v4i16 tr16(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)p);
 }
 
-// MFMA 32x32x16 operand fragment for tile rows rb..rb+31 and k-step s:
+// MFMA 32x32x16 operand fragment for tile rows rb..rb+31 and k-step s (0, 1):
 // lane l holds row rb + (l & 31) and k = 16 s + 8 (l >> 5) + 0..7.
 template <bool KMAJ>
 __device__ __forceinline__ bf16x8 read_frag(const bf16* lds, int rb, int s, int lane) {
@@ -183,39 +182,60 @@ __device__ __forceinline__ bf16x8 read_frag(const bf16* lds, int rb, int s, int 
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Vector memory operations retire in issue order: with three slices (8 loads
+// each per wavefront) in flight, 16 outstanding means the oldest slice has
+// landed in LDS.  The barrier then publishes it to the whole workgroup.  (A
+// __syncthreads() would also wait for the two younger slices.)
+__device__ __forceinline__ void wait_oldest_slice_and_sync() {
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+}
 
 template <bool AK, bool BKM, int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  // two LDS stages per operand, as four separate objects so that the
-  // compiler can tell the in-flight LDS-direct loads (into one stage) from the
-  // fragment reads (of the other) and does not wait on the loads
+  // four LDS stages per operand, as separate objects so that the compiler can
+  // tell the in-flight LDS-direct loads (into three stages) from the fragment
+  // reads (of the fourth) and does not wait on them
   __shared__ __attribute__((aligned(1024))) bf16 As0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) bf16 As1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16 As2[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16 As3[BM * kBK];
   __shared__ __attribute__((aligned(1024))) bf16 Bs0[BN * kBK];
   __shared__ __attribute__((aligned(1024))) bf16 Bs1[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16 Bs2[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16 Bs3[BN * kBK];
 
-  // Tile order: workgroup ids are dealt round-robin to the 8 XCDs; give each
-  // XCD a contiguous run of logical tiles, walked in column groups of 8
-  // tile-rows so that neighbours share A rows and B rows in the XCD's L2.
+  // Persistent: workgroup w owns work items (tile, K split) w', w' + G, ...
+  // (G = grid size).  Workgroup ids are dealt round-robin to the 8 XCDs, so
+  // w' gives every XCD a contiguous run of logical items per round; tiles are
+  // walked in column groups of 8 tile-rows so that neighbours share A rows and
+  // B columns in the XCD's L2.
+  const int G = gridDim.x;
   const int ntiles = p.tiles_m * p.tiles_n;
-  int b = blockIdx.x;
-  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
-  constexpr int GROUP = 8;
-  const int group_span = GROUP * p.tiles_n;
-  const int grp = b / group_span;
-  const int first_m = grp * GROUP;
-  const int gsize = min(p.tiles_m - first_m, GROUP);
-  const int tm = first_m + (b % group_span) % gsize;
-  const int tn = (b % group_span) / gsize;
+  const int nitems = ntiles * p.splits;
+  const int wfirst = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  if (wfirst >= nitems) return;
 
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int split = blockIdx.z;
-  const int kbeg = split * p.kchunk;
-  const int kend = min(p.K, kbeg + p.kchunk);
-  const int nk = (kend - kbeg + kBK - 1) / kBK;
+  struct Item {
+    int m0, n0, kbeg, kend, nk, split;
+  };
+  auto item = [&](int i) {
+    Item r;
+    r.split = i / ntiles;
+    const int t = i - r.split * ntiles;
+    constexpr int GROUP = 8;
+    const int group_span = GROUP * p.tiles_n;
+    const int first_m = (t / group_span) * GROUP;
+    const int gsize = min(p.tiles_m - first_m, GROUP);
+    r.m0 = (first_m + (t % group_span) % gsize) * BM;
+    r.n0 = ((t % group_span) / gsize) * BN;
+    r.kbeg = r.split * p.kchunk;
+    r.kend = min(p.K, r.kbeg + p.kchunk);
+    r.nk = max((r.kend - r.kbeg + kBK - 1) / kBK, 0);
+    return r;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,13 +249,22 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
 
-  // One staged 64-deep K slice: four 16-deep MFMA steps.  While step s
-  // multiplies, the fragments of step s + 1 are read from LDS and a quarter of
-  // the next slice's LDS-direct loads (2 blocks of A, 2 of B per wave) are
-  // issued into the other buffer; sched_group_barrier interleaves the three
-  // instruction streams so that the matrix cores are never left waiting for
-  // their issue.
-  auto compute = [&](const bf16* as, const bf16* bs, bf16* an, bf16* bn, int k_next, bool live) {
+  // Load one whole slice (4 blocks of A and 4 of B per wavefront).
+  auto load_slice = [&](bf16* an, bf16* bn, int m_, int n_, int k_, int kend_, bool live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma_block<AK>(ra, p.lda, m_, k_, p.M, kend_, an, wv * 4 + q, lane, live);
+      dma_block<BKM>(rb, p.ldb, n_, k_, p.N, kend_, bn, wv * 4 + q, lane, live);
+    }
+  };
+
+  // One staged 32-deep slice: two 16-deep MFMA steps.  While step 0
+  // multiplies, the fragments of step 1 are read from LDS; the loads of the
+  // slice three ahead are spread over both steps.  sched_group_barrier
+  // interleaves the instruction streams so that the matrix cores are not left
+  // waiting for their issue.
+  auto compute = [&](const bf16* as, const bf16* bs, bf16* an, bf16* bn, int m_next, int n_next, int k_next,
+                     int kend_next, bool live) {
     bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
     for (int a = 0; a < FM; ++a) af[0][a] = read_frag<AK>(as, wm * TM + a * 32, 0, lane);
@@ -244,78 +273,105 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < kBK / 16) {
+      if (s == 0) {
 #pragma unroll
-        for (int a = 0; a < FM; ++a) af[cur ^ 1][a] = read_frag<AK>(as, wm * TM + a * 32, s + 1, lane);
+        for (int a = 0; a < FM; ++a) af[1][a] = read_frag<AK>(as, wm * TM + a * 32, 1, lane);
 #pragma unroll
-        for (int c = 0; c < FN; ++c) bfr[cur ^ 1][c] = read_frag<BKM>(bs, wn * TN + c * 32, s + 1, lane);
+        for (int c = 0; c < FN; ++c) bfr[1][c] = read_frag<BKM>(bs, wn * TN + c * 32, 1, lane);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        dma_block<AK>(ra, p.lda, m0, k_next, p.M, kend, an, wv * 8 + 2 * s + q, lane, live);
-        dma_block<BKM>(rb, p.ldb, n0, k_next, p.N, kend, bn, wv * 8 + 2 * s + q, lane, live);
+        dma_block<AK>(ra, p.lda, m_next, k_next, p.M, kend_next, an, wv * 4 + 2 * s + q, lane, live);
+        dma_block<BKM>(rb, p.ldb, n_next, k_next, p.N, kend_next, bn, wv * 4 + 2 * s + q, lane, live);
       }
 #pragma unroll
       for (int a = 0; a < FM; ++a)
 #pragma unroll
         for (int c = 0; c < FN; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][c], af[cur][a], acc[a][c], 0, 0, 0);
-      // interleave: MFMA, LDS read, MFMA, LDS read, ... with the 4 LDS-direct loads spread out
-      // LDS read instructions per step (none are left on the last step; its
-      // read groups stay empty)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][c], af[s][a], acc[a][c], 0, 0, 0);
+      // LDS read instructions of step 1 (read during step 0)
       constexpr int NR = (AK ? FM : 2 * FM) + (BKM ? FN : 2 * FN);
 #pragma unroll
       for (int i = 0; i < FM * FN; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if ((i & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (s == 0 && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if ((i & 7) == 3) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
       }
-      if (NR > FM * FN) __builtin_amdgcn_sched_group_barrier(0x100, NR - FM * FN, 0);
+      if (s == 0 && NR > FM * FN) __builtin_amdgcn_sched_group_barrier(0x100, NR - FM * FN, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (nk > 0) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      dma_block<AK>(ra, p.lda, m0, kbeg, p.M, kend, As0, wv * 8 + q, lane, true);
-      dma_block<BKM>(rb, p.ldb, n0, kbeg, p.N, kend, Bs0, wv * 8 + q, lane, true);
-    }
-  }
-  wait_vmem();
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    compute(As0, Bs0, As1, Bs1, kbeg + (kt + 1) * kBK, true);
-    wait_vmem();
-    __syncthreads();
-    compute(As1, Bs1, As0, Bs0, kbeg + (kt + 2) * kBK, kt + 2 < nk);
-    wait_vmem();
-    __syncthreads();
-  }
-  if (kt < nk) {
-    compute(As0, Bs0, As1, Bs1, kbeg + (kt + 1) * kBK, false);
-    wait_vmem();  // the tail's no-op loads still target LDS
-  }
-
   // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so
   // a lane holds output row m = lane & 31 of its block and, in register
   // group q = r / 4, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
+  // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so
+  // a lane holds output row m = lane & 31 of its block and, in register
+  // group q = r / 4, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
+  auto epilogue = [&](const Item& ci) {
 #pragma unroll
-  for (int a = 0; a < FM; ++a) {
-    const long i = m0 + wm * TM + a * 32 + (lane & 31);
-    if (i >= p.M) continue;
+    for (int a = 0; a < FM; ++a) {
+      const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
 #pragma unroll
-    for (int c = 0; c < FN; ++c)
+      for (int c = 0; c < FN; ++c) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const long j = n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
-        if (j < p.N)
-          epi_apply4<EPI, bf16>(p.e, split, i, j,
-                                f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]});
+        for (int q = 0; q < 4; ++q) {
+          const long j = ci.n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
+          if (i < p.M && j < p.N)
+            epi_apply4<EPI>(p.e, ci.split, i, j,
+                            f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2],
+                                  acc[a][c][4 * q + 3]});
+        }
+        if constexpr (EPI == EPI_F32_ACC) __builtin_amdgcn_sched_barrier(0);
       }
+    }
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
+  };
+
+  int it = wfirst;
+  Item ci = item(it);
+  // prologue: the first three slices
+  load_slice(As0, Bs0, ci.m0, ci.n0, ci.kbeg, ci.kend, 0 < ci.nk);
+  load_slice(As1, Bs1, ci.m0, ci.n0, ci.kbeg + kBK, ci.kend, 1 < ci.nk);
+  load_slice(As2, Bs2, ci.m0, ci.n0, ci.kbeg + 2 * kBK, ci.kend, 2 < ci.nk);
+  wait_oldest_slice_and_sync();
+
+#define NC_STEP(S, NEXT_STAGE, M_, N_, K_, KEND_, LIVE)                                     \
+  compute(As##S, Bs##S, As##NEXT_STAGE, Bs##NEXT_STAGE, M_, N_, K_, KEND_, LIVE);          \
+  wait_oldest_slice_and_sync();
+
+  // Work items in turn.  Each runs a multiple of four 32-deep slices (stage i
+  // holds slices i, i+4, ...); missing slices load zeros and add exactly 0.
+  // The last slices of an item prefetch the first three of the next item, so
+  // only the very first slices wait for their loads.
+  for (;;) {
+    const int nk4 = (max(ci.nk, 1) + 3) & ~3;
+    const int nit = it + G;
+    const bool has_next = nit < nitems;
+    const Item nx = has_next ? item(nit) : ci;
+    const bool nlive = has_next;
+    int kt = 0;
+    for (; kt + 4 < nk4; kt += 4) {
+      NC_STEP(0, 3, ci.m0, ci.n0, ci.kbeg + (kt + 3) * kBK, ci.kend, kt + 3 < ci.nk)
+      NC_STEP(1, 0, ci.m0, ci.n0, ci.kbeg + (kt + 4) * kBK, ci.kend, kt + 4 < ci.nk)
+      NC_STEP(2, 1, ci.m0, ci.n0, ci.kbeg + (kt + 5) * kBK, ci.kend, kt + 5 < ci.nk)
+      NC_STEP(3, 2, ci.m0, ci.n0, ci.kbeg + (kt + 6) * kBK, ci.kend, kt + 6 < ci.nk)
+    }
+    // last four slices: after the item's own slice kt + 3, prefetch the next item
+    NC_STEP(0, 3, ci.m0, ci.n0, ci.kbeg + (kt + 3) * kBK, ci.kend, kt + 3 < ci.nk)
+    NC_STEP(1, 0, nx.m0, nx.n0, nx.kbeg, nx.kend, nlive && 0 < nx.nk)
+    NC_STEP(2, 1, nx.m0, nx.n0, nx.kbeg + kBK, nx.kend, nlive && 1 < nx.nk)
+    NC_STEP(3, 2, nx.m0, nx.n0, nx.kbeg + 2 * kBK, nx.kend, nlive && 2 < nx.nk)
+    epilogue(ci);
+    if (!has_next) break;
+    it = nit;
+    ci = nx;
   }
+#undef NC_STEP
+  wait_vmem();  // the final no-op loads still target LDS
 }
 
 // ------------------------------------------------------------------ SIMT fp32 path
@@ -399,6 +455,19 @@ static void launch_simt(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStr
   else gemm_simt_kernel<false, false, EPI><<<grid, 256, 0, s>>>(p);
 }
 
+// Compute units of the current device (cached per device).
+static int num_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 int gemm_splits(int M, int N, int K, int dtype) {
   const int t = dtype == 0 ? 256 : 64;
   const long tiles = (long)((M + t - 1) / t) * ((N + t - 1) / t);
@@ -438,7 +507,8 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   if (g.epi == EPI_F32 && g.splitk_ws) splits = gemm_splits(g.M, g.N, g.K, g.dtype);
   int kchunk = g.K;
   if (splits > 1) {
-    kchunk = ((g.K + splits - 1) / splits + kBK - 1) / kBK * kBK;
+    // chunks of a multiple of four 32-deep slices (the kernel runs them in fours)
+    kchunk = ((g.K + splits - 1) / splits + 4 * kBK - 1) / (4 * kBK) * (4 * kBK);
     splits = (g.K + kchunk - 1) / kchunk;
   }
   if (splits > 1) {
@@ -448,11 +518,21 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
     p.e.split_stride = (long)g.M * g.N;
   }
   p.kchunk = kchunk > 0 ? kchunk : 1;
+  p.splits = splits;
   dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  if (g.dtype == 0) {
+    // persistent: one workgroup per compute unit (each holds 128 KB of LDS)
+    const long items = (long)p.tiles_m * p.tiles_n * splits;
+    grid = dim3((unsigned)std::min<long>(items, num_cus()), 1, 1);
+  }
   // K == 0 runs the kernels with an empty k-loop: the epilogue sees zeros.
   if (g.dtype == 0) {
     switch (g.epi) {
-      case EPI_F32: launch_mfma<EPI_F32>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_F32:
+        // accumulation into C gets its own kernel (the C loads need registers)
+        if (p.e.beta) launch_mfma<EPI_F32_ACC>(p, g.a_k, g.b_k, grid, s);
+        else launch_mfma<EPI_F32>(p, g.a_k, g.b_k, grid, s);
+        break;
       case EPI_RESID: launch_mfma<EPI_RESID>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_LP: launch_mfma<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_RELU2: launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;

@@ -8,7 +8,8 @@
 namespace nc {
 
 // ---- GEMM epilogues
-enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4 };
+enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4,
+       EPI_F32_ACC = 5 /* internal to the GEMM: EPI_F32 with beta = 1 */ };
 
 struct EpiArgs {
   float* c32 = nullptr;  // EPI_F32 (beta selects store / accumulate), EPI_RESID
