@@ -7,13 +7,13 @@
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A 256-thread
 // workgroup owns a 256x256 output tile; its four wavefronts each own 128x128
-// (4x4 MFMA blocks of 32x32).  K advances 64 at a time through two LDS
-// buffers (the next tile's global loads are in flight while the current one
-// is multiplied).  LDS rows are 64 bf16 (128 B) with the 16-byte chunk index
-// XOR-swizzled by (row & 7), so the MFMA fragment reads (one 16-byte chunk per
-// lane, 32 consecutive rows) are bank-conflict free.  Operands whose
-// reduction index is not contiguous in memory are loaded as 8x8 bf16 blocks
-// and transposed in registers before the LDS store.
+// (4x4 MFMA blocks of 32x32).  The grid is persistent (one workgroup per
+// compute unit walking (tile, K split) items).  K advances through four LDS
+// stages of 32-deep slices filled by LDS-direct buffer loads issued three
+// slices ahead.  k-contiguous slices hold 64-byte rows with an XOR-swizzled
+// 16-byte chunk index; operands whose reduction index is strided are staged
+// as they lie in memory (k rows of 256 m) and read transposed with
+// ds_read_b64_tr_b16.  Both layouts are read without bank conflicts.
 //
 // fp32 debug path: a plain 64x64 LDS-tiled SIMT kernel with the same epilogues.
 //
@@ -33,7 +33,7 @@ struct GemmParams {
   long lda, ldb;
   uint32_t a_bytes, b_bytes;  // extent of each operand (buffer bound; beyond it loads read 0)
   int M, N, K;
-  int kchunk;  // K range per split (multiple of 64)
+  int kchunk;  // K range per split (multiple of 128 when split)
   int splits;
   int tiles_m, tiles_n;
   EpiArgs e;
@@ -119,10 +119,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // k-contiguous slices are [256 rows][32 k] (64-byte rows of four 16-byte
-// chunks).  The chunk index is XOR-ed with ((row >> 1) ^ (row >> 3)) & 3, which
-// gives the 16-byte fragment reads of 8 (or 16) consecutive rows 8 (or 16)
-// different slots of a 128-byte (or 256-byte) bank window.
-__device__ __forceinline__ int swf(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// chunks); the chunk index is XOR-ed with (row >> 2) & 3.  A 16-byte LDS read
+// of a wavefront is served in four 16-lane phases over 64 four-byte banks
+// (measured on gfx950): a phase is the four lane quads 4q .. 4q+3 of one
+// 32-lane half whose quad index q has the same bit parity.  A fragment read
+// puts 32 consecutive rows on the lanes of a half, so the four quads of a
+// phase have distinct q mod 4 = (row >> 2) & 3, and the four rows of a quad
+// lie in distinct 64-byte quarters of the 256-byte bank window: the swizzled
+// chunks fill all 16 slots.
+__device__ __forceinline__ int swf(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz(int row, int kc) { return row * kBK + ((kc ^ swf(row)) << 3); }
 
 // m-contiguous slices are [32 k][256 m]; the 16-byte chunk index is XOR-ed
@@ -131,27 +136,36 @@ __device__ __forceinline__ int swz(int row, int kc) { return row * kBK + ((kc ^ 
 // and, pairwise, in different halves of a 128-byte window (bits 1-2).
 __device__ __forceinline__ int swk(int k) { const int r = k & 3; return 4 * r + 2 * ((r >> 1) & 1); }
 
-// Stage 1 KB (one wavefront instruction, 64 x 16 B) of a 32-deep slice of a
-// 256-row operand into LDS with an LDS-direct buffer load.  The LDS slots of
-// one instruction are consecutive, so each lane picks the global chunk that
-// belongs at its slot.  `b` (0..15, wave-uniform) selects the block; `live`
-// = false turns the load into a read of zeros (an offset past the buffer).
+// Loads of a 32-deep slice of a 256-row operand: 16 blocks of 1 KB, one
+// wavefront LDS-direct buffer load (64 lanes x 16 B) each, into consecutive
+// LDS slots; each lane picks the global chunk that belongs at its slot.  The
+// per-lane byte offset of block b relative to the slice's first k is fixed
+// for a work item (computed once); the slice itself is selected by moving the
+// buffer's base address (scalar work), and a slice past the item's K range
+// gets a zero-length buffer, so every one of its loads reads 0.  Rows past
+// the operand (m >= M) get an offset past any buffer.
 template <bool KMAJ>
-__device__ __forceinline__ void dma_block(rsrc_t rs, long ld, int row0, int k0, int rows_lim, int k_lim,
-                                          bf16* lds, int b, int lane, bool live) {
-  uint32_t off;
+__device__ __forceinline__ uint32_t dma_voff(long ld, int row0, int rows_lim, int b, int lane) {
   if constexpr (KMAJ) {
     const int row = b * 16 + (lane >> 2);
     const int kc = (lane & 3) ^ swf(row);
-    const int gr = row0 + row, gk = k0 + kc * 8;
-    off = (live && gr < rows_lim && gk < k_lim) ? (uint32_t)(((long)gr * ld + gk) * 2) : kOOB;
+    const int gr = row0 + row;
+    return gr < rows_lim ? (uint32_t)(((long)gr * ld + kc * 8) * 2) : kOOB;
   } else {
     const int k = 2 * b + (lane >> 5);
     const int mc = (lane & 31) ^ swk(k);
-    const int gk = k0 + k, gm = row0 + mc * 8;
-    off = (live && gk < k_lim && gm < rows_lim) ? (uint32_t)(((long)gk * ld + gm) * 2) : kOOB;
+    const int gm = row0 + mc * 8;
+    return gm < rows_lim ? (uint32_t)(((long)k * ld + gm) * 2) : kOOB;
   }
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + b * 512), 16, off, 0, 0, 0);
+}
+// The k offset within the slice of the chunk a lane loads in block b
+// (k-contiguous operands only; used to cut a final partial slice).
+__device__ __forceinline__ int dma_kofs(int b, int lane) {
+  const int row = b * 16 + (lane >> 2);
+  return ((lane & 3) ^ swf(row)) * 8;
+}
+__device__ __forceinline__ void dma_issue(rsrc_t rs, uint32_t voff, bf16* lds, int b) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + b * 512), 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ v4i16 tr16(const bf16* p) {
@@ -182,15 +196,25 @@ __device__ __forceinline__ bf16x8 read_frag(const bf16* lds, int rb, int s, int 
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Vector memory operations retire in issue order: with three slices (8 loads
-// each per wavefront) in flight, 16 outstanding means the oldest slice has
-// landed in LDS.  The barrier then publishes it to the whole workgroup.  (A
-// __syncthreads() would also wait for the two younger slices.)
-__device__ __forceinline__ void wait_oldest_slice_and_sync() {
+// Vector memory operations retire in issue order.  Loads run three slices
+// ahead and each slice is issued as two halves of 4 loads per wavefront, one
+// per MFMA step.  In the middle of slice s the loads still allowed in flight
+// are those of slice s+2 and the first half of s+3 (12); after them slice s+1
+// has landed in LDS, and the barrier publishes it to the whole workgroup
+// (a __syncthreads() would also wait for the younger slices).  lgkmcnt(0):
+// this wavefront's reads of slice s are complete, so after the barrier the
+// loads that follow may overwrite the stage of slice s-1 (stage (s+3) mod 4).
+__device__ __forceinline__ void wait_next_slice_and_sync() {
+  asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Prologue: three slices (24 loads) issued, slice 0 needed.
+__device__ __forceinline__ void wait_first_slice_and_sync() {
   asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
 }
 
-template <bool AK, bool BKM, int EPI>
+// KTAIL: a k-contiguous operand has K % 32 != 0, so the last slice of the
+// last K split is cut per lane (a k-strided operand ends with its buffer).
+template <bool AK, bool BKM, int EPI, bool KTAIL>
 __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -240,8 +264,35 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wv / WN, wn = wv % WN;
-  const rsrc_t ra = make_rsrc(p.A, p.a_bytes);
-  const rsrc_t rb = make_rsrc(p.B, p.b_bytes);
+  // byte step of the buffer base per k
+  const long a_kstep = AK ? 2 : p.lda * 2, b_kstep = BKM ? 2 : p.ldb * 2;
+  // buffer of the slice starting at k0 (a zero-length one when it is dead)
+  auto slice_rsrc = [&](const void* base, uint32_t bytes, long kstep, int k0, bool live) {
+    const long sh = live ? (long)k0 * kstep : 0;
+    return make_rsrc((const char*)base + sh, live ? bytes - (uint32_t)sh : 0u);
+  };
+  // per-lane offsets of this wavefront's four blocks of A and B for an item
+  auto item_voff = [&](const Item& it_, uint32_t* va, uint32_t* vb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      va[q] = dma_voff<AK>(p.lda, it_.m0, p.M, wv * 4 + q, lane);
+      vb[q] = dma_voff<BKM>(p.ldb, it_.n0, p.N, wv * 4 + q, lane);
+    }
+  };
+  // The loads of blocks q0, q0+1 of the slice starting at k0 (ending the K range at kend).
+  auto issue2 = [&](bf16* an, bf16* bn, const uint32_t* va, const uint32_t* vb, rsrc_t rsa, rsrc_t rsb, int q0,
+                    int k0, int kend) {
+#pragma unroll
+    for (int q = q0; q < q0 + 2; ++q) {
+      uint32_t oa = va[q], ob = vb[q];
+      if constexpr (KTAIL) {
+        if (AK && k0 + dma_kofs(wv * 4 + q, lane) >= kend) oa = kOOB;
+        if (BKM && k0 + dma_kofs(wv * 4 + q, lane) >= kend) ob = kOOB;
+      }
+      dma_issue(rsa, oa, an, wv * 4 + q);
+      dma_issue(rsb, ob, bn, wv * 4 + q);
+    }
+  };
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -250,61 +301,62 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
 
   // Load one whole slice (4 blocks of A and 4 of B per wavefront).
-  auto load_slice = [&](bf16* an, bf16* bn, int m_, int n_, int k_, int kend_, bool live) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dma_block<AK>(ra, p.lda, m_, k_, p.M, kend_, an, wv * 4 + q, lane, live);
-      dma_block<BKM>(rb, p.ldb, n_, k_, p.N, kend_, bn, wv * 4 + q, lane, live);
-    }
+  auto load_slice = [&](bf16* an, bf16* bn, const uint32_t* va, const uint32_t* vb, const Item& it_, int j) {
+    const int k0 = it_.kbeg + j * kBK;
+    const bool live = j < it_.nk;
+    const rsrc_t rsa = slice_rsrc(p.A, p.a_bytes, a_kstep, k0, live);
+    const rsrc_t rsb = slice_rsrc(p.B, p.b_bytes, b_kstep, k0, live);
+    issue2(an, bn, va, vb, rsa, rsb, 0, k0, it_.kend);
+    issue2(an, bn, va, vb, rsa, rsb, 2, k0, it_.kend);
   };
 
-  // One staged 32-deep slice: two 16-deep MFMA steps.  While step 0
-  // multiplies, the fragments of step 1 are read from LDS; the loads of the
-  // slice three ahead are spread over both steps.  sched_group_barrier
-  // interleaves the instruction streams so that the matrix cores are not left
-  // waiting for their issue.
-  auto compute = [&](const bf16* as, const bf16* bs, bf16* an, bf16* bn, int m_next, int n_next, int k_next,
-                     int kend_next, bool live) {
-    bf16x8 af[2][FM], bfr[2][FN];
+  // Operand fragments: f0 (k 0..15 of a slice) is read one slice ahead, f1
+  // (k 16..31) during the slice's first MFMA step.
+  bf16x8 fa0[FM], fb0[FN];
+  auto read_step = [&](const bf16* as, const bf16* bs, int st, bf16x8* fa, bf16x8* fb) {
 #pragma unroll
-    for (int a = 0; a < FM; ++a) af[0][a] = read_frag<AK>(as, wm * TM + a * 32, 0, lane);
+    for (int a = 0; a < FM; ++a) fa[a] = read_frag<AK>(as, wm * TM + a * 32, st, lane);
 #pragma unroll
-    for (int c = 0; c < FN; ++c) bfr[0][c] = read_frag<BKM>(bs, wn * TN + c * 32, 0, lane);
+    for (int c = 0; c < FN; ++c) fb[c] = read_frag<BKM>(bs, wn * TN + c * 32, st, lane);
+  };
+  // One MFMA step over the wavefront's 4x4 blocks, interleaved (by
+  // sched_group_barrier) with the NR LDS fragment reads and the 4 loads
+  // issued in the same step, so the matrix cores are not left waiting for
+  // their issue.
+  constexpr int NR = (AK ? FM : 2 * FM) + (BKM ? FN : 2 * FN);
+  auto mfma_step = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int c = 0; c < FN; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c], fa[a], acc[a][c], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FM * FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if ((i & 7) == 3) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+    if (NR > FM * FN) __builtin_amdgcn_sched_group_barrier(0x100, NR - FM * FN, 0);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      if (s == 0) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a) af[1][a] = read_frag<AK>(as, wm * TM + a * 32, 1, lane);
-#pragma unroll
-        for (int c = 0; c < FN; ++c) bfr[1][c] = read_frag<BKM>(bs, wn * TN + c * 32, 1, lane);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        dma_block<AK>(ra, p.lda, m_next, k_next, p.M, kend_next, an, wv * 4 + 2 * s + q, lane, live);
-        dma_block<BKM>(rb, p.ldb, n_next, k_next, p.N, kend_next, bn, wv * 4 + 2 * s + q, lane, live);
-      }
-#pragma unroll
-      for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int c = 0; c < FN; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][c], af[s][a], acc[a][c], 0, 0, 0);
-      // LDS read instructions of step 1 (read during step 0)
-      constexpr int NR = (AK ? FM : 2 * FM) + (BKM ? FN : 2 * FN);
-#pragma unroll
-      for (int i = 0; i < FM * FN; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (s == 0 && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if ((i & 7) == 3) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      }
-      if (s == 0 && NR > FM * FN) __builtin_amdgcn_sched_group_barrier(0x100, NR - FM * FN, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  };
+  // One staged 32-deep slice (in as/bs; the next slice is in as_nx/bs_nx) and
+  // the loads of slice j of item it_ (into an/bn, with the item's offsets va/vb).
+  auto compute = [&](const bf16* as, const bf16* bs, const bf16* as_nx, const bf16* bs_nx, bf16* an, bf16* bn,
+                     const uint32_t* va, const uint32_t* vb, const Item& it_, int j, bool alive) {
+    const int k0 = it_.kbeg + j * kBK;
+    const bool live = alive && j < it_.nk;
+    const rsrc_t rsa = slice_rsrc(p.A, p.a_bytes, a_kstep, k0, live);
+    const rsrc_t rsb = slice_rsrc(p.B, p.b_bytes, b_kstep, k0, live);
+    bf16x8 fa1[FM], fb1[FN];
+    issue2(an, bn, va, vb, rsa, rsb, 0, k0, it_.kend);
+    read_step(as, bs, 1, fa1, fb1);
+    mfma_step(fa0, fb0);
+    wait_next_slice_and_sync();
+    issue2(an, bn, va, vb, rsa, rsb, 2, k0, it_.kend);
+    read_step(as_nx, bs_nx, 0, fa0, fb0);
+    mfma_step(fa1, fb1);
   };
 
-  // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so
-  // a lane holds output row m = lane & 31 of its block and, in register
-  // group q = r / 4, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
   // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so
   // a lane holds output row m = lane & 31 of its block and, in register
   // group q = r / 4, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
@@ -333,15 +385,18 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
 
   int it = wfirst;
   Item ci = item(it);
-  // prologue: the first three slices
-  load_slice(As0, Bs0, ci.m0, ci.n0, ci.kbeg, ci.kend, 0 < ci.nk);
-  load_slice(As1, Bs1, ci.m0, ci.n0, ci.kbeg + kBK, ci.kend, 1 < ci.nk);
-  load_slice(As2, Bs2, ci.m0, ci.n0, ci.kbeg + 2 * kBK, ci.kend, 2 < ci.nk);
-  wait_oldest_slice_and_sync();
+  uint32_t va[4], vb[4];
+  item_voff(ci, va, vb);
+  // prologue: the first three slices, then the first fragments
+  load_slice(As0, Bs0, va, vb, ci, 0);
+  load_slice(As1, Bs1, va, vb, ci, 1);
+  load_slice(As2, Bs2, va, vb, ci, 2);
+  wait_first_slice_and_sync();
+  read_step(As0, Bs0, 0, fa0, fb0);
 
-#define NC_STEP(S, NEXT_STAGE, M_, N_, K_, KEND_, LIVE)                                     \
-  compute(As##S, Bs##S, As##NEXT_STAGE, Bs##NEXT_STAGE, M_, N_, K_, KEND_, LIVE);          \
-  wait_oldest_slice_and_sync();
+  // Slice in stage S; the next slice is in stage S+1 and the loads go to S+3 (mod 4).
+#define NC_STEP(S, S1, S3, VA, VB, IT, J, ALIVE) \
+  compute(As##S, Bs##S, As##S1, Bs##S1, As##S3, Bs##S3, VA, VB, IT, J, ALIVE);
 
   // Work items in turn.  Each runs a multiple of four 32-deep slices (stage i
   // holds slices i, i+4, ...); missing slices load zeros and add exactly 0.
@@ -352,23 +407,29 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     const int nit = it + G;
     const bool has_next = nit < nitems;
     const Item nx = has_next ? item(nit) : ci;
-    const bool nlive = has_next;
     int kt = 0;
     for (; kt + 4 < nk4; kt += 4) {
-      NC_STEP(0, 3, ci.m0, ci.n0, ci.kbeg + (kt + 3) * kBK, ci.kend, kt + 3 < ci.nk)
-      NC_STEP(1, 0, ci.m0, ci.n0, ci.kbeg + (kt + 4) * kBK, ci.kend, kt + 4 < ci.nk)
-      NC_STEP(2, 1, ci.m0, ci.n0, ci.kbeg + (kt + 5) * kBK, ci.kend, kt + 5 < ci.nk)
-      NC_STEP(3, 2, ci.m0, ci.n0, ci.kbeg + (kt + 6) * kBK, ci.kend, kt + 6 < ci.nk)
+      NC_STEP(0, 1, 3, va, vb, ci, kt + 3, true)
+      NC_STEP(1, 2, 0, va, vb, ci, kt + 4, true)
+      NC_STEP(2, 3, 1, va, vb, ci, kt + 5, true)
+      NC_STEP(3, 0, 2, va, vb, ci, kt + 6, true)
     }
     // last four slices: after the item's own slice kt + 3, prefetch the next item
-    NC_STEP(0, 3, ci.m0, ci.n0, ci.kbeg + (kt + 3) * kBK, ci.kend, kt + 3 < ci.nk)
-    NC_STEP(1, 0, nx.m0, nx.n0, nx.kbeg, nx.kend, nlive && 0 < nx.nk)
-    NC_STEP(2, 1, nx.m0, nx.n0, nx.kbeg + kBK, nx.kend, nlive && 1 < nx.nk)
-    NC_STEP(3, 2, nx.m0, nx.n0, nx.kbeg + 2 * kBK, nx.kend, nlive && 2 < nx.nk)
+    NC_STEP(0, 1, 3, va, vb, ci, kt + 3, true)
+    uint32_t na[4], nb[4];
+    item_voff(nx, na, nb);
+    NC_STEP(1, 2, 0, na, nb, nx, 0, has_next)
+    NC_STEP(2, 3, 1, na, nb, nx, 1, has_next)
+    NC_STEP(3, 0, 2, na, nb, nx, 2, has_next)
     epilogue(ci);
     if (!has_next) break;
     it = nit;
     ci = nx;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      va[q] = na[q];
+      vb[q] = nb[q];
+    }
   }
 #undef NC_STEP
   wait_vmem();  // the final no-op loads still target LDS
@@ -439,12 +500,29 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ host dispatch
+template <int EPI, bool KTAIL>
+static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
+  if (ak && bk) gemm_mfma_kernel<true, true, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
+  else if (ak) gemm_mfma_kernel<true, false, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
+  else if (bk) gemm_mfma_kernel<false, true, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
+  else gemm_mfma_kernel<false, false, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
+}
+// A k-contiguous operand with K % 32 != 0 needs the per-lane cut of the last
+// slice; the model's layers never do (their widths are multiples of 64), so
+// only the fp32-output products (the general matrix-product entry point)
+// carry that variant.
 template <int EPI>
-static void launch_mfma(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
-  if (ak && bk) gemm_mfma_kernel<true, true, EPI><<<grid, 256, 0, s>>>(p);
-  else if (ak) gemm_mfma_kernel<true, false, EPI><<<grid, 256, 0, s>>>(p);
-  else if (bk) gemm_mfma_kernel<false, true, EPI><<<grid, 256, 0, s>>>(p);
-  else gemm_mfma_kernel<false, false, EPI><<<grid, 256, 0, s>>>(p);
+static int launch_mfma(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
+  const bool ktail = (ak || bk) && (p.K % kBK) != 0;
+  if (!ktail) {
+    launch_mfma_k<EPI, false>(p, ak, bk, grid, s);
+    return 0;
+  }
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+    launch_mfma_k<EPI, true>(p, ak, bk, grid, s);
+    return 0;
+  }
+  return NC_ERR_UNSUPPORTED;
 }
 
 template <int EPI>
@@ -527,18 +605,19 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   }
   // K == 0 runs the kernels with an empty k-loop: the epilogue sees zeros.
   if (g.dtype == 0) {
+    int rc = 0;
     switch (g.epi) {
       case EPI_F32:
         // accumulation into C gets its own kernel (the C loads need registers)
-        if (p.e.beta) launch_mfma<EPI_F32_ACC>(p, g.a_k, g.b_k, grid, s);
-        else launch_mfma<EPI_F32>(p, g.a_k, g.b_k, grid, s);
+        rc = p.e.beta ? launch_mfma<EPI_F32_ACC>(p, g.a_k, g.b_k, grid, s) : launch_mfma<EPI_F32>(p, g.a_k, g.b_k, grid, s);
         break;
-      case EPI_RESID: launch_mfma<EPI_RESID>(p, g.a_k, g.b_k, grid, s); break;
-      case EPI_LP: launch_mfma<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
-      case EPI_RELU2: launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
-      case EPI_DRELU2: launch_mfma<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_RESID: rc = launch_mfma<EPI_RESID>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_LP: rc = launch_mfma<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_RELU2: rc = launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_DRELU2: rc = launch_mfma<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
       default: return 8;
     }
+    if (rc) return rc;
   } else {
     switch (g.epi) {
       case EPI_F32: launch_simt<EPI_F32>(p, g.a_k, g.b_k, grid, s); break;
