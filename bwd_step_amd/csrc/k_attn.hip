@@ -27,6 +27,8 @@
 //
 // fp32 debug path: one wavefront per query (forward, dQ) or per key (dK/dV),
 // plain loops over the causal range.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -530,18 +532,26 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
         pacc[kk] = mfma(row_frag(Vs, kk * 32 + li, 2 * s + g), df[s], pacc[kk]);
       }
     }
-    const bool need_mask = (kbase + 63 > wq_min) || (kbase + 64 > T);
+    // dS^T = P (dP - D); the causal / length mask only on blocks that cross
+    // the diagonal or the end (a branch per block)
+    auto softmax = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = ex2(fmaf(sacc[kk][r], c, nlse));
-        if (need_mask) {
-          const int key = kbase + kk * 32 + acc_row(r, g);
-          if (key > qi || key >= T) pr = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float pr = ex2(fmaf(sacc[kk][r], c, nlse));
+          if constexpr (MASKED) {
+            const int key = kbase + kk * 32 + acc_row(r, g);
+            if (key > qi || key >= T) pr = 0.f;
+          }
+          pacc[kk][r] = pr * (pacc[kk][r] - Dl);
         }
-        pacc[kk][r] = pr * (pacc[kk][r] - Dl);  // dS^T
-      }
+    };
+    if ((kbase + 63 > wq_min) || (kbase + 64 > T))
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -584,7 +594,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) bf16 Q1[64 * HD];
   __shared__ __attribute__((aligned(1024))) bf16 O0[64 * HD];
   __shared__ __attribute__((aligned(1024))) bf16 O1[64 * HD];
-  __shared__ float L0[64], L1[64], D0[64], D1[64];
+  __shared__ __attribute__((aligned(16))) float L0[64], L1[64], D0[64], D1[64];
 
   const int T = p.T;
   const int kbk = blockIdx.x;  // low key blocks have the most queries: launched first
@@ -661,20 +671,35 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
           pacc[mi] = mfma(row_frag(Os, mi * 32 + li, 2 * s + g), vf[s], pacc[mi]);
         }
       }
-      const bool need_mask = (qbase < wk_min + 31) || (qbase + 64 > T);
+      // P = exp2(S c - L) and dS = P (dP - D); the causal / length mask only
+      // on blocks that cross the diagonal or the end (a branch per block).
+      auto softmax = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = mi * 32 + acc_row(r, g);
-          float pr = ex2(fmaf(sacc[mi][r], c, -Ls[ql]));
-          if (need_mask) {
-            const int q = qbase + ql;
-            if (q < kj || q >= T) pr = 0.f;
+          for (int rb = 0; rb < 4; ++rb) {
+            // accumulator registers 4 rb .. 4 rb + 3 hold four consecutive queries
+            const int ql0 = mi * 32 + 8 * rb + 4 * g;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql0);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rb + e;
+              float pr = ex2(fmaf(sacc[mi][r], c, -l4[e]));
+              if constexpr (MASKED) {
+                const int q = qbase + ql0 + e;
+                if (q < kj || q >= T) pr = 0.f;
+              }
+              sacc[mi][r] = pr;                           // P
+              pacc[mi][r] = pr * (pacc[mi][r] - d4[e]);   // dS
+            }
           }
-          sacc[mi][r] = pr;                             // P
-          pacc[mi][r] = pr * (pacc[mi][r] - Ds[ql]);    // dS
-        }
+      };
+      if ((qbase < wk_min + 31) || (qbase + 64 > T))
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
