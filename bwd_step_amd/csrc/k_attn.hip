@@ -35,7 +35,6 @@
 namespace nc {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // 2^x with the hardware instruction (no range fix-up; results below the
 // smallest normal flush to zero, which is harmless for softmax weights).
@@ -225,7 +224,7 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
       w.y = pack_bf16x2(oacc[x][rg * 4 + 2] * inv, oacc[x][rg * 4 + 3] * inv);
       *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
     }
-  if (g == 0) p.lse[(size_t)bh * T + qi] = (mx + log2f(ltot)) * kLn2;
+  if (g == 0) p.lse[(size_t)bh * T + qi] = mx + log2f(ltot);  // base 2
 }
 
 // ------------------------------------------------------------------ forward, head_dim 128
@@ -419,7 +418,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
       w.y = pack_bf16x2(oacc[x][rg * 4 + 2] * inv, oacc[x][rg * 4 + 3] * inv);
       *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
     }
-  if (g == 0) p.lse[(size_t)bh * T + qi] = (mx + log2f(ltot)) * kLn2;
+  if (g == 0) p.lse[(size_t)bh * T + qi] = mx + log2f(ltot);  // base 2
 }
 
 // ------------------------------------------------------------------ backward, head_dim 128
@@ -492,7 +491,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
     df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
   }
-  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] * kLog2e : 0.f;
+  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] : 0.f;
   const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
   const float c = p.scale_log2;
 
@@ -586,153 +585,231 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     }
 }
 
-// dK, dV: 128 keys per workgroup (K and V fragments held in registers), 64-query
-// blocks of qh and dO staged in LDS, lse and D for the block in LDS.
+// LDS-direct load written as inline assembly: 64 lanes x 16 bytes from the
+// buffer into the 1-KB LDS slot at byte address `lds`.  The compiler does not
+// see these loads, so it adds no waits of its own for them: the kernels
+// that use this count them and wait explicitly (s_waitcnt vmcnt), and the
+// barrier asm that follows carries a memory clobber, so no LDS read moves
+// above it.  m0 (the LDS destination) is saved and restored.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+// Workgroup order for the backward kernels: workgroups are dealt to the 8
+// XCDs round-robin, so consecutive logical blocks (the key or query blocks of
+// one (batch, head)) are remapped onto one XCD, where they share Q/dO or K/V
+// in its L2.
+__device__ __forceinline__ int xcd_block(int lin, int n) {
+  return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
+}
+
+// dK, dV: 128 keys per workgroup, 32 per wavefront (its K and -V fragments in
+// registers).  Blocks of 64 queries (qh, dO and their lse and D) stream
+// through four LDS stages, loaded two blocks ahead.  A block is processed as
+// two halves of 32 queries, software-pipelined: the P / dS arithmetic of one
+// half is issued together with the S / dP products of the next half, then
+// the dV / dK products of the half follow.  With -V in place of V the dP
+// accumulator starts at D and ends at D - dP, so P (D - dP) = -dS comes out
+// of one multiply; the sign is restored when dK is written.
+//
+// LDS: one array of four 36-KB stages (qh tile, dO tile: 64 rows x 256 bytes
+// with the sw2 chunk swizzle; then four 1-KB vector slots: lse (base 2), D,
+// and copies of both, one slot loaded by each wavefront).
 __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
   constexpr int HD = 128, KS = 8, HB = 4;
-  __shared__ __attribute__((aligned(1024))) bf16 Q0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 Q1[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 O0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 O1[64 * HD];
-  __shared__ __attribute__((aligned(16))) float L0[64], L1[64], D0[64], D1[64];
+  constexpr uint32_t kTile = 64 * HD * 2, kStage = 2 * kTile + 4096;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kStage];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int T = p.T;
-  const int kbk = blockIdx.x;  // low key blocks have the most queries: launched first
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int nkb = gridDim.x;
+  const int lin = xcd_block(blockIdx.x + nkb * blockIdx.y, nkb * gridDim.y);
+  const int kbk = lin % nkb;  // key blocks of one (b, h) in turn, the longest first
+  const int bh = lin / nkb, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, li = lane & 31;
   const int k0 = kbk * 128;
-  const int kj = k0 + wv * 32 + li;
+  const int wk = k0 + wv * 32;  // the wavefront's first key
+  const int kj = wk + li;       // this lane's key
   const size_t tok0 = (size_t)b * T;
   const rsrc_t rq = make_rsrc((const bf16*)p.q + tok0 * p.ldq,
                               (uint32_t)(((size_t)(T - 1) * p.ldq + (size_t)p.H * HD) * 2));
   const rsrc_t ro = make_rsrc((const bf16*)p.dout + tok0 * p.lddo,
                               (uint32_t)(((size_t)(T - 1) * p.lddo + (size_t)p.H * HD) * 2));
+  // wavefronts 0 and 2 load lse (base 2), 1 and 3 load D
+  const rsrc_t rv = make_rsrc((wv & 1) ? (const void*)(p.Dbuf + (size_t)bh * T) : (const void*)(p.lse + (size_t)bh * T),
+                              (uint32_t)T * 4u);
   const long col = (long)h * HD;
-  const float* lsep = p.lse + (size_t)bh * T;
-  const float* Dp = p.Dbuf + (size_t)bh * T;
+  const int qb0 = k0 / 64;
+  const int nb = (T + 63) / 64 - qb0;  // query blocks at or after the diagonal
 
+  // Per-lane byte offsets of this wavefront's tile loads (4 slots of 4 rows
+  // for each tile) relative to the block's first row, and of its vector load.
+  uint32_t toff_q[4], toff_o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wv * 4 + i) * 4 + (lane >> 4);
+    const int cc = (lane & 15) ^ sw2(row);
+    toff_q[i] = (uint32_t)(((long)row * p.ldq + col + cc * 8) * 2);
+    toff_o[i] = (uint32_t)(((long)row * p.lddo + col + cc * 8) * 2);
+  }
+  // loads of query block j into stage st (9 per wavefront); rows past T and
+  // blocks past the last read 0
+  auto load_block = [&](int st, int j) {
+    const int row0 = j < nb ? (qb0 + j) * 64 : T;
+    const uint32_t sb = lds0 + (uint32_t)st * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + (wv * 4 + i) * 4 + (lane >> 4);
+      const bool ok = row < T;
+      dma16(rq, ok ? toff_q[i] + (uint32_t)(row0 * p.ldq * 2) : kOOB, sb + (uint32_t)(wv * 4 + i) * 1024u);
+      dma16(ro, ok ? toff_o[i] + (uint32_t)(row0 * p.lddo * 2) : kOOB, sb + kTile + (uint32_t)(wv * 4 + i) * 1024u);
+    }
+    const int t = row0 + 4 * lane;
+    dma16(rv, (lane < 16 && t < T) ? (uint32_t)t * 4u : kOOB, sb + 2 * kTile + (uint32_t)wv * 1024u);
+  };
+  // Loads retire in issue order: with the 9 loads of the newest block still
+  // in flight, the previous block has landed.  The barrier publishes it and
+  // orders every wavefront's reads of older stages before the next loads.
+  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory"); };
+
+  load_block(0, 0);
+  load_block(1, 1);
   const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
   const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kf[KS], vn[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     kf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(kp + (size_t)kj * p.ldk + s * 16 + g * 8) : bf16x8{};
-    vf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(vp + (size_t)kj * p.ldv + s * 16 + g * 8) : bf16x8{};
+    const bf16x8 v = kj < T ? *reinterpret_cast<const bf16x8*>(vp + (size_t)kj * p.ldv + s * 16 + g * 8) : bf16x8{};
+    vn[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);  // -V
   }
   f32x16 dk[HB], dv[HB];
 #pragma unroll
   for (int x = 0; x < HB; ++x) { dk[x] = f32x16{}; dv[x] = f32x16{}; }
   const float c = p.scale_log2;
 
-  const int nqb = (T + 63) / 64;
-  const int qb0 = k0 / 64;
-  const int wk_min = k0 + wv * 32;
-  const int tid = threadIdx.x;
-
-  // stage the first query block
+  // S and D - dP of one half (mi) of the block in stage st
+  auto phase_a = [&](uint32_t st, int mi, f32x16& S, f32x16& Pd) {
+    const char* sb = smem + st * kStage;
+    const bf16* Qs = (const bf16*)sb;
+    const bf16* Os = (const bf16*)(sb + kTile);
+    const float* Ds = (const float*)(sb + 2 * kTile) + 256;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tile_dma(rq, p.ldq, col, qb0 * 64, T, Q0, wv * 4 + i, lane);
-    tile_dma(ro, p.lddo, col, qb0 * 64, T, O0, wv * 4 + i, lane);
-  }
-  if (tid < 64) {
-    const int t = qb0 * 64 + tid;
-    L0[tid] = t < T ? lsep[t] * kLog2e : 0.f;
-    D0[tid] = t < T ? Dp[t] : 0.f;
-  }
-  wait_vmem();
-  __syncthreads();
-
-  auto block = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, bf16* Qn, bf16* On, float* Ln,
-                   float* Dn, int qb) {
-    const int qnext = qb + 1 < nqb ? (qb + 1) * 64 : T;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile_dma(rq, p.ldq, col, qnext, T, Qn, wv * 4 + i, lane);
-      tile_dma(ro, p.lddo, col, qnext, T, On, wv * 4 + i, lane);
+    for (int rb = 0; rb < 4; ++rb) {
+      // accumulator registers 4 rb .. 4 rb + 3 hold four consecutive queries
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + mi * 32 + 8 * rb + 4 * g);
+      Pd[4 * rb + 0] = d4.x;
+      Pd[4 * rb + 1] = d4.y;
+      Pd[4 * rb + 2] = d4.z;
+      Pd[4 * rb + 3] = d4.w;
     }
-    float ln = 0.f, dn = 0.f;
-    if (tid < 64 && qnext + tid < T) {
-      ln = lsep[qnext + tid] * kLog2e;
-      dn = Dp[qnext + tid];
-    }
-    const int qbase = qb * 64;
-    if (qbase + 63 >= wk_min) {
-      f32x16 sacc[2], pacc[2];
+    S = f32x16{};
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        sacc[mi] = f32x16{};
-        pacc[mi] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          sacc[mi] = mfma(row_frag(Qs, mi * 32 + li, 2 * s + g), kf[s], sacc[mi]);
-          pacc[mi] = mfma(row_frag(Os, mi * 32 + li, 2 * s + g), vf[s], pacc[mi]);
-        }
-      }
-      // P = exp2(S c - L) and dS = P (dP - D); the causal / length mask only
-      // on blocks that cross the diagonal or the end (a branch per block).
-      auto softmax = [&](auto masked) {
-        constexpr bool MASKED = decltype(masked)::value;
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            // accumulator registers 4 rb .. 4 rb + 3 hold four consecutive queries
-            const int ql0 = mi * 32 + 8 * rb + 4 * g;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql0);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rb + e;
-              float pr = ex2(fmaf(sacc[mi][r], c, -l4[e]));
-              if constexpr (MASKED) {
-                const int q = qbase + ql0 + e;
-                if (q < kj || q >= T) pr = 0.f;
-              }
-              sacc[mi][r] = pr;                           // P
-              pacc[mi][r] = pr * (pacc[mi][r] - d4[e]);   // dS
-            }
-          }
-      };
-      if ((qbase < wk_min + 31) || (qbase + 64 > T))
-        softmax(std::true_type{});
-      else
-        softmax(std::false_type{});
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pf = pack8(sacc[mi], t);
-          const bf16x8 sf = pack8(pacc[mi], t);
-#pragma unroll
-          for (int x = 0; x < HB; ++x) {
-            dv[x] = mfma(tr_frag(Os, x, mi * 32 + t * 16, lane), pf, dv[x]);
-            dk[x] = mfma(tr_frag(Qs, x, mi * 32 + t * 16, lane), sf, dk[x]);
-          }
-        }
-    }
-    if (tid < 64) {
-      Ln[tid] = ln;
-      Dn[tid] = dn;
+    for (int s = 0; s < KS; ++s) {
+      S = mfma(row_frag(Qs, mi * 32 + li, 2 * s + g), kf[s], S);
+      Pd = mfma(row_frag(Os, mi * 32 + li, 2 * s + g), vn[s], Pd);
     }
   };
+  // P = exp2(S c - lse) and -dS = P (D - dP) of one half, as bf16 B operands;
+  // MASKED: apply the causal / length mask (passes that meet the diagonal or T)
+  auto phase_b = [&](auto masked, const f32x16& S, const f32x16& Pd, uint32_t st, int mi, int qh, bf16x8* pf,
+                     bf16x8* sf) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const float* Ls = (const float*)(smem + st * kStage + 2 * kTile);
+    f32x16 P, dS;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + mi * 32 + 8 * rb + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rb + e;
+        float pr = ex2(fmaf(S[r], c, -l4[e]));
+        if constexpr (MASKED) {
+          const int q = qh + 8 * rb + 4 * g + e;
+          pr = (q < kj || q >= T) ? 0.f : pr;
+        }
+        P[r] = pr;
+        dS[r] = pr * Pd[r];
+      }
+    }
+    pf[0] = pack8(P, 0);
+    pf[1] = pack8(P, 1);
+    sf[0] = pack8(dS, 0);
+    sf[1] = pack8(dS, 1);
+  };
+  // dV += P^T dO and dK' += (-dS)^T qh for one half of the block in stage st
+  auto phase_c = [&](uint32_t st, int mi, const bf16x8* pf, const bf16x8* sf) {
+    const char* sb = smem + st * kStage;
+    const bf16* Qs = (const bf16*)sb;
+    const bf16* Os = (const bf16*)(sb + kTile);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int x = 0; x < HB; ++x) {
+        dv[x] = mfma(tr_frag(Os, x, mi * 32 + t * 16, lane), pf[t], dv[x]);
+        dk[x] = mfma(tr_frag(Qs, x, mi * 32 + t * 16, lane), sf[t], dk[x]);
+      }
+  };
+  // Instruction interleave of one pipelined section: each MFMA preceded by
+  // NDS LDS reads and followed by NVALU vector instructions.
+  auto interleave = [&](auto nds, auto nvalu) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
+  using I6 = std::integral_constant<int, 6>;
 
-  int qb = qb0;
-  for (; qb + 1 < nqb; qb += 2) {
-    block(Q0, O0, L0, D0, Q1, O1, L1, D1, qb);
-    wait_vmem();
-    __syncthreads();
-    block(Q1, O1, L1, D1, Q0, O0, L0, D0, qb + 1);
-    wait_vmem();
-    __syncthreads();
+  // One pass over block j (in stage j mod 4): its second half, then the first
+  // half of block j + 1, whose loads are waited for in the middle.
+  f32x16 Sa, Pa;  // the pending half: S and D - dP, products done, arithmetic not yet
+  auto pass = [&](auto masked, int j) {
+    const uint32_t cur = (uint32_t)j & 3u, nxt = (uint32_t)(j + 1) & 3u;
+    load_block((j + 2) & 3, j + 2);
+    const int qbase = (qb0 + j) * 64;
+    bf16x8 pf[2], sf[2];
+    f32x16 Sb, Pb;
+    __builtin_amdgcn_sched_barrier(0);
+    phase_a(cur, 1, Sb, Pb);
+    phase_b(masked, Sa, Pa, cur, 0, qbase, pf, sf);
+    interleave(I2{}, I6{});
+    phase_c(cur, 0, pf, sf);
+    interleave(I2{}, I0{});
+    wait_block_and_sync();  // block j + 1
+    phase_a(nxt, 0, Sa, Pa);
+    phase_b(masked, Sb, Pb, cur, 1, qbase + 32, pf, sf);
+    interleave(I2{}, I6{});
+    phase_c(cur, 1, pf, sf);
+    interleave(I2{}, I0{});
+  };
+
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, K and V
+  phase_a(0, 0, Sa, Pa);
+  for (int j = 0; j < nb; ++j) {
+    // the first two blocks meet the diagonal; a block past T - 64 meets the end
+    if (j < 2 || (qb0 + j + 1) * 64 > T) pass(std::true_type{}, j);
+    else pass(std::false_type{}, j);
   }
-  if (qb < nqb) block(Q0, O0, L0, D0, Q1, O1, L1, D1, qb);
-  wait_vmem();
+  wait_vmem();  // the loads of the two blocks past the end still target LDS
 
   if (kj >= T) return;
-  const float sc = p.scale;
+  const float sc = -p.scale;  // dK' = -dK
   float* dkp = p.dk32 + (tok0 + kj) * p.lddk + h * HD;
 #pragma unroll
   for (int x = 0; x < HB; ++x)
@@ -823,7 +900,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_mfma(AttnArgs p) {
     sd.store_cols(Dt);
     if (threadIdx.x < 64) {
       const int t = qbase + threadIdx.x;
-      lse_s[threadIdx.x] = t < T ? lsep[t] * kLog2e : 0.f;
+      lse_s[threadIdx.x] = t < T ? lsep[t] : 0.f;
       D_s[threadIdx.x] = t < T ? Dp[t] : 0.f;
     }
     __syncthreads();
@@ -925,7 +1002,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_mfma(AttnArgs p) {
     qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
     df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
   }
-  const float lse_l = qi < T ? p.lse[(size_t)bh * T + qi] * kLog2e : 0.f;
+  const float lse_l = qi < T ? p.lse[(size_t)bh * T + qi] : 0.f;
   const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
 
   f32x16 dq[HB];
