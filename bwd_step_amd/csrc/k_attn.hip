@@ -459,132 +459,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* S, int x, int kb, int lane
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// dQ: 128 queries per workgroup, 64-key blocks of K and V staged in LDS.
-__global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
-  constexpr int HD = 128, KS = 8, HB = 4;
-  __shared__ __attribute__((aligned(1024))) bf16 K0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 K1[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 V0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 V1[64 * HD];
-
-  const int T = p.T;
-  const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, li = lane & 31;
-  const int q0 = qb * 128;
-  const int qi = q0 + wv * 32 + li;
-  const size_t tok0 = (size_t)b * T;
-  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
-                              (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2));
-  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv,
-                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2));
-  const long col = (long)h * HD;
-
-  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
-  bf16x8 qf[KS], df[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
-    df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
-  }
-  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] : 0.f;
-  const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
-  const float c = p.scale_log2;
-
-  f32x16 dq[HB];
-#pragma unroll
-  for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
-
-  const int q_last = min(T - 1, q0 + 127);
-  const int nkv = q_last / 64 + 1;
-  const int wq_min = q0 + wv * 32, wq_max = wq_min + 31;
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tile_dma(rk, p.ldk, col, 0, T, K0, wv * 4 + i, lane);
-    tile_dma(rv, p.ldv, col, 0, T, V0, wv * 4 + i, lane);
-  }
-  wait_vmem();
-  __syncthreads();
-
-  auto block = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn, int kb) {
-    const int knext = kb + 1 < nkv ? (kb + 1) * 64 : T;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile_dma(rk, p.ldk, col, knext, T, Kn, wv * 4 + i, lane);
-      tile_dma(rv, p.ldv, col, knext, T, Vn, wv * 4 + i, lane);
-    }
-    const int kbase = kb * 64;
-    if (kbase > wq_max) return;
-    f32x16 sacc[2], pacc[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      sacc[kk] = f32x16{};
-      pacc[kk] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sacc[kk] = mfma(row_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], sacc[kk]);
-        pacc[kk] = mfma(row_frag(Vs, kk * 32 + li, 2 * s + g), df[s], pacc[kk]);
-      }
-    }
-    // dS^T = P (dP - D); the causal / length mask only on blocks that cross
-    // the diagonal or the end (a branch per block)
-    auto softmax = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = ex2(fmaf(sacc[kk][r], c, nlse));
-          if constexpr (MASKED) {
-            const int key = kbase + kk * 32 + acc_row(r, g);
-            if (key > qi || key >= T) pr = 0.f;
-          }
-          pacc[kk][r] = pr * (pacc[kk][r] - Dl);
-        }
-    };
-    if ((kbase + 63 > wq_min) || (kbase + 64 > T))
-      softmax(std::true_type{});
-    else
-      softmax(std::false_type{});
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 sf = pack8(pacc[kk], t);
-#pragma unroll
-        for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 32 + t * 16, lane), sf, dq[x]);
-      }
-  };
-
-  int kb = 0;
-  for (; kb + 1 < nkv; kb += 2) {
-    block(K0, V0, K1, V1, kb);
-    wait_vmem();
-    __syncthreads();
-    block(K1, V1, K0, V0, kb + 1);
-    wait_vmem();
-    __syncthreads();
-  }
-  if (kb < nkv) block(K0, V0, K1, V1, kb);
-  wait_vmem();
-
-  if (qi >= T) return;
-  const float sc = p.scale;
-  float* dqp = p.dq32 + (tok0 + qi) * p.lddq + h * HD;
-#pragma unroll
-  for (int x = 0; x < HB; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      f32x4 w{dq[x][rg * 4 + 0] * sc, dq[x][rg * 4 + 1] * sc, dq[x][rg * 4 + 2] * sc, dq[x][rg * 4 + 3] * sc};
-      *reinterpret_cast<f32x4*>(dqp + x * 32 + 8 * rg + 4 * g) = w;
-    }
-}
-
 // LDS-direct load written as inline assembly: 64 lanes x 16 bytes from the
 // buffer into the 1-KB LDS slot at byte address `lds`.  The compiler does not
 // see these loads, so it adds no waits of its own for them: the kernels
@@ -610,6 +484,172 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
 // in its L2.
 __device__ __forceinline__ int xcd_block(int lin, int n) {
   return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
+}
+
+// dQ: 128 queries per workgroup, 32 per wavefront (its qh and dO fragments
+// in registers).  Blocks of 64 keys (K and V tiles, 64 rows x 256 bytes with
+// the sw2 chunk swizzle) stream through four LDS stages, loaded two blocks
+// ahead (same scheme as the dK/dV kernel below).  A block is processed as two
+// halves of 32 keys: the dS arithmetic of one half is issued together with
+// the S / dP products of the next half, then the dQ products of the half.
+__global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  constexpr uint32_t kTile = 64 * HD * 2, kStage = 2 * kTile;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kStage];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int T = p.T;
+  const int nqb = gridDim.x;
+  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
+  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn, the longest first
+  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int q0 = qb * 128;
+  const int qi = q0 + wv * 32 + li;  // this lane's query
+  const int wq = q0 + wv * 32;       // the wavefront's first query
+  const size_t tok0 = (size_t)b * T;
+  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
+                              (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2));
+  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv,
+                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2));
+  const long col = (long)h * HD;
+  const int nkv = min(T - 1, q0 + 127) / 64 + 1;  // key blocks up to the diagonal
+
+  uint32_t toff_k[4], toff_v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wv * 4 + i) * 4 + (lane >> 4);
+    const int cc = (lane & 15) ^ sw2(row);
+    toff_k[i] = (uint32_t)(((long)row * p.ldk + col + cc * 8) * 2);
+    toff_v[i] = (uint32_t)(((long)row * p.ldv + col + cc * 8) * 2);
+  }
+  // loads of key block j into stage st (8 per wavefront); rows past T and
+  // blocks past the last read 0
+  auto load_block = [&](int st, int j) {
+    const int row0 = j < nkv ? j * 64 : T;
+    const uint32_t sb = lds0 + (uint32_t)st * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = row0 + (wv * 4 + i) * 4 + (lane >> 4) < T;
+      dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 4 + i) * 1024u);
+      dma16(rv, ok ? toff_v[i] + (uint32_t)(row0 * p.ldv * 2) : kOOB, sb + kTile + (uint32_t)(wv * 4 + i) * 1024u);
+    }
+  };
+  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory"); };
+
+  load_block(0, 0);
+  load_block(1, 1);
+  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
+  const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
+    df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
+  }
+  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] : 0.f;  // base 2
+  const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
+  const float c = p.scale_log2;
+  f32x16 dq[HB];
+#pragma unroll
+  for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
+
+  // S^T and dP^T of one half (kk: 32 keys) of the block in stage st
+  auto phase_a = [&](uint32_t st, int kk, f32x16& S, f32x16& Pd) {
+    const char* sb = smem + st * kStage;
+    const bf16* Ks = (const bf16*)sb;
+    const bf16* Vs = (const bf16*)(sb + kTile);
+    S = f32x16{};
+    Pd = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      S = mfma(row_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], S);
+      Pd = mfma(row_frag(Vs, kk * 32 + li, 2 * s + g), df[s], Pd);
+    }
+  };
+  // dS^T = P (dP - D) of one half as bf16 B operands; MASKED: causal / length mask
+  auto phase_b = [&](auto masked, const f32x16& S, const f32x16& Pd, int kh, bf16x8* sf) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x16 dS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = ex2(fmaf(S[r], c, nlse));
+      if constexpr (MASKED) {
+        const int key = kh + acc_row(r, g);
+        pr = (key > qi || key >= T) ? 0.f : pr;
+      }
+      dS[r] = pr * (Pd[r] - Dl);
+    }
+    sf[0] = pack8(dS, 0);
+    sf[1] = pack8(dS, 1);
+  };
+  // dQ += dS K for one half of the block in stage st
+  auto phase_c = [&](uint32_t st, int kk, const bf16x8* sf) {
+    const bf16* Ks = (const bf16*)(smem + st * kStage);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 32 + t * 16, lane), sf[t], dq[x]);
+  };
+  // MFMA-led interleave: each MFMA preceded by NDS LDS reads and followed by
+  // NVALU vector instructions, over NM MFMAs.
+  auto interleave = [&](auto nm, auto nds, auto nvalu) {
+#pragma unroll
+    for (int i = 0; i < decltype(nm)::value; ++i) {
+      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+
+  f32x16 Sa, Pa;  // the pending half: S^T and dP^T done, arithmetic not yet
+  auto pass = [&](auto masked, int j) {
+    const uint32_t cur = (uint32_t)j & 3u, nxt = (uint32_t)(j + 1) & 3u;
+    load_block((j + 2) & 3, j + 2);
+    const int kbase = j * 64;
+    bf16x8 sf[2];
+    f32x16 Sb, Pb;
+    __builtin_amdgcn_sched_barrier(0);
+    phase_a(cur, 1, Sb, Pb);
+    phase_b(masked, Sa, Pa, kbase, sf);
+    interleave(I16{}, I1{}, I4{});
+    phase_c(cur, 0, sf);
+    interleave(I8{}, I4{}, I0{});
+    wait_block_and_sync();  // block j + 1
+    phase_a(nxt, 0, Sa, Pa);
+    phase_b(masked, Sb, Pb, kbase + 32, sf);
+    interleave(I16{}, I1{}, I4{});
+    phase_c(cur, 1, sf);
+    interleave(I8{}, I4{}, I0{});
+  };
+
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, qh and dO
+  phase_a(0, 0, Sa, Pa);
+  for (int j = 0; j < nkv; ++j) {
+    // the last two blocks meet the diagonal; a block past T - 64 meets the end
+    if (j >= nkv - 2 || (j + 1) * 64 > T) pass(std::true_type{}, j);
+    else pass(std::false_type{}, j);
+  }
+  wait_vmem();  // the loads of the two blocks past the end still target LDS
+
+  if (qi >= T) return;
+  const float sc = p.scale;
+  float* dqp = p.dq32 + (tok0 + qi) * p.lddq + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      f32x4 w{dq[x][rg * 4 + 0] * sc, dq[x][rg * 4 + 1] * sc, dq[x][rg * 4 + 2] * sc, dq[x][rg * 4 + 3] * sc};
+      *reinterpret_cast<f32x4*>(dqp + x * 32 + 8 * rg + 4 * g) = w;
+    }
 }
 
 // dK, dV: 128 keys per workgroup, 32 per wavefront (its K and -V fragments in
