@@ -508,7 +508,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
   const int g = lane >> 5, li = lane & 31;
   const int q0 = qb * 128;
   const int qi = q0 + wv * 32 + li;  // this lane's query
-  const int wq = q0 + wv * 32;       // the wavefront's first query
+
   const size_t tok0 = (size_t)b * T;
   const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
                               (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2));

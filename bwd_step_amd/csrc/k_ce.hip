@@ -9,6 +9,8 @@
 // workgroup owns a row: pass 1 keeps a per-thread online (max, sum), merged
 // across the workgroup; pass 2 re-reads the row (now L2/MALL-resident) and
 // writes G.  The mean loss is reduced over all rows in a fixed order.
+// bf16 path: the row statistics come from the LM-head GEMM epilogue instead
+// (per 128-column segment), and G overwrites the bf16 logits (ce_finish).
 #include "common.h"
 #include "kernels.h"
 
@@ -81,6 +83,67 @@ int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, l
     ce_row_kernel<bf16><<<rows, 256, 0, s>>>(logits, ldl, tgt, (bf16*)G, ldg, loss_rows, V, inv_n, status);
   else
     ce_row_kernel<float><<<rows, 256, 0, s>>>(logits, ldl, tgt, (float*)G, ldg, loss_rows, V, inv_n, status);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+// Finish a chunk from the partials of the LM-head GEMM epilogue (bf16 path):
+// a workgroup per row combines the (max, sum exp) pairs of its 128-column
+// segments into lse, writes loss_n = lse - l_{n, y_n} (fp32 target logit
+// from the epilogue), then overwrites the row's bf16 logits in place with
+// G_nv = (exp(l_nv - lse) - [v == y_n]) / N_total.
+__global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict__ part, int nseg,
+                                                        const float* __restrict__ tlog,
+                                                        const int32_t* __restrict__ tgt, bf16* __restrict__ LG,
+                                                        long ld, float* __restrict__ loss_rows, int V, float inv_n,
+                                                        int* __restrict__ status) {
+  const int row = blockIdx.x;
+  const float* pr = part + (size_t)row * nseg * 2;
+  float m = -INFINITY, s = 0.f;
+  for (int k = threadIdx.x; k < nseg; k += 256) online_merge(m, s, pr[2 * k], pr[2 * k + 1]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    online_merge(m, s, m2, s2);
+  }
+  bf16* g = LG + (size_t)row * ld;
+  int y = tgt[row];
+  const bool y_ok = y >= 0 && y < V;
+  if (!y_ok) y = y < 0 ? 0 : V - 1;
+  // the clamped target of an out-of-range id has no fp32 logit: read the
+  // stored one before the row is overwritten
+  const float ty = y_ok ? tlog[row] : to_f32(g[y]);
+  __shared__ float sm[4], ss[4];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[wv] = m; ss[wv] = s; }
+  __syncthreads();
+  m = sm[0]; s = ss[0];
+  for (int w = 1; w < 4; ++w) online_merge(m, s, sm[w], ss[w]);
+  const float lse = m + logf(s);
+  if (threadIdx.x == 0) {
+    loss_rows[row] = lse - ty;
+    if (!y_ok) atomicOr(status, kStatusTokenRange);
+  }
+  for (int c = threadIdx.x * 8; c < V; c += 2048) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(g + c);
+    float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y),
+                  bf16lo_to_f32(w.z), bf16hi_to_f32(w.z), bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (expf(v[e] - lse) - (c + e == y ? 1.f : 0.f)) * inv_n;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<u32x4*>(g + c) = w;
+  }
+}
+
+int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
+                     float* loss_rows, int rows, int V, int n_total, int* status, hipStream_t s) {
+  if (rows == 0) return 0;
+  if (V % 8 || ld % 8) return NC_ERR_ARG;
+  ce_finish_kernel<<<rows, 256, 0, s>>>(part, nseg, tlog, tgt, (bf16*)logits_G, ld, loss_rows, V,
+                                        1.0f / (float)n_total, status);
   NC_LAUNCH_CHECK();
   return 0;
 }

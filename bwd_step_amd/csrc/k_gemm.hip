@@ -107,7 +107,6 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int split, long i, l
 
 // ------------------------------------------------------------------ MFMA path
 constexpr int kBK = 32;  // K depth of one staged slice
-constexpr int kNS = 4;   // LDS stages: loads run three slices ahead of the MFMAs
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every operand: loads return 0
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -383,6 +382,65 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
   };
 
+  // Cross-entropy epilogue of the LM head: logits stored in bf16 and, for
+  // each row, the max and the sum of exp(l - max) over this wavefront's 128
+  // columns (the lanes l and l ^ 32 hold one row's columns), and the fp32
+  // logit of the target column.
+  auto epilogue_ce = [&](const Item& ci) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const long jw = ci.n0 + wn * TN;         // the wavefront's first column
+    const long jb = jw + 4 * (lane >> 5);    // column of acc[a][c][4 q + e] is jb + 32 c + 8 q + e
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+      const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
+      const bool row_ok = i < p.M;
+      const int y = row_ok ? p.e.tgt[i] : -1;
+      // running (max, sum exp(l - max)) in the log2 domain, one 32-column block at a time
+      float m2 = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int c = 0; c < FN; ++c) {
+        float cm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N) cm = fmaxf(cm, acc[a][c][r] * kLog2e);
+        if (cm != -INFINITY) {
+          float cs = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N)
+              cs += __builtin_amdgcn_exp2f(fmaf(acc[a][c][r], kLog2e, -cm));
+          const float mn = fmaxf(m2, cm);
+          s = s * __builtin_amdgcn_exp2f(m2 - mn) + cs * __builtin_amdgcn_exp2f(cm - mn);
+          m2 = mn;
+        }
+        if (row_ok) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const long j = jb + 32 * c + 8 * q;
+            const f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+            if (j < p.N) store4((bf16*)p.e.c_lp + i * p.e.ld_lp + j, v);
+            const long dy = (long)y - j;
+            if (dy >= 0 && dy < 4) p.e.tlog[i] = dy == 0 ? v.x : dy == 1 ? v.y : dy == 2 ? v.z : v.w;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // merge with the partner lane holding the row's other columns
+      const float pm = __shfl_xor(m2, 32, 64), ps = __shfl_xor(s, 32, 64);
+      const float mn = fmaxf(m2, pm);
+      if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m2 - mn) + ps * __builtin_amdgcn_exp2f(pm - mn);
+      if (row_ok && lane < 32 && jw < p.N) {
+        float* pp = p.e.part + ((size_t)i * p.e.nseg + (size_t)(jw / TN)) * 2;
+        pp[0] = mn * (1.0f / kLog2e);  // natural-log max
+        pp[1] = s;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
+  };
+
   int it = wfirst;
   Item ci = item(it);
   uint32_t va[4], vb[4];
@@ -421,15 +479,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     NC_STEP(1, 2, 0, na, nb, nx, 0, has_next)
     NC_STEP(2, 3, 1, na, nb, nx, 1, has_next)
     NC_STEP(3, 0, 2, na, nb, nx, 2, has_next)
-    epilogue(ci);
+    if constexpr (EPI == EPI_CE) epilogue_ce(ci);
+    else epilogue(ci);
     if (!has_next) break;
     it = nit;
     ci = nx;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      va[q] = na[q];
-      vb[q] = nb[q];
-    }
+    va[0] = na[0]; va[1] = na[1]; va[2] = na[2]; va[3] = na[3];
+    vb[0] = nb[0]; vb[1] = nb[1]; vb[2] = nb[2]; vb[3] = nb[3];
   }
 #undef NC_STEP
   wait_vmem();  // the final no-op loads still target LDS
@@ -546,15 +602,36 @@ static int num_cus() {
   return cache[dev];
 }
 
+// K splits of the fp32-output product (1 = none).  bf16 path (persistent,
+// one workgroup per compute unit): the split count minimizing the serial
+// work of the busiest workgroup, rounds x K-chunk, plus the time of writing
+// and reducing the fp32 partials (in the same units: one unit is one k of
+// a 256 x 256 tile, ~ M N / 21000 units per split); ties go to fewer splits.
 int gemm_splits(int M, int N, int K, int dtype) {
-  const int t = dtype == 0 ? 256 : 64;
-  const long tiles = (long)((M + t - 1) / t) * ((N + t - 1) / t);
-  if (tiles >= 512 || K < 2048) return 1;
-  int s = (int)((1024 + tiles - 1) / tiles);
-  const int maxs = K / 1024;
-  if (s > maxs) s = maxs;
-  if (s > 32) s = 32;
-  return s < 1 ? 1 : s;
+  if (K < 2048) return 1;
+  if (dtype != 0) {
+    const long tiles = (long)((M + 63) / 64) * ((N + 63) / 64);
+    if (tiles >= 512) return 1;
+    int s = (int)((1024 + tiles - 1) / tiles);
+    s = std::min(s, std::min(K / 1024, 32));
+    return s < 1 ? 1 : s;
+  }
+  const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+  const long cus = num_cus();
+  const int smax = std::min(32, K / 1024);
+  int best = 1;
+  double best_cost = 0;
+  for (int s = 1; s <= smax; ++s) {
+    const long kc = ((K + s - 1) / s + 127) / 128 * 128;
+    const long ss = (K + kc - 1) / kc;
+    const long rounds = (tiles * ss + cus - 1) / cus;
+    const double cost = (double)rounds * kc + (ss > 1 ? (double)ss * M * N / 21000.0 : 0.0);
+    if (s == 1 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 uint64_t gemm_ws_bytes(int M, int N, int K, int dtype) {
@@ -588,6 +665,10 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
     // chunks of a multiple of four 32-deep slices (the kernel runs them in fours)
     kchunk = ((g.K + splits - 1) / splits + 4 * kBK - 1) / (4 * kBK) * (4 * kBK);
     splits = (g.K + kchunk - 1) / kchunk;
+    if ((uint64_t)splits * g.M * g.N * 4 > g.splitk_bytes) {
+      splits = 1;
+      kchunk = g.K;
+    }
   }
   if (splits > 1) {
     p.e.c32 = g.splitk_ws;
@@ -615,6 +696,7 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
       case EPI_LP: rc = launch_mfma<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_RELU2: rc = launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_DRELU2: rc = launch_mfma<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_CE: rc = launch_mfma<EPI_CE>(p, g.a_k, g.b_k, grid, s); break;
       default: return 8;
     }
     if (rc) return rc;

@@ -9,7 +9,8 @@ namespace nc {
 
 // ---- GEMM epilogues
 enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4,
-       EPI_F32_ACC = 5 /* internal to the GEMM: EPI_F32 with beta = 1 */ };
+       EPI_F32_ACC = 5 /* internal to the GEMM: EPI_F32 with beta = 1 */,
+       EPI_CE = 6 /* logits: bf16 store + per-row softmax partials + target logit (bf16 path) */ };
 
 struct EpiArgs {
   float* c32 = nullptr;  // EPI_F32 (beta selects store / accumulate), EPI_RESID
@@ -21,6 +22,13 @@ struct EpiArgs {
   long ld_lp = 0;
   const void* aux = nullptr;  // EPI_DRELU2: u
   long ld_aux = 0;
+  // EPI_CE: logits in c_lp (bf16, ld_lp); for each row and 128-column segment
+  // (max, sum exp(l - max)) in part[row][seg][2] (nseg segments per row); the
+  // fp32 logit of column tgt[row] in tlog[row]
+  const int32_t* tgt = nullptr;
+  float* part = nullptr;
+  float* tlog = nullptr;
+  int nseg = 0;
 };
 
 struct GemmCall {
@@ -35,6 +43,7 @@ struct GemmCall {
   EpiArgs e;
   int dtype = 0;
   float* splitk_ws = nullptr;  // fp32 partials for split-K (EPI_F32 only); may be null
+  uint64_t splitk_bytes = 0;   // its size: a split that does not fit is not used
 };
 
 int launch_gemm(const GemmCall& g, hipStream_t s);
@@ -80,6 +89,10 @@ int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 
 // ---- cross-entropy
+// Finish the cross-entropy of a chunk from the EPI_CE partials: loss_rows,
+// and G = (softmax - onehot) * inv_n written over the bf16 logits in place.
+int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
+                     float* loss_rows, int rows, int V, int n_total, int* status, hipStream_t s);
 int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
                    int V, int n_total, int dtype, int* status, hipStream_t s);
 int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s);

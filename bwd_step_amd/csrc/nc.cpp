@@ -26,9 +26,24 @@ using namespace nc;
 
 namespace {
 
-constexpr int kCeChunk = 8192;  // tokens per LM-head chunk
+// Tokens per LM-head chunk: up to 16384, and the chunk's G ([chunk][V] in the
+// GEMM operand type) below 2 GiB, the reach of the GEMM's buffer loads.
+inline int ce_chunk(int N, int V, int dtype) {
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  const size_t cap = ((size_t)0x7fff0000 / ((size_t)V * es)) / 256 * 256;
+  return (int)std::min<size_t>({(size_t)N, (size_t)16384, std::max<size_t>(cap, 256)});
+}
+
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// LM-head chunk scratch besides G: bf16 path, the GEMM epilogue's per-row
+// softmax partials (max, sum exp) over 128-column segments and the target
+// logits; fp32 path, the fp32 logits.
+size_t ce_aux_bytes(size_t chunk, size_t V, int dtype) {
+  if (dtype == NC_BF16) return chunk * ((V + 127) / 128) * 2 * 4 + al(chunk * 4);
+  return chunk * V * 4;
+}
 
 struct Desc {
   std::string name;
@@ -44,6 +59,7 @@ struct Plan {
   size_t layers_base;
   // step-global buffers
   size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, Dbuf, rope, logits, G, loss_rows, splitk, embed_ws;
+  uint64_t splitk_bytes = 0;
   size_t total;
 };
 
@@ -141,8 +157,8 @@ Plan make_plan(const nc_config& c, int batch) {
   p.dqk32 = take(N * 2 * hh * 4);
   p.Dbuf = take(N * H * 4);
   p.rope = take((size_t)c.seq_len * c.head_dim * 4);
-  const size_t chunk = std::min<size_t>(N, kCeChunk);
-  p.logits = take(chunk * V * 4);
+  const size_t chunk = (size_t)ce_chunk((int)N, (int)V, c.dtype);
+  p.logits = take(ce_aux_bytes(chunk, V, c.dtype));
   p.G = take(chunk * V * es);
   p.loss_rows = take(N * 4);
   uint64_t sk = 0;
@@ -154,6 +170,7 @@ Plan make_plan(const nc_config& c, int batch) {
   sk = std::max(sk, gemm_ws_bytes((int)chunk, (int)d, (int)V, c.dtype));
   sk = std::max(sk, gemm_ws_bytes((int)V, (int)d, (int)chunk, c.dtype));
   p.splitk = take(sk);
+  p.splitk_bytes = sk;
   p.embed_ws = take(embed_bwd_ws_bytes(n, (int)d, (int)V));
   // per-layer saved activations
   p.layers_base = o;
@@ -247,25 +264,41 @@ GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, 
 }
 
 // LM head + cross-entropy over tokens in chunks: loss_rows, dz (fp32, [N,d]),
-// dW (fp32 [V,d]; overwritten or accumulated).  G and logits are chunk-sized.
+// dW (fp32 [V,d]; overwritten or accumulated).  G and the scratch `aux`
+// (ce_aux_bytes) are chunk-sized.  bf16: the logits GEMM writes bf16 logits
+// into G with the softmax partials (EPI_CE), ce_finish turns them into G in
+// place; fp32: fp32 logits, then ce_rows.
 int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss_rows, float* dz,
-              float* dW, int accumulate, int dtype, float* logits, void* G, float* splitk, int* status, hipStream_t s,
-              Prof* pf) {
+              float* dW, int accumulate, int dtype, float* aux, void* G, float* splitk, uint64_t splitk_bytes,
+              int* status, hipStream_t s, Prof* pf) {
   const size_t es = dtype == NC_BF16 ? 2 : 4;
-  for (int c0 = 0; c0 < N; c0 += kCeChunk) {
-    const int rows = std::min(kCeChunk, N - c0);
+  const int nseg = (V + 127) / 128;
+  const int chunk = ce_chunk(N, V, dtype);
+  for (int c0 = 0; c0 < N; c0 += chunk) {
+    const int rows = std::min(chunk, N - c0);
     const char* zc = (const char*)z + (size_t)c0 * d * es;
     GemmCall lg = mk(zc, d, true, W, d, true, rows, V, d, dtype);
-    lg.epi = EPI_F32; lg.e.c32 = logits; lg.e.ldc = V; lg.e.beta = 0;
-    PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
-    PROF(pf, PC_CE, 0, (double)rows * V * (4 + es), launch_ce_rows(logits, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
+    if (dtype == NC_BF16) {
+      float* part = aux;
+      float* tlog = aux + (size_t)chunk * nseg * 2;
+      lg.epi = EPI_CE; lg.e.c_lp = G; lg.e.ld_lp = V; lg.e.tgt = y + c0; lg.e.part = part; lg.e.tlog = tlog;
+      lg.e.nseg = nseg;
+      PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
+      PROF(pf, PC_CE, 0, (double)rows * V * 4 + (double)rows * nseg * 8,
+           launch_ce_finish(part, nseg, tlog, y + c0, G, V, loss_rows + c0, rows, V, N, status, s));
+    } else {
+      lg.epi = EPI_F32; lg.e.c32 = aux; lg.e.ldc = V; lg.e.beta = 0;
+      PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
+      PROF(pf, PC_CE, 0, (double)rows * V * (4 + es),
+           launch_ce_rows(aux, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
+    }
     GemmCall gw = mk(G, V, false, zc, d, false, V, d, rows, dtype);
     gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
-    gw.splitk_ws = splitk;
+    gw.splitk_ws = splitk; gw.splitk_bytes = splitk_bytes;
     PROF(pf, PC_GEMM, gflops(gw), 0, launch_gemm(gw, s));
     GemmCall gz = mk(G, V, true, W, d, false, rows, d, V, dtype);
     gz.epi = EPI_F32; gz.e.c32 = dz + (size_t)c0 * d; gz.e.ldc = d; gz.e.beta = 0;
-    gz.splitk_ws = splitk;
+    gz.splitk_ws = splitk; gz.splitk_bytes = splitk_bytes;
     PROF(pf, PC_GEMM, gflops(gz), 0, launch_gemm(gz, s));
   }
   return NC_OK;
@@ -348,7 +381,8 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   const double pairs = (double)batch * H * c.seq_len * (c.seq_len + 1) / 2.0;
   const double rms_bwd_bytes = (double)N * d * (4 + es + 4 + 4 + es) + N * 4.0;
   TRY(lmhead_ce(W + P.z, prm + lm.offset * es, targets, N, d, V, (float*)(W + P.loss_rows), tmp,
-                grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, status, s, pf));
+                grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, P.splitk_bytes, status, s,
+                pf));
   PROF(pf, PC_OTHER, 0, 0, launch_mean((float*)(W + P.loss_rows), N, loss, status, s));
   PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 4,
        launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
@@ -373,13 +407,13 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.u; b1.e.ld_aux = F;
     PROF(pf, PC_GEMM, gflops(b1), 0, launch_gemm(b1, s));
     GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
-    b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk;
+    b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b2), 0, launch_gemm(b2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
     b3.epi = EPI_F32; b3.e.c32 = tmp; b3.e.ldc = d;
     PROF(pf, PC_GEMM, gflops(b3), 0, launch_gemm(b3, s));
     GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
-    b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk;
+    b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk; b4.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b4), 0, launch_gemm(b4, s));
     PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.m, (float*)(L + P.r2), dx, dx_lp, N, d, 1, dt, s));
 
@@ -388,7 +422,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
     PROF(pf, PC_GEMM, gflops(b5), 0, launch_gemm(b5, s));
     GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
-    b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk;
+    b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk; b6.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b6), 0, launch_gemm(b6, s));
 
     AttnArgs a;
@@ -413,7 +447,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     b7.epi = EPI_F32; b7.e.c32 = tmp; b7.e.ldc = d;
     PROF(pf, PC_GEMM, gflops(b7), 0, launch_gemm(b7, s));
     GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
-    b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk;
+    b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b8), 0, launch_gemm(b8, s));
     PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.a1, (float*)(L + P.r1), dx, dx_lp, N, d, 1, dt, s));
   }
@@ -633,12 +667,12 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void
 }
 
 static size_t ce_ws_parts(int N, int d, int V, int dtype, size_t* off) {
-  const size_t chunk = std::min<size_t>(N, kCeChunk);
+  const size_t chunk = (size_t)ce_chunk(N, V, dtype);
   const size_t es = dtype == NC_BF16 ? 2 : 4;
   size_t o = 0;
   auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
   off[0] = take(256);
-  off[1] = take(chunk * V * 4);
+  off[1] = take(ce_aux_bytes(chunk, (size_t)V, dtype));
   off[2] = take(chunk * V * es);
   off[3] = take((size_t)N * 4);
   off[4] = take(std::max(gemm_ws_bytes((int)chunk, d, V, dtype), gemm_ws_bytes(V, d, (int)chunk, dtype)));
@@ -661,11 +695,11 @@ int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, 
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)workspace;
   int* status = (int*)w;
-  const uint64_t sk_bytes = std::max(gemm_ws_bytes(std::min(N, kCeChunk), d, V, dtype),
-                                     gemm_ws_bytes(V, d, std::min(N, kCeChunk), dtype));
+  const int chunk = ce_chunk(N, V, dtype);
+  const uint64_t sk_bytes = std::max(gemm_ws_bytes(chunk, d, V, dtype), gemm_ws_bytes(V, d, chunk, dtype));
   float* sk = sk_bytes ? (float*)(w + off[4]) : nullptr;
   TRY(lmhead_ce(z, W, y, N, d, V, (float*)(w + off[3]), dz, dW, 0, dtype, (float*)(w + off[1]), w + off[2], sk,
-                status, s, nullptr));
+                sk_bytes, status, s, nullptr));
   return launch_mean((float*)(w + off[3]), N, loss, status, s);
 }
 
@@ -724,7 +758,10 @@ int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb, int b_
   GemmCall g = mk(A, lda, a_kmajor, B, ldb, b_kmajor, M, N, K, dtype);
   g.epi = EPI_F32; g.e.c32 = C; g.e.ldc = ldc; g.e.beta = beta;
   const uint64_t need = gemm_ws_bytes(M, N, K, dtype);
-  if (need && workspace && ws_bytes >= need) g.splitk_ws = (float*)workspace;
+  if (need && workspace && ws_bytes >= need) {
+    g.splitk_ws = (float*)workspace;
+    g.splitk_bytes = ws_bytes;
+  }
   return launch_gemm(g, (hipStream_t)stream);
 }
 

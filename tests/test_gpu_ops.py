@@ -184,7 +184,7 @@ def ce_oracle(z, W, y):
 
 
 @pytest.mark.parametrize("dt", DTS)
-@pytest.mark.parametrize("N,d,V", [(300, 128, 1024), (8192 + 300, 64, 512)])
+@pytest.mark.parametrize("N,d,V", [(300, 128, 1024), (16384 + 300, 64, 512), (200, 64, 576)])
 def test_lmhead_ce(dt, N, d, V):
     banner(f"lmhead_ce {dt} N={N} d={d} V={V}")
     z = prep(synth.normal((N, d), 6, synth.STREAM_HIDDEN), dt)
