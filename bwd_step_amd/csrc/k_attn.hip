@@ -550,7 +550,20 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
   }
   const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] : 0.f;  // base 2
-  const float Dl = qi < T ? p.Dbuf[(size_t)bh * T + qi] : 0.f;
+  // D = rowsum(dO * O) of this lane's query (lanes l and l ^ 32 hold the two
+  // halves of the row), also written for the dK/dV kernel that runs next
+  float Dl = 0.f;
+  {
+    const bf16* op = (const bf16*)p.o + tok0 * p.ldo + h * HD;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 o8 = qi < T ? *reinterpret_cast<const bf16x8*>(op + (size_t)qi * p.ldo + s * 16 + g * 8) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Dl = fmaf(to_f32(df[s][e]), to_f32(o8[e]), Dl);
+    }
+    Dl += __shfl_xor(Dl, 32, 64);
+    if (g == 0 && qi < T) p.Dbuf[(size_t)bh * T + qi] = Dl;
+  }
   const float c = p.scale_log2;
   f32x16 dq[HB];
 #pragma unroll
@@ -1242,13 +1255,14 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
   if (p.B * p.H * p.T == 0) return 0;
   const long rows = (long)p.B * p.T * p.H;
   if (dtype == 0) {
-    attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
     dim3 gk((p.T + 127) / 128, p.B * p.H);
     dim3 gq((p.T + 127) / 128, p.B * p.H);
     if (hd == 128) {
-      attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
+      // the dQ kernel computes D = rowsum(dO * O) for the dK/dV kernel
       attn_bwd_dq128<<<gq, 256, 0, s>>>(p);
+      attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
     } else if (hd == 64) {
+      attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
       attn_bwd_dkdv_mfma<64><<<gk, 256, 0, s>>>(p);
       attn_bwd_dq_mfma<64><<<gq, 256, 0, s>>>(p);
     } else {
