@@ -17,17 +17,25 @@
 namespace nc {
 
 // --------------------------------------------------------------- RMSNorm
+// With `res` (bf16 [N, d], the previous sublayer's output): x += res first
+// (the residual update of the stream, written back to x), then the norm.
 template <class T>
-__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
-                                                          float* __restrict__ r, int N, int d, float eps) {
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(float* __restrict__ x, const bf16* __restrict__ res,
+                                                          T* __restrict__ y, float* __restrict__ r, int N, int d,
+                                                          float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
-  const f32x4* xr = reinterpret_cast<const f32x4*>(x + (size_t)row * d);
+  f32x4* xr = reinterpret_cast<f32x4*>(x + (size_t)row * d);
   const int nc4 = d >> 2;
   float ss = 0.f;
   for (int c = lane; c < nc4; c += 64) {
     f32x4 v = xr[c];
+    if (res) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(res + (size_t)row * d + 4 * c);
+      v += f32x4{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
+      xr[c] = v;
+    }
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   ss = wave_sum(ss);
@@ -69,8 +77,9 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
   }
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+// dy in TD (fp32, or bf16 when the producing GEMM stored bf16)
+template <class T, class TD>
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const TD* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ r, float* __restrict__ dx,
                                                           T* __restrict__ dx_lp, int N, int d, int accumulate) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -80,14 +89,14 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
   const int nc4 = d >> 2;
   float dot = 0.f;
   for (int c = lane; c < nc4; c += 64) {
-    f32x4 g = *reinterpret_cast<const f32x4*>(dy + base + 4 * c);
+    f32x4 g = load4(dy + base + 4 * c);
     f32x4 v = load4(y + base + 4 * c);
     dot += g.x * v.x + g.y * v.y + g.z * v.z + g.w * v.w;
   }
   dot = wave_sum(dot) / (float)d;
   const float rr = r[row];
   for (int c = lane; c < nc4; c += 64) {
-    f32x4 g = *reinterpret_cast<const f32x4*>(dy + base + 4 * c);
+    f32x4 g = load4(dy + base + 4 * c);
     f32x4 v = load4(y + base + 4 * c);
     f32x4 o = (g - v * dot) * rr;
     f32x4* dp = reinterpret_cast<f32x4*>(dx + base + 4 * c);
@@ -98,30 +107,40 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
 }
 
 template <class T>
-int rmsnorm_fwd_t(const float* x, void* y, float* r, int N, int d, float eps, hipStream_t s) {
+int rmsnorm_fwd_t(float* x, const void* res, void* y, float* r, int N, int d, float eps, hipStream_t s) {
   if (N == 0) return 0;
-  rmsnorm_fwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(x, (T*)y, r, N, d, eps);
+  rmsnorm_fwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(x, (const bf16*)res, (T*)y, r, N, d, eps);
   NC_LAUNCH_CHECK();
   return 0;
 }
 
 int launch_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, hipStream_t s) {
-  return dtype == 0 ? rmsnorm_fwd_t<bf16>(x, y, r, N, d, eps, s) : rmsnorm_fwd_t<float>(x, y, r, N, d, eps, s);
+  return dtype == 0 ? rmsnorm_fwd_t<bf16>(const_cast<float*>(x), nullptr, y, r, N, d, eps, s)
+                    : rmsnorm_fwd_t<float>(const_cast<float*>(x), nullptr, y, r, N, d, eps, s);
 }
 
-template <class T>
-int rmsnorm_bwd_t(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d, int acc,
+int launch_rmsnorm_add_fwd(float* x, const void* res, void* y, float* r, int N, int d, float eps, hipStream_t s) {
+  return rmsnorm_fwd_t<bf16>(x, res, y, r, N, d, eps, s);
+}
+
+template <class T, class TD>
+int rmsnorm_bwd_t(const void* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d, int acc,
                   hipStream_t s) {
   if (N == 0) return 0;
-  rmsnorm_bwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(dy, (const T*)y, r, dx, (T*)dx_lp, N, d, acc);
+  rmsnorm_bwd_kernel<T, TD><<<(N + 3) / 4, 256, 0, s>>>((const TD*)dy, (const T*)y, r, dx, (T*)dx_lp, N, d, acc);
   NC_LAUNCH_CHECK();
   return 0;
 }
 
 int launch_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
                        int accumulate, int dtype, hipStream_t s) {
-  return dtype == 0 ? rmsnorm_bwd_t<bf16>(dy, y, r, dx, dx_lp, N, d, accumulate, s)
-                    : rmsnorm_bwd_t<float>(dy, y, r, dx, dx_lp, N, d, accumulate, s);
+  return dtype == 0 ? rmsnorm_bwd_t<bf16, float>(dy, y, r, dx, dx_lp, N, d, accumulate, s)
+                    : rmsnorm_bwd_t<float, float>(dy, y, r, dx, dx_lp, N, d, accumulate, s);
+}
+
+int launch_rmsnorm_bwd_lpdy(const void* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
+                            int accumulate, hipStream_t s) {
+  return rmsnorm_bwd_t<bf16, bf16>(dy, y, r, dx, dx_lp, N, d, accumulate, s);
 }
 
 // --------------------------------------------------------------- RoPE table

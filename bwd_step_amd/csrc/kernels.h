@@ -54,6 +54,11 @@ uint64_t gemm_ws_bytes(int M, int N, int K, int dtype);
 int launch_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, hipStream_t s);
 int launch_rmsnorm_bwd(const float* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
                        int accumulate, int dtype, hipStream_t s);
+// bf16 path: x += res (bf16) then the norm (the residual update fused in)
+int launch_rmsnorm_add_fwd(float* x, const void* res, void* y, float* r, int N, int d, float eps, hipStream_t s);
+// bf16 path: the backward with a bf16 dy
+int launch_rmsnorm_bwd_lpdy(const void* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
+                            int accumulate, hipStream_t s);
 int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s);
 int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
                            void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,

@@ -320,6 +320,30 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   const double pairs = (double)batch * H * c.seq_len * (c.seq_len + 1) / 2.0;  // causal (query, key) pairs
   PROF(pf, PC_EMB_FWD, 0, (double)N * d * (es + 4) + N * 4.0, launch_embed_fwd(prm, tokens, x, N, d, V, dt, status, s));
   PROF(pf, PC_OTHER, 0, 0, launch_rope_table(cs, c.seq_len, hd, c.rope_base, s));
+  // bf16 path: the output projections store their sublayer output y in bf16
+  // and the next RMSNorm adds it to the fp32 stream x (x += y, then the norm);
+  // fp32 path: the projections add into x in their epilogue.
+  void* ybuf = W + P.dx_lp;
+  const void* pend = nullptr;
+  auto norm = [&](void* out, float* r) -> int {
+    if (pend) {
+      const void* res = pend;
+      pend = nullptr;
+      PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + 2 + 4 + es) + N * 4.0,
+           launch_rmsnorm_add_fwd(x, res, out, r, N, d, c.norm_eps, s));
+      return NC_OK;
+    }
+    PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0, launch_rmsnorm_fwd(x, out, r, N, d, c.norm_eps, dt, s));
+    return NC_OK;
+  };
+  auto proj_out = [&](GemmCall& g) {
+    if (dt == NC_BF16) {
+      g.epi = EPI_LP; g.e.c_lp = ybuf; g.e.ld_lp = d;
+      pend = ybuf;
+    } else {
+      g.epi = EPI_RESID; g.e.c32 = x; g.e.ldc = d;
+    }
+  };
   for (int l = 0; l < c.depth; ++l) {
     char* L = W + P.layers_base + (size_t)l * P.layer_stride;
     const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
@@ -328,8 +352,7 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
     void* a1 = L + P.a1;
     char* qkv = L + P.qkv;
-    PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
-         launch_rmsnorm_fwd(x, a1, (float*)(L + P.r1), N, d, c.norm_eps, dt, s));
+    TRY(norm(a1, (float*)(L + P.r1)));
     GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, 3 * hh, d, dt);
     g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
     PROF(pf, PC_GEMM, gflops(g1), 0, launch_gemm(g1, s));
@@ -344,19 +367,17 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     a.B = batch; a.H = H; a.T = c.seq_len;
     PROF(pf, PC_ATTN_FWD, 4.0 * hd * pairs, 0, launch_attn_fwd(a, hd, dt, s));
     GemmCall g2 = mk(L + P.O, hh, true, Wo, hh, true, N, d, hh, dt);
-    g2.epi = EPI_RESID; g2.e.c32 = x; g2.e.ldc = d;
+    proj_out(g2);
     PROF(pf, PC_GEMM, gflops(g2), 0, launch_gemm(g2, s));
-    PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
-         launch_rmsnorm_fwd(x, L + P.m, (float*)(L + P.r2), N, d, c.norm_eps, dt, s));
+    TRY(norm(L + P.m, (float*)(L + P.r2)));
     GemmCall g3 = mk(L + P.m, d, true, W1, d, true, N, F, d, dt);
     g3.epi = EPI_RELU2; g3.e.c_lp = L + P.u; g3.e.c_lp2 = L + P.g; g3.e.ld_lp = F;
     PROF(pf, PC_GEMM, gflops(g3), 0, launch_gemm(g3, s));
     GemmCall g4 = mk(L + P.g, F, true, W2, F, true, N, d, F, dt);
-    g4.epi = EPI_RESID; g4.e.c32 = x; g4.e.ldc = d;
+    proj_out(g4);
     PROF(pf, PC_GEMM, gflops(g4), 0, launch_gemm(g4, s));
   }
-  PROF(pf, PC_RMS_FWD, 0, (double)N * d * (4 + es) + N * 4.0,
-       launch_rmsnorm_fwd(x, W + P.z, (float*)(W + P.rf), N, d, c.norm_eps, dt, s));
+  TRY(norm(W + P.z, (float*)(W + P.rf)));
   return NC_OK;
 }
 
@@ -387,6 +408,25 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 4,
        launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
 
+  // The input gradients of the MLP and QKV projections feed only the RMSNorm
+  // backward: bf16 path, stored in bf16 (tmp as a bf16 [N, d] buffer); fp32
+  // path, fp32.
+  auto dgrad_out = [&](GemmCall& g) {
+    if (dt == NC_BF16) {
+      g.epi = EPI_LP; g.e.c_lp = tmp; g.e.ld_lp = d;
+    } else {
+      g.epi = EPI_F32; g.e.c32 = tmp; g.e.ldc = d;
+    }
+  };
+  auto norm_bwd = [&](const void* y, const float* r) -> int {
+    if (dt == NC_BF16) {
+      PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 2,
+           launch_rmsnorm_bwd_lpdy(tmp, y, r, dx, dx_lp, N, d, 1, s));
+    } else {
+      PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, y, r, dx, dx_lp, N, d, 1, dt, s));
+    }
+    return NC_OK;
+  };
   for (int l = c.depth - 1; l >= 0; --l) {
     char* L = W + P.layers_base + (size_t)l * P.layer_stride;
     const Desc& dqkv_d = ctx->layout[1 + 4 * l];
@@ -410,12 +450,12 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b2), 0, launch_gemm(b2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
-    b3.epi = EPI_F32; b3.e.c32 = tmp; b3.e.ldc = d;
+    dgrad_out(b3);
     PROF(pf, PC_GEMM, gflops(b3), 0, launch_gemm(b3, s));
     GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
     b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk; b4.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b4), 0, launch_gemm(b4, s));
-    PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.m, (float*)(L + P.r2), dx, dx_lp, N, d, 1, dt, s));
+    TRY(norm_bwd(L + P.m, (float*)(L + P.r2)));
 
     // attention output projection: dO = dx W_o; dW_o = dx^T O
     GemmCall b5 = mk(dx_lp, d, true, Wo, hh, false, N, hh, d, dt);
@@ -444,12 +484,12 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
     GemmCall b7 = mk(dqkv, 3 * hh, true, Wqkv, d, false, N, d, 3 * hh, dt);
-    b7.epi = EPI_F32; b7.e.c32 = tmp; b7.e.ldc = d;
+    dgrad_out(b7);
     PROF(pf, PC_GEMM, gflops(b7), 0, launch_gemm(b7, s));
     GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
     b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b8), 0, launch_gemm(b8, s));
-    PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes, launch_rmsnorm_bwd(tmp, L + P.a1, (float*)(L + P.r1), dx, dx_lp, N, d, 1, dt, s));
+    TRY(norm_bwd(L + P.a1, (float*)(L + P.r1)));
   }
   PROF(pf, PC_EMB_BWD, 0, (double)N * d * 4 + (double)V * d * 4 * (accumulate ? 2 : 1) + N * 4.0,
        launch_embed_bwd(dx, tokens, grads, N, d, V, accumulate, W + P.embed_ws, s));
