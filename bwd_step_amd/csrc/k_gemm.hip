@@ -19,7 +19,7 @@
 //
 // Epilogues are fused so that each output is written once: fp32 store or
 // accumulate, bf16 store, residual add into the fp32 stream, ReLU² (stores
-// u and g = max(u,0)^2), and the ReLU² backward (du = dg * 2 max(u,0)).
+// g = max(u,0)^2 only), and the ReLU² backward (du = dg * 2 sqrt(g)).
 #include <algorithm>
 
 #include "common.h"
@@ -63,6 +63,13 @@ __device__ __forceinline__ f32x4 load4(const T* p) {
   }
 }
 
+// ReLU² backward from the saved g = relu(u)^2: d/du relu(u)^2 = 2 relu(u) =
+// 2 sqrt(g), so u itself is never stored.
+__device__ __forceinline__ f32x4 drelu2(f32x4 dg, f32x4 g) {
+  return f32x4{2.f * __builtin_sqrtf(g.x) * dg.x, 2.f * __builtin_sqrtf(g.y) * dg.y,
+               2.f * __builtin_sqrtf(g.z) * dg.z, 2.f * __builtin_sqrtf(g.w) * dg.w};
+}
+
 template <int EPI, class T = bf16>
 __device__ __forceinline__ void epi_apply4(const EpiArgs& e, int split, long i, long j, f32x4 v) {
   if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
@@ -75,14 +82,10 @@ __device__ __forceinline__ void epi_apply4(const EpiArgs& e, int split, long i, 
   } else if constexpr (EPI == EPI_LP) {
     store4((T*)e.c_lp + i * e.ld_lp + j, v);
   } else if constexpr (EPI == EPI_RELU2) {
-    store4((T*)e.c_lp + i * e.ld_lp + j, v);
     const f32x4 r{fmaxf(v.x, 0.f), fmaxf(v.y, 0.f), fmaxf(v.z, 0.f), fmaxf(v.w, 0.f)};
-    store4((T*)e.c_lp2 + i * e.ld_lp + j, r * r);
+    store4((T*)e.c_lp + i * e.ld_lp + j, r * r);
   } else if constexpr (EPI == EPI_DRELU2) {
-    const f32x4 u = load4((const T*)e.aux + i * e.ld_aux + j);
-    const f32x4 du{u.x > 0.f ? 2.f * u.x * v.x : 0.f, u.y > 0.f ? 2.f * u.y * v.y : 0.f,
-                   u.z > 0.f ? 2.f * u.z * v.z : 0.f, u.w > 0.f ? 2.f * u.w * v.w : 0.f};
-    store4((T*)e.c_lp + i * e.ld_lp + j, du);
+    store4((T*)e.c_lp + i * e.ld_lp + j, drelu2(v, load4((const T*)e.aux + i * e.ld_aux + j)));
   }
 }
 
@@ -96,12 +99,11 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int split, long i, l
   } else if constexpr (EPI == EPI_LP) {
     ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(v);
   } else if constexpr (EPI == EPI_RELU2) {
-    ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(v);
     const float r = v > 0.f ? v : 0.f;
-    ((T*)e.c_lp2)[i * e.ld_lp + j] = from_f32<T>(r * r);
+    ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(r * r);
   } else if constexpr (EPI == EPI_DRELU2) {
-    const float u = to_f32(((const T*)e.aux)[i * e.ld_aux + j]);
-    ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(u > 0.f ? 2.f * u * v : 0.f);
+    const float g = to_f32(((const T*)e.aux)[i * e.ld_aux + j]);
+    ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(2.f * sqrtf(g) * v);
   }
 }
 
@@ -387,6 +389,45 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
   };
 
+  // ReLU² backward epilogue: the saved g of the next 32-row block is loaded
+  // while the current block is computed and stored, so the load latency is
+  // paid once per tile rather than once per block.
+  auto epilogue_drelu2 = [&](const Item& ci) {
+    u32x2 gv[2][FN][4];
+    auto load_g = [&](int a, u32x2 (&dst)[FN][4]) {
+      const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < FN; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const long j = ci.n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
+          dst[c][q] = (i < p.M && j < p.N)
+                          ? *reinterpret_cast<const u32x2*>((const bf16*)p.e.aux + i * p.e.ld_aux + j)
+                          : u32x2{0u, 0u};
+        }
+    };
+    load_g(0, gv[0]);
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+      if (a + 1 < FM) load_g(a + 1, gv[(a + 1) & 1]);
+      const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < FN; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const long j = ci.n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
+          const u32x2 w = gv[a & 1][c][q];
+          const f32x4 g{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
+          const f32x4 dg{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+          if (i < p.M && j < p.N) store4((bf16*)p.e.c_lp + i * p.e.ld_lp + j, drelu2(dg, g));
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
+  };
+
   // Cross-entropy epilogue of the LM head: logits stored in bf16 and, for
   // each row, the max and the sum of exp(l - max) over this wavefront's 128
   // columns (the lanes l and l ^ 32 hold one row's columns), and the fp32
@@ -485,6 +526,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     NC_STEP(2, 3, 1, na, nb, nx, 1, has_next)
     NC_STEP(3, 0, 2, na, nb, nx, 2, has_next)
     if constexpr (EPI == EPI_CE) epilogue_ce(ci);
+    else if constexpr (EPI == EPI_DRELU2) epilogue_drelu2(ci);
     else epilogue(ci);
     if (!has_next) break;
     it = nit;

@@ -17,10 +17,10 @@ struct EpiArgs {
   long ldc = 0;
   int beta = 0;
   long split_stride = 0;    // elements between split-K partial slices
-  void* c_lp = nullptr;     // EPI_LP / EPI_RELU2 (u) / EPI_DRELU2 (du)
-  void* c_lp2 = nullptr;    // EPI_RELU2 (g)
+  void* c_lp = nullptr;     // EPI_LP / EPI_RELU2 (g = relu(u)^2) / EPI_DRELU2 (du)
+  void* c_lp2 = nullptr;    // unused
   long ld_lp = 0;
-  const void* aux = nullptr;  // EPI_DRELU2: u
+  const void* aux = nullptr;  // EPI_DRELU2: g
   long ld_aux = 0;
   // EPI_CE: logits in c_lp (bf16, ld_lp); for each row and 128-column segment
   // (max, sum exp(l - max)) in part[row][seg][2] (nseg segments per row); the

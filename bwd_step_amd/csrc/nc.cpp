@@ -55,7 +55,7 @@ struct Plan {
   int batch = 0;
   size_t status = 0;
   // per-layer saved activations: offsets inside layer 0, plus the layer stride
-  size_t a1, r1, qkv, rq, rk, O, lse, m, r2, u, g, layer_stride;
+  size_t a1, r1, qkv, rq, rk, O, lse, m, r2, g, layer_stride;
   size_t layers_base;
   // step-global buffers
   size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, Dbuf, rope, logits, G, loss_rows, splitk, embed_ws;
@@ -185,7 +185,6 @@ Plan make_plan(const nc_config& c, int batch) {
   p.lse = ltake(N * H * 4);
   p.m = ltake(N * d * es);
   p.r2 = ltake(N * 4);
-  p.u = ltake(N * F * es);
   p.g = ltake(N * F * es);
   p.layer_stride = lo;
   o += lo * c.depth;
@@ -371,7 +370,7 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     PROF(pf, PC_GEMM, gflops(g2), 0, launch_gemm(g2, s));
     TRY(norm(L + P.m, (float*)(L + P.r2)));
     GemmCall g3 = mk(L + P.m, d, true, W1, d, true, N, F, d, dt);
-    g3.epi = EPI_RELU2; g3.e.c_lp = L + P.u; g3.e.c_lp2 = L + P.g; g3.e.ld_lp = F;
+    g3.epi = EPI_RELU2; g3.e.c_lp = L + P.g; g3.e.ld_lp = F;
     PROF(pf, PC_GEMM, gflops(g3), 0, launch_gemm(g3, s));
     GemmCall g4 = mk(L + P.g, F, true, W2, F, true, N, d, F, dt);
     proj_out(g4);
@@ -442,9 +441,9 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     char* dqkv = W + P.dqkv;
     float* dqk32 = (float*)(W + P.dqk32);
 
-    // MLP: du = (dx W_2) * 2 relu(u); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
+    // MLP: du = (dx W_2) * 2 relu(u), with relu(u) = sqrt(g); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
-    b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.u; b1.e.ld_aux = F;
+    b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.g; b1.e.ld_aux = F;
     PROF(pf, PC_GEMM, gflops(b1), 0, launch_gemm(b1, s));
     GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
     b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
