@@ -65,10 +65,13 @@ __device__ __forceinline__ f32x4 load4(const T* p) {
 }
 
 // ReLU² backward from the saved g = relu(u)^2: d/du relu(u)^2 = 2 relu(u) =
-// 2 sqrt(g), so u itself is never stored.
+// 2 sqrt(g), so u itself is never stored.  g >= 0 comes from bf16 storage and
+// the result is rounded to bf16, so the hardware square root (v_sqrt_f32,
+// 1 ulp) replaces the correctly rounded expansion, which costs about ten
+// VALU instructions per element in an MFMA epilogue.
 __device__ __forceinline__ f32x4 drelu2(f32x4 dg, f32x4 g) {
-  return f32x4{2.f * __builtin_sqrtf(g.x) * dg.x, 2.f * __builtin_sqrtf(g.y) * dg.y,
-               2.f * __builtin_sqrtf(g.z) * dg.z, 2.f * __builtin_sqrtf(g.w) * dg.w};
+  return f32x4{2.f * __builtin_amdgcn_sqrtf(g.x) * dg.x, 2.f * __builtin_amdgcn_sqrtf(g.y) * dg.y,
+               2.f * __builtin_amdgcn_sqrtf(g.z) * dg.z, 2.f * __builtin_amdgcn_sqrtf(g.w) * dg.w};
 }
 
 template <int EPI, class T = bf16>
@@ -434,42 +437,45 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   // logit of the target column.
   auto epilogue_ce = [&](const Item& ci) {
     constexpr float kLog2e = 1.4426950408889634f;
-    const long jw = ci.n0 + wn * TN;         // the wavefront's first column
-    const long jb = jw + 4 * (lane >> 5);    // column of acc[a][c][4 q + e] is jb + 32 c + 8 q + e
+    const int jw = ci.n0 + wn * TN;        // the wavefront's first column (N < 2^31)
+    const int jb = jw + 4 * (lane >> 5);   // column of acc[a][c][4 q + e] is jb + 32 c + 8 q + e
+    const bool full = ci.n0 + BN <= p.N;   // uniform: every column of the tile exists
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
       const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
       const bool row_ok = i < p.M;
-      const int y = row_ok ? p.e.tgt[i] : -1;
-      // running (max, sum exp(l - max)) in the log2 domain, one 32-column block at a time
-      float m2 = -INFINITY, s = 0.f;
+      const int yc = (row_ok ? p.e.tgt[i] : -1) - jb;  // target column relative to jb
+      bf16* crow = (bf16*)p.e.c_lp + i * p.e.ld_lp + jb;
+      // pass 1: bf16 logits out, the fp32 target logit, the row maximum
+      float mraw = -INFINITY;
 #pragma unroll
       for (int c = 0; c < FN; ++c) {
-        float cm = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N) cm = fmaxf(cm, acc[a][c][r] * kLog2e);
-        if (cm != -INFINITY) {
-          float cs = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int j = 32 * c + 8 * q;
+          const f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+          if (full) {
+            mraw = fmaxf(mraw, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (jb + j + e < p.N) mraw = fmaxf(mraw, v[e]);
+          }
+          if (row_ok && (full || jb + j < p.N)) store4(crow + j, v);
+          const unsigned dy = (unsigned)(yc - j);
+          if (row_ok && dy < 4u) p.e.tlog[i] = dy == 0 ? v.x : dy == 1 ? v.y : dy == 2 ? v.z : v.w;
+        }
+      }
+      // pass 2: sum of exp(l - max) in the log2 domain
+      const float m2 = mraw * kLog2e;
+      float s = 0.f;
+      if (mraw != -INFINITY) {
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N)
-              cs += __builtin_amdgcn_exp2f(fmaf(acc[a][c][r], kLog2e, -cm));
-          const float mn = fmaxf(m2, cm);
-          s = s * __builtin_amdgcn_exp2f(m2 - mn) + cs * __builtin_amdgcn_exp2f(cm - mn);
-          m2 = mn;
-        }
-        if (row_ok) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const long j = jb + 32 * c + 8 * q;
-            const f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
-            if (j < p.N) store4((bf16*)p.e.c_lp + i * p.e.ld_lp + j, v);
-            const long dy = (long)y - j;
-            if (dy >= 0 && dy < 4) p.e.tlog[i] = dy == 0 ? v.x : dy == 1 ? v.y : dy == 2 ? v.z : v.w;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            if (full || jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N)
+              s += __builtin_amdgcn_exp2f(fmaf(acc[a][c][r], kLog2e, -m2));
       }
       // merge with the partner lane holding the row's other columns
       const float pm = __shfl_xor(m2, 32, 64), ps = __shfl_xor(s, 32, 64);
@@ -480,6 +486,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
         pp[0] = mn * (1.0f / kLog2e);  // natural-log max
         pp[1] = s;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int a = 0; a < FM; ++a)
