@@ -646,11 +646,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, qh and dO
   phase_a(0, 0, Sa, Pa);
-  for (int j = 0; j < nkv; ++j) {
-    // the last two blocks meet the diagonal; a block past T - 64 meets the end
-    if (j >= nkv - 2 || (j + 1) * 64 > T) pass(std::true_type{}, j);
-    else pass(std::false_type{}, j);
-  }
+  // The last two blocks meet the diagonal and a block j with (j + 1) * 64 > T
+  // (j >= T / 64) meets the end, so the masked passes are a suffix.  Two
+  // loops with one pass body each keep the accumulators in one place (one
+  // loop with both bodies behind a branch moved dQ between register files
+  // on every trip).
+  const int jm = max(0, min(nkv - 2, T / 64));
+  int j = 0;
+  for (; j < jm; ++j) pass(std::false_type{}, j);
+  for (; j < nkv; ++j) pass(std::true_type{}, j);
   wait_vmem();  // the loads of the two blocks past the end still target LDS
 
   if (qi >= T) return;
@@ -854,11 +858,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, K and V
   phase_a(0, 0, Sa, Pa);
-  for (int j = 0; j < nb; ++j) {
-    // the first two blocks meet the diagonal; a block past T - 64 meets the end
-    if (j < 2 || (qb0 + j + 1) * 64 > T) pass(std::true_type{}, j);
-    else pass(std::false_type{}, j);
-  }
+  // The first two blocks meet the diagonal and a block j with
+  // (qb0 + j + 1) * 64 > T (j >= T / 64 - qb0) meets the end: masked passes
+  // are a prefix and a suffix, each range run by a loop of its own so that
+  // the accumulators stay in one register file.
+  const int j_end = min(nb, max(2, T / 64 - qb0));
+  int j = 0;
+  for (; j < min(2, nb); ++j) pass(std::true_type{}, j);
+  for (; j < j_end; ++j) pass(std::false_type{}, j);
+  for (; j < nb; ++j) pass(std::true_type{}, j);
   wait_vmem();  // the loads of the two blocks past the end still target LDS
 
   if (kj >= T) return;
