@@ -110,6 +110,14 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // half `g` (= lane / 32) of the wavefront.
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// Workgroup order for the attention kernels: workgroups are dealt to the 8
+// XCDs round-robin, so consecutive logical blocks (the key or query blocks of
+// one (batch, head)) are remapped onto one XCD, where they share Q/dO or K/V
+// in its L2.
+__device__ __forceinline__ int xcd_block(int lin, int n) {
+  return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
+}
+
 // ------------------------------------------------------------------ forward
 template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
@@ -118,9 +126,10 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 Vt[HD * (64 + 4)];
 
   const int T = p.T;
-  const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int nqb = gridDim.x;  // (T + 127) / 128
+  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
+  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn on one XCD, the longest first
+  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 5, li = lane & 31;
   const int q0 = qb * 128;
   const int qi = q0 + wv * 32 + li;
@@ -278,6 +287,7 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16* Vs, int x, int kb, int lan
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+
 __global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
   constexpr int HD = 128, KS = 8, HB = 4;
   __shared__ __attribute__((aligned(1024))) bf16 K0[64 * HD];
@@ -286,9 +296,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) bf16 V1[64 * HD];
 
   const int T = p.T;
-  const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int nqb = gridDim.x;  // (T + 127) / 128
+  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
+  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn on one XCD, the longest first
+  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, li = lane & 31;
@@ -476,14 +487,6 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
       : "=&s"(saved)
       : "s"(lds), "v"(voff), "s"(rs)
       : "memory");
-}
-
-// Workgroup order for the backward kernels: workgroups are dealt to the 8
-// XCDs round-robin, so consecutive logical blocks (the key or query blocks of
-// one (batch, head)) are remapped onto one XCD, where they share Q/dO or K/V
-// in its L2.
-__device__ __forceinline__ int xcd_block(int lin, int n) {
-  return (n & 7) == 0 ? (lin & 7) * (n >> 3) + (lin >> 3) : lin;
 }
 
 // dQ: 128 queries per workgroup, 32 per wavefront (its qh and dO fragments
@@ -1044,9 +1047,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_mfma(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 Vs[64 * (HD + 8)];
 
   const int T = p.T;
-  const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int nqb = gridDim.x;  // (T + 127) / 128
+  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
+  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn on one XCD, the longest first
+  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 5, li = lane & 31;
   const int q0 = qb * 128;
   const int qi = q0 + wv * 32 + li;
