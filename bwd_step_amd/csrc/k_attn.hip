@@ -572,17 +572,27 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
 #pragma unroll
   for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
 
-  // S^T and dP^T of one half (kk: 32 keys) of the block in stage st
+  // S^T and dP^T of one half (kk: 32 keys) of the block in stage st.  All 16
+  // fragment reads are issued in a scheduling region of their own, ahead of
+  // the MFMAs: with one wavefront per SIMD, a read placed next to the MFMA
+  // that consumes it stalls that MFMA for the whole LDS latency.
   auto phase_a = [&](uint32_t st, int kk, f32x16& S, f32x16& Pd) {
     const char* sb = smem + st * kStage;
     const bf16* Ks = (const bf16*)sb;
     const bf16* Vs = (const bf16*)(sb + kTile);
+    bf16x8 fk[KS], fv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      fk[s] = row_frag(Ks, kk * 32 + li, 2 * s + g);
+      fv[s] = row_frag(Vs, kk * 32 + li, 2 * s + g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     S = f32x16{};
     Pd = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      S = mfma(row_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], S);
-      Pd = mfma(row_frag(Vs, kk * 32 + li, 2 * s + g), df[s], Pd);
+      S = mfma(fk[s], qf[s], S);
+      Pd = mfma(fv[s], df[s], Pd);
     }
   };
   // dS^T = P (dP - D) of one half as bf16 B operands; MASKED: causal / length mask
@@ -609,20 +619,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
 #pragma unroll
       for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 32 + t * 16, lane), sf[t], dq[x]);
   };
-  // MFMA-led interleave: each MFMA preceded by NDS LDS reads and followed by
-  // NVALU vector instructions, over NM MFMAs.
-  auto interleave = [&](auto nm, auto nds, auto nvalu) {
+  // Instruction interleave of one section: LEAD LDS reads first, then NM
+  // groups of one MFMA, NDS LDS reads (for later MFMAs) and NVALU vector
+  // instructions.  The lead keeps the fragment reads several MFMAs ahead of
+  // their use, so with one wavefront per SIMD an MFMA does not wait out the
+  // LDS latency of its own operand.
+  auto interleave = [&](auto nm, auto lead, auto nds, auto nvalu) {
+    if constexpr (decltype(lead)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(lead)::value, 0);
 #pragma unroll
     for (int i = 0; i < decltype(nm)::value; ++i) {
-      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
       if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I4 = std::integral_constant<int, 4>;
+  using I2 = std::integral_constant<int, 2>;
+  using I6 = std::integral_constant<int, 6>;
   using I8 = std::integral_constant<int, 8>;
   using I16 = std::integral_constant<int, 16>;
 
@@ -636,15 +650,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     phase_a(cur, 1, Sb, Pb);
     phase_b(masked, Sa, Pa, kbase, sf);
-    interleave(I16{}, I1{}, I4{});
+    interleave(I16{}, I0{}, I0{}, I6{});
     phase_c(cur, 0, sf);
-    interleave(I8{}, I4{}, I0{});
+    interleave(I8{}, I6{}, I2{}, I0{});
     wait_block_and_sync();  // block j + 1
     phase_a(nxt, 0, Sa, Pa);
     phase_b(masked, Sb, Pb, kbase + 32, sf);
-    interleave(I16{}, I1{}, I4{});
+    interleave(I16{}, I0{}, I0{}, I6{});
     phase_c(cur, 1, sf);
-    interleave(I8{}, I4{}, I0{});
+    interleave(I8{}, I6{}, I2{}, I0{});
   };
 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, qh and dO
@@ -759,26 +773,37 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
   for (int x = 0; x < HB; ++x) { dk[x] = f32x16{}; dv[x] = f32x16{}; }
   const float c = p.scale_log2;
 
-  // S and D - dP of one half (mi) of the block in stage st
+  // S and D - dP of one half (mi) of the block in stage st.  The fragment and
+  // D reads are issued in a scheduling region of their own, ahead of the
+  // MFMAs, so that no MFMA waits out the LDS latency of its own operand.
   auto phase_a = [&](uint32_t st, int mi, f32x16& S, f32x16& Pd) {
     const char* sb = smem + st * kStage;
     const bf16* Qs = (const bf16*)sb;
     const bf16* Os = (const bf16*)(sb + kTile);
     const float* Ds = (const float*)(sb + 2 * kTile) + 256;
+    bf16x8 fq[KS], fo[KS];
+    f32x4 d4[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) d4[rb] = *reinterpret_cast<const f32x4*>(Ds + mi * 32 + 8 * rb + 4 * g);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      fq[s] = row_frag(Qs, mi * 32 + li, 2 * s + g);
+      fo[s] = row_frag(Os, mi * 32 + li, 2 * s + g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       // accumulator registers 4 rb .. 4 rb + 3 hold four consecutive queries
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + mi * 32 + 8 * rb + 4 * g);
-      Pd[4 * rb + 0] = d4.x;
-      Pd[4 * rb + 1] = d4.y;
-      Pd[4 * rb + 2] = d4.z;
-      Pd[4 * rb + 3] = d4.w;
+      Pd[4 * rb + 0] = d4[rb].x;
+      Pd[4 * rb + 1] = d4[rb].y;
+      Pd[4 * rb + 2] = d4[rb].z;
+      Pd[4 * rb + 3] = d4[rb].w;
     }
     S = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      S = mfma(row_frag(Qs, mi * 32 + li, 2 * s + g), kf[s], S);
-      Pd = mfma(row_frag(Os, mi * 32 + li, 2 * s + g), vn[s], Pd);
+      S = mfma(fq[s], kf[s], S);
+      Pd = mfma(fo[s], vn[s], Pd);
     }
   };
   // P = exp2(S c - lse) and -dS = P (D - dP) of one half, as bf16 B operands;
@@ -821,20 +846,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
         dk[x] = mfma(tr_frag(Qs, x, mi * 32 + t * 16, lane), sf[t], dk[x]);
       }
   };
-  // Instruction interleave of one pipelined section: each MFMA preceded by
-  // NDS LDS reads and followed by NVALU vector instructions.
-  auto interleave = [&](auto nds, auto nvalu) {
+  // Instruction interleave of one pipelined section of 16 MFMAs: LEAD LDS
+  // reads first, then per MFMA NDS LDS reads (for later MFMAs) and NVALU
+  // vector instructions, so that the reads run ahead of their MFMAs.
+  auto interleave = [&](auto lead, auto nds, auto nvalu) {
+    if constexpr (decltype(lead)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(lead)::value, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
       if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   using I0 = std::integral_constant<int, 0>;
   using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
+  using I8 = std::integral_constant<int, 8>;
 
   // One pass over block j (in stage j mod 4): its second half, then the first
   // half of block j + 1, whose loads are waited for in the middle.
@@ -848,15 +877,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     phase_a(cur, 1, Sb, Pb);
     phase_b(masked, Sa, Pa, cur, 0, qbase, pf, sf);
-    interleave(I2{}, I6{});
+    interleave(I4{}, I0{}, I6{});
     phase_c(cur, 0, pf, sf);
-    interleave(I2{}, I0{});
+    interleave(I8{}, I2{}, I0{});
     wait_block_and_sync();  // block j + 1
     phase_a(nxt, 0, Sa, Pa);
     phase_b(masked, Sb, Pb, cur, 1, qbase + 32, pf, sf);
-    interleave(I2{}, I6{});
+    interleave(I4{}, I0{}, I6{});
     phase_c(cur, 1, pf, sf);
-    interleave(I2{}, I0{});
+    interleave(I8{}, I2{}, I0{});
   };
 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, K and V
