@@ -106,10 +106,98 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const TD* __restrict__
   }
 }
 
+// The same two kernels with the row held in registers (NCH 16-byte chunks of
+// the row per lane, d <= 256 * NCH): every input is read from memory once,
+// instead of once for the statistic and again for the output.  At most 64
+// VGPRs (eight wavefronts per SIMD), so that enough loads stay in flight.
+template <class T, int NCH>
+__global__ void __launch_bounds__(256, 8) rmsnorm_fwd_reg_kernel(float* __restrict__ x, const bf16* __restrict__ res,
+                                                              T* __restrict__ y, float* __restrict__ r, int N, int d,
+                                                              float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  f32x4* xr = reinterpret_cast<f32x4*>(x + (size_t)row * d);
+  const int nc4 = d >> 2;
+  f32x4 v[NCH];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + 64 * k;
+    v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < nc4) {
+      v[k] = xr[c];
+      if (res) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(res + (size_t)row * d + 4 * c);
+        v[k] += f32x4{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
+        xr[c] = v[k];
+      }
+    }
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / (float)d + eps);
+  if (lane == 0) r[row] = rr;
+  T* yr = y + (size_t)row * d;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nc4) store4(yr + 4 * c, v[k] * rr);
+  }
+}
+
+template <class T, class TD, int NCH>
+__global__ void __launch_bounds__(256, 8) rmsnorm_bwd_reg_kernel(const TD* __restrict__ dy, const T* __restrict__ y,
+                                                              const float* __restrict__ r, float* __restrict__ dx,
+                                                              T* __restrict__ dx_lp, int N, int d, int accumulate) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const size_t base = (size_t)row * d;
+  const int nc4 = d >> 2;
+  f32x4 gk[NCH], vk[NCH];
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + 64 * k;
+    gk[k] = vk[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < nc4) {
+      gk[k] = load4(dy + base + 4 * c);
+      vk[k] = load4(y + base + 4 * c);
+    }
+    dot += gk[k].x * vk[k].x + gk[k].y * vk[k].y + gk[k].z * vk[k].z + gk[k].w * vk[k].w;
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float rr = r[row];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nc4) {
+      f32x4 o = (gk[k] - vk[k] * dot) * rr;
+      f32x4* dp = reinterpret_cast<f32x4*>(dx + base + 4 * c);
+      if (accumulate) o += *dp;
+      *dp = o;
+      if (dx_lp) store4(dx_lp + base + 4 * c, o);
+    }
+  }
+}
+
 template <class T>
 int rmsnorm_fwd_t(float* x, const void* res, void* y, float* r, int N, int d, float eps, hipStream_t s) {
   if (N == 0) return 0;
-  rmsnorm_fwd_kernel<T><<<(N + 3) / 4, 256, 0, s>>>(x, (const bf16*)res, (T*)y, r, N, d, eps);
+  const unsigned grid = (unsigned)((N + 3) / 4);
+  const bf16* rs = (const bf16*)res;
+  switch ((d + 255) / 256) {
+    case 1: rmsnorm_fwd_reg_kernel<T, 1><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 2: rmsnorm_fwd_reg_kernel<T, 2><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 3: rmsnorm_fwd_reg_kernel<T, 3><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 4: rmsnorm_fwd_reg_kernel<T, 4><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 5: rmsnorm_fwd_reg_kernel<T, 5><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 6: rmsnorm_fwd_reg_kernel<T, 6><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 7: rmsnorm_fwd_reg_kernel<T, 7><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    case 8: rmsnorm_fwd_reg_kernel<T, 8><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+    default: rmsnorm_fwd_kernel<T><<<grid, 256, 0, s>>>(x, rs, (T*)y, r, N, d, eps); break;
+  }
   NC_LAUNCH_CHECK();
   return 0;
 }
@@ -127,7 +215,21 @@ template <class T, class TD>
 int rmsnorm_bwd_t(const void* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d, int acc,
                   hipStream_t s) {
   if (N == 0) return 0;
-  rmsnorm_bwd_kernel<T, TD><<<(N + 3) / 4, 256, 0, s>>>((const TD*)dy, (const T*)y, r, dx, (T*)dx_lp, N, d, acc);
+  const unsigned grid = (unsigned)((N + 3) / 4);
+  const TD* g = (const TD*)dy;
+  const T* yy = (const T*)y;
+  T* lp = (T*)dx_lp;
+  switch ((d + 255) / 256) {
+    case 1: rmsnorm_bwd_reg_kernel<T, TD, 1><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 2: rmsnorm_bwd_reg_kernel<T, TD, 2><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 3: rmsnorm_bwd_reg_kernel<T, TD, 3><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 4: rmsnorm_bwd_reg_kernel<T, TD, 4><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 5: rmsnorm_bwd_reg_kernel<T, TD, 5><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 6: rmsnorm_bwd_reg_kernel<T, TD, 6><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 7: rmsnorm_bwd_reg_kernel<T, TD, 7><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    case 8: rmsnorm_bwd_reg_kernel<T, TD, 8><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+    default: rmsnorm_bwd_kernel<T, TD><<<grid, 256, 0, s>>>(g, yy, r, dx, lp, N, d, acc); break;
+  }
   NC_LAUNCH_CHECK();
   return 0;
 }
