@@ -568,6 +568,11 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     if (g == 0 && qi < T) p.Dbuf[(size_t)bh * T + qi] = Dl;
   }
   const float c = p.scale_log2;
+  // dP^T accumulators start at -D (one value per lane: its query), so they
+  // end at dP - D and dS = P (dP - D) takes one multiply
+  f32x16 negD;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD[r] = -Dl;
   f32x16 dq[HB];
 #pragma unroll
   for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
@@ -588,7 +593,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     S = f32x16{};
-    Pd = f32x16{};
+    Pd = negD;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       S = mfma(fk[s], qf[s], S);
@@ -606,7 +611,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
         const int key = kh + acc_row(r, g);
         pr = (key > qi || key >= T) ? 0.f : pr;
       }
-      dS[r] = pr * (Pd[r] - Dl);
+      dS[r] = pr * Pd[r];
     }
     sf[0] = pack8(dS, 0);
     sf[1] = pack8(dS, 1);
