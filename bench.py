@@ -12,8 +12,10 @@ events, and the float64 oracle's throughput on this host (cpu_baseline).
 
 --op attention | lmhead times one operation entry point instead of the step
 (the attention microbenchmark B16 x H10 x T2048 x hd128, or the fused LM head
-+ cross-entropy on 32768 x 1280 x 65536); these lines are for profiling the
-kernels and carry their own metric, not the headline one.
++ cross-entropy on 32768 x 1280 x 65536); --op copy times a plain 1 GiB
+device-to-device copy, the reference that scales the HBM byte counters
+(FETCH_SIZE, WRITE_SIZE) behind the roofline's `traffic`.  These lines are
+for profiling and carry their own metric, not the headline one.
 """
 
 import argparse
@@ -35,6 +37,28 @@ CONFIGS = {
     "d26": (26, 16, "zipf"),
 }
 METRIC = "train tokens/sec + MFU (fwd+bwd) on 1 MI355X, depth-20 bf16 seq 2048"
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_d20_b32x2048_hbm_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "bwd_step_amd", "csrc", "k_gemm.hip")
+
+
+def gemm_traffic_per_call():
+    """HBM bytes per GEMM call from the committed FETCH_SIZE / WRITE_SIZE runs
+    (profiles/gemm_d20_b32x2048_hbm_traffic.md), or None when that summary is
+    missing or was taken on a different GEMM source than the one built."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_call:\s*([0-9.eE+]+)", text)
+    h = re.search(r"k_gemm\.hip sha256:\s*([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != src:
+        return None
+    return float(m.group(1))
 
 
 def model_flops_per_token(c):
@@ -110,7 +134,14 @@ def op_bench(args):
 
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(args.seed)
-    if args.op == "attention":
+    if args.op == "copy":
+        nbytes = 1 << 30
+        src = torch.randint(0, 255, (nbytes,), device=dev, dtype=torch.uint8, generator=g)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)  # noqa: E731
+        flops = 0.0
+        name = "device copy of 1 GiB (byte-counter reference)"
+    elif args.op == "attention":
         B, H, T, hd = 16, 10, 2048, 128
         q, k, v, do = (torch.randn(B, T, H, hd, device=dev, generator=g).to(torch.bfloat16) for _ in range(4))
         fn = lambda: ops.attention_fwd_bwd(q, k, v, do)  # noqa: E731
@@ -135,6 +166,11 @@ def op_bench(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    if args.op == "copy":
+        print(json.dumps({"metric": name + " GB/s (read + write)", "value": round(2 * nbytes / ms / 1e6, 1),
+                          "unit": "GB/s", "ms_per_call": round(ms, 4), "bytes_read": nbytes, "bytes_written": nbytes,
+                          "steps": args.steps, "warmup": args.warmup, "higher_is_better": True}), flush=True)
+        return
     print(json.dumps({"metric": name + " model TFLOP/s", "value": round(flops / ms / 1e9, 1), "unit": "TFLOP/s",
                       "ms_per_call": round(ms, 4), "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
                       "data": "synthetic, seeded torch generator", "higher_is_better": True}), flush=True)
@@ -148,7 +184,7 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--op", choices=["attention", "lmhead"], default=None)
+    ap.add_argument("--op", choices=["attention", "lmhead", "copy"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the data-parallel sharding across "
@@ -224,7 +260,7 @@ def main():
     fpt = model_flops_per_token(cfg)
     mfu = tok_s * fpt / PEAK_BF16_FLOPS
 
-    launches, g_ms, g_fl, _ = prof["gemm"]
+    launches, g_ms, g_fl, g_by = prof["gemm"]
     gemm_tflops = g_fl / (g_ms / 1e3) / 1e12
     kernels = {}
     for name, (n, kms, fl, by) in prof.items():
@@ -269,7 +305,9 @@ def main():
             "peak": PEAK_BF16_FLOPS / 1e12,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops * 1e12 / PEAK_BF16_FLOPS, 4),
-            "traffic": None,
+            "traffic": gemm_traffic_per_call(),
+            "traffic_unit": "bytes per call (HBM, FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy)",
+            "algorithmic_bytes_per_call": round(g_by / launches),
             "launches_per_step": launches / args.steps,
             "avg_launch_us": round(g_ms * 1e3 / launches, 2),
         },

@@ -252,6 +252,22 @@ int read_status(void* ws, hipStream_t s) {
   } while (0)
 
 inline double gflops(const GemmCall& g) { return 2.0 * g.M * (double)g.N * g.K; }
+// Algorithmic HBM bytes of one GEMM call: each operand read once, the output
+// (and whatever the epilogue reads) once; split-K partials are not counted.
+inline double gbytes(const GemmCall& g) {
+  const double es = g.dtype == NC_BF16 ? 2.0 : 4.0, mn = (double)g.M * g.N;
+  double out = 0.0;
+  switch (g.epi) {
+    case EPI_F32: out = (g.e.beta ? 8.0 : 4.0) * mn; break;   // fp32 store (accumulate: read + write)
+    case EPI_F32_ACC: out = 8.0 * mn; break;
+    case EPI_RESID: out = 8.0 * mn; break;                     // fp32 residual read + write
+    case EPI_LP: case EPI_RELU2: out = es * mn; break;
+    case EPI_DRELU2: out = 2.0 * es * mn; break;               // g read, du written
+    case EPI_CE: out = 2.0 * mn + 8.0 * g.M * (double)g.e.nseg + 4.0 * g.M; break;
+    default: break;
+  }
+  return es * ((double)g.M * g.K + (double)g.N * g.K) + out;
+}
 
 GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, int M, int N, int K, int dtype) {
   GemmCall g;
@@ -282,23 +298,23 @@ int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int 
       float* tlog = aux + (size_t)chunk * nseg * 2;
       lg.epi = EPI_CE; lg.e.c_lp = G; lg.e.ld_lp = V; lg.e.tgt = y + c0; lg.e.part = part; lg.e.tlog = tlog;
       lg.e.nseg = nseg;
-      PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
+      PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
       PROF(pf, PC_CE, 0, (double)rows * V * 4 + (double)rows * nseg * 8,
            launch_ce_finish(part, nseg, tlog, y + c0, G, V, loss_rows + c0, rows, V, N, status, s));
     } else {
       lg.epi = EPI_F32; lg.e.c32 = aux; lg.e.ldc = V; lg.e.beta = 0;
-      PROF(pf, PC_GEMM, gflops(lg), 0, launch_gemm(lg, s));
+      PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
       PROF(pf, PC_CE, 0, (double)rows * V * (4 + es),
            launch_ce_rows(aux, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
     }
     GemmCall gw = mk(G, V, false, zc, d, false, V, d, rows, dtype);
     gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
     gw.splitk_ws = splitk; gw.splitk_bytes = splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(gw), 0, launch_gemm(gw, s));
+    PROF(pf, PC_GEMM, gflops(gw), gbytes(gw), launch_gemm(gw, s));
     GemmCall gz = mk(G, V, true, W, d, false, rows, d, V, dtype);
     gz.epi = EPI_F32; gz.e.c32 = dz + (size_t)c0 * d; gz.e.ldc = d; gz.e.beta = 0;
     gz.splitk_ws = splitk; gz.splitk_bytes = splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(gz), 0, launch_gemm(gz, s));
+    PROF(pf, PC_GEMM, gflops(gz), gbytes(gz), launch_gemm(gz, s));
   }
   return NC_OK;
 }
@@ -354,7 +370,7 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     TRY(norm(a1, (float*)(L + P.r1)));
     GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, 3 * hh, d, dt);
     g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
-    PROF(pf, PC_GEMM, gflops(g1), 0, launch_gemm(g1, s));
+    PROF(pf, PC_GEMM, gflops(g1), gbytes(g1), launch_gemm(g1, s));
     PROF(pf, PC_QK_FWD, 0, 4.0 * N * hh * es + 2.0 * N * H * 4, launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
                                (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, c.seq_len, c.norm_eps, dt, s));
     AttnArgs a;
@@ -367,14 +383,14 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     PROF(pf, PC_ATTN_FWD, 4.0 * hd * pairs, 0, launch_attn_fwd(a, hd, dt, s));
     GemmCall g2 = mk(L + P.O, hh, true, Wo, hh, true, N, d, hh, dt);
     proj_out(g2);
-    PROF(pf, PC_GEMM, gflops(g2), 0, launch_gemm(g2, s));
+    PROF(pf, PC_GEMM, gflops(g2), gbytes(g2), launch_gemm(g2, s));
     TRY(norm(L + P.m, (float*)(L + P.r2)));
     GemmCall g3 = mk(L + P.m, d, true, W1, d, true, N, F, d, dt);
     g3.epi = EPI_RELU2; g3.e.c_lp = L + P.g; g3.e.ld_lp = F;
-    PROF(pf, PC_GEMM, gflops(g3), 0, launch_gemm(g3, s));
+    PROF(pf, PC_GEMM, gflops(g3), gbytes(g3), launch_gemm(g3, s));
     GemmCall g4 = mk(L + P.g, F, true, W2, F, true, N, d, F, dt);
     proj_out(g4);
-    PROF(pf, PC_GEMM, gflops(g4), 0, launch_gemm(g4, s));
+    PROF(pf, PC_GEMM, gflops(g4), gbytes(g4), launch_gemm(g4, s));
   }
   TRY(norm(W + P.z, (float*)(W + P.rf)));
   return NC_OK;
@@ -444,25 +460,25 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     // MLP: du = (dx W_2) * 2 relu(u), with relu(u) = sqrt(g); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.g; b1.e.ld_aux = F;
-    PROF(pf, PC_GEMM, gflops(b1), 0, launch_gemm(b1, s));
+    PROF(pf, PC_GEMM, gflops(b1), gbytes(b1), launch_gemm(b1, s));
     GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
     b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b2), 0, launch_gemm(b2, s));
+    PROF(pf, PC_GEMM, gflops(b2), gbytes(b2), launch_gemm(b2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
     dgrad_out(b3);
-    PROF(pf, PC_GEMM, gflops(b3), 0, launch_gemm(b3, s));
+    PROF(pf, PC_GEMM, gflops(b3), gbytes(b3), launch_gemm(b3, s));
     GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
     b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk; b4.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b4), 0, launch_gemm(b4, s));
+    PROF(pf, PC_GEMM, gflops(b4), gbytes(b4), launch_gemm(b4, s));
     TRY(norm_bwd(L + P.m, (float*)(L + P.r2)));
 
     // attention output projection: dO = dx W_o; dW_o = dx^T O
     GemmCall b5 = mk(dx_lp, d, true, Wo, hh, false, N, hh, d, dt);
     b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
-    PROF(pf, PC_GEMM, gflops(b5), 0, launch_gemm(b5, s));
+    PROF(pf, PC_GEMM, gflops(b5), gbytes(b5), launch_gemm(b5, s));
     GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
     b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk; b6.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b6), 0, launch_gemm(b6, s));
+    PROF(pf, PC_GEMM, gflops(b6), gbytes(b6), launch_gemm(b6, s));
 
     AttnArgs a;
     a.q = qkv; a.ldq = 3 * hh;
@@ -484,10 +500,10 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
     GemmCall b7 = mk(dqkv, 3 * hh, true, Wqkv, d, false, N, d, 3 * hh, dt);
     dgrad_out(b7);
-    PROF(pf, PC_GEMM, gflops(b7), 0, launch_gemm(b7, s));
+    PROF(pf, PC_GEMM, gflops(b7), gbytes(b7), launch_gemm(b7, s));
     GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
     b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b8), 0, launch_gemm(b8, s));
+    PROF(pf, PC_GEMM, gflops(b8), gbytes(b8), launch_gemm(b8, s));
     TRY(norm_bwd(L + P.a1, (float*)(L + P.r1)));
   }
   PROF(pf, PC_EMB_BWD, 0, (double)N * d * 4 + (double)V * d * 4 * (accumulate ? 2 : 1) + N * 4.0,
