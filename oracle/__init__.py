@@ -18,7 +18,9 @@ pages this project was built from):
 * same page, "The 'One Dial' Design" -> "How dimensions are derived":
   d_model = 64 * depth, heads = d_model / 128, head_dim = 128, FFN = 4 * d_model.
 * same page, "The Full Pipeline" -> "Pretraining": causal next-token
-  prediction with a cross-entropy loss.
+  prediction with a cross-entropy loss; the optimizer step (Muon for the
+  matrices, AdamW for the embedding and unembedding, cosine schedule with
+  warmup, clipping at 1.0, weight decay 0.1) is in ``optim.py``.
 
 Readings where the pages are silent (each is listed in the design doc):
 parameter-free RMSNorm with eps = 1e-6 inside the square root; pre-norm
@@ -44,3 +46,4 @@ from .model import (  # noqa: F401
     forward_logits,
 )
 from . import ops  # noqa: F401
+from . import optim  # noqa: F401
