@@ -124,5 +124,34 @@ class Model:
         """Synchronise and return the device status code (0 = ok)."""
         return int(lib().nc_check(self._h))
 
+    # ---- optimizer step (nc_optim_*)
+    OPTIM_DEFAULTS = dict(lr_adamw=3e-3, lr_muon=0.02, beta1=0.9, beta2=0.95, eps=1e-8, momentum=0.95,
+                          weight_decay=0.1, clip=1.0, final_frac=0.0, warmup_steps=1, total_steps=1, ns_steps=5)
+
+    def optim_state_bytes(self):
+        return int(lib().nc_optim_state_bytes(self._h))
+
+    def optim_workspace_bytes(self):
+        return int(lib().nc_optim_workspace_bytes(self._h))
+
+    def optim_init(self, params, state):
+        """Masters = params, moments = 0 (state: device buffer of optim_state_bytes())."""
+        self.set_stream()
+        check(lib().nc_optim_init(self._h, _ptr(params), _ptr(state)), "nc_optim_init")
+
+    def optim_step(self, step, grads, params, state, workspace, grad_norm=None, **hp):
+        """One optimizer step; hp overrides OPTIM_DEFAULTS (nc_optim_config fields)."""
+        vals = dict(self.OPTIM_DEFAULTS)
+        unknown = set(hp) - set(vals)
+        if unknown:
+            raise TypeError(f"unknown optimizer settings {sorted(unknown)}")
+        vals.update(hp)
+        cfg = _nc.NcOptimConfig(**vals)
+        self.set_stream()
+        check(lib().nc_optim_step(self._h, ctypes.byref(cfg), int(step), _ptr(grads), _ptr(params), _ptr(state),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(grad_norm) if grad_norm is not None else None),
+              "nc_optim_step")
+
 
 from . import ops  # noqa: E402,F401

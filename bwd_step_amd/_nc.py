@@ -38,6 +38,15 @@ class NcTensorDesc(ctypes.Structure):
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
 
 
+class NcOptimConfig(ctypes.Structure):
+    _fields_ = [
+        ("lr_adamw", ctypes.c_float), ("lr_muon", ctypes.c_float), ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float), ("eps", ctypes.c_float), ("momentum", ctypes.c_float),
+        ("weight_decay", ctypes.c_float), ("clip", ctypes.c_float), ("final_frac", ctypes.c_float),
+        ("warmup_steps", ctypes.c_int32), ("total_steps", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+    ]
+
+
 class NcProfEntry(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("ms", ctypes.c_double),
                 ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
@@ -70,6 +79,10 @@ SIGNATURES = {
     "nc_embedding_bwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _u64, _vp]),
     "nc_gemm_workspace_bytes": (_u64, [_i, _i, _i, _i]),
     "nc_gemm": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _vp, _u64, _vp]),
+    "nc_optim_state_bytes": (_u64, [_vp]),
+    "nc_optim_workspace_bytes": (_u64, [_vp]),
+    "nc_optim_init": (_i, [_vp, _vp, _vp]),
+    "nc_optim_step": (_i, [_vp, ctypes.POINTER(NcOptimConfig), _i, _vp, _vp, _vp, _vp, _u64, _vp]),
 }
 
 _lib = None

@@ -102,4 +102,26 @@ int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, l
                    int V, int n_total, int dtype, int* status, hipStream_t s);
 int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s);
 
+// ---- optimizer (k_optim.hip)
+// deterministic sum of squares: nblk fp64 partials, then one finishing block
+int launch_sumsq(const float* x, size_t n, double* partials, int nblk, hipStream_t s);
+// mode 0: out0 = sqrt(sum) (may be null), out1 = min(1, clip / (sqrt(sum) + 1e-6));
+// mode 1: out1 = 1 / (sqrt(sum) + 1e-7)
+int launch_norm_finish(const double* partials, int nblk, float clip, int mode, float* out0, float* out1,
+                       hipStream_t s);
+int launch_adamw(float* w, float* m, float* v, const float* g, void* param, size_t n, const float* clip_scale,
+                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, int dtype, hipStream_t s);
+int launch_muon_momentum(const float* g, float* buf, float* U, size_t n, const float* clip_scale, float mu,
+                         double* partials, int nblk, hipStream_t s);
+// X = U * inv_norm in the wide orientation (U^T when rows > cols), element type dtype
+int launch_ns_init(const float* U, int rows, int cols, const float* inv_norm, void* X, int dtype, hipStream_t s);
+// out = alpha x + beta y (x, out: element type dtype; y: fp32)
+int launch_axpby(void* out, const void* x, const float* y, size_t n, float alpha, float beta, int dtype,
+                 hipStream_t s);
+// w -= lr (adj O + wd w), O = X (or X^T for a tall matrix); param = w
+int launch_muon_apply(float* w, void* param, const void* X, int rows, int cols, float lr, float adj, float wd,
+                      int dtype, hipStream_t s);
+int launch_widen(float* out, const void* in, size_t n, int dtype, hipStream_t s);
+int launch_zero(float* p, size_t n, hipStream_t s);
+
 }  // namespace nc

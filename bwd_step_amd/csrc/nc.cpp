@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -818,6 +819,173 @@ int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb, int b_
     g.splitk_bytes = ws_bytes;
   }
   return launch_gemm(g, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ optimizer
+namespace {
+
+constexpr int kNormBlocks = 1024;
+
+bool optim_is_adamw(const Desc& t) { return t.name == "E" || t.name == "W_lm"; }
+
+// State (fp32 elements): masters [nparams], then per tensor in layout order
+// its AdamW moments (2 x size) or its Muon momentum (1 x size).
+struct OptimPlan {
+  std::vector<uint64_t> aux;  // per tensor: element offset of its first state array
+  uint64_t state_elems = 0;
+  // workspace (bytes)
+  size_t partials = 0, scalars = 0, U = 0, X = 0, A = 0, AA = 0, B2 = 0, BX = 0, splitk = 0, total = 0;
+  uint64_t splitk_bytes = 0;
+};
+
+OptimPlan optim_plan(const nc_ctx* x) {
+  OptimPlan p;
+  uint64_t o = x->nparams;
+  size_t max_mn = 0, max_rr = 0;
+  uint64_t sk = 0;
+  const int dt = x->cfg.dtype;
+  for (const Desc& t : x->layout) {
+    const uint64_t n = (uint64_t)t.rows * t.cols;
+    p.aux.push_back(o);
+    o += optim_is_adamw(t) ? 2 * n : n;
+    if (!optim_is_adamw(t)) {
+      const int r = std::min(t.rows, t.cols), c = std::max(t.rows, t.cols);
+      max_mn = std::max(max_mn, (size_t)n);
+      max_rr = std::max(max_rr, (size_t)r * r);
+      sk = std::max(sk, gemm_ws_bytes(r, r, r, dt));
+      sk = std::max(sk, gemm_ws_bytes(r, c, r, dt));
+    }
+  }
+  p.state_elems = o;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  size_t w = 0;
+  auto take = [&](size_t b) { size_t r = w; w += al(b); return r; };
+  p.partials = take(kNormBlocks * sizeof(double));
+  p.scalars = take(4 * sizeof(float));  // grad norm, clip factor, 1/|U|_F
+  p.U = take(max_mn * 4);
+  p.X = take(max_mn * es);
+  p.A = take(max_rr * es);
+  p.AA = take(max_rr * 4);
+  p.B2 = take(max_rr * es);
+  p.BX = take(max_mn * 4);
+  p.splitk = take(sk);
+  p.splitk_bytes = sk;
+  p.total = w;
+  return p;
+}
+
+// Schedule multiplier of step s (the formula nc.h states).
+double optim_lr_mult(const nc_optim_config& c, int s) {
+  if (s < c.warmup_steps) return (s + 1.0) / c.warmup_steps;
+  double p = (double)(s - c.warmup_steps) / std::max(1, c.total_steps - c.warmup_steps);
+  p = std::min(1.0, std::max(0.0, p));
+  return c.final_frac + (1.0 - c.final_frac) * 0.5 * (1.0 + std::cos(M_PI * p));
+}
+
+bool optim_config_ok(const nc_optim_config& c) {
+  auto in01 = [](float v) { return v >= 0.f && v < 1.f; };
+  return c.lr_adamw >= 0.f && c.lr_muon >= 0.f && in01(c.beta1) && in01(c.beta2) && c.eps > 0.f &&
+         in01(c.momentum) && c.weight_decay >= 0.f && c.clip > 0.f && c.final_frac >= 0.f && c.final_frac <= 1.f &&
+         c.warmup_steps >= 1 && c.total_steps >= c.warmup_steps && c.ns_steps >= 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t nc_optim_state_bytes(const nc_ctx* ctx) {
+  if (!ctx) return 0;
+  return optim_plan(ctx).state_elems * 4;
+}
+
+uint64_t nc_optim_workspace_bytes(const nc_ctx* ctx) {
+  if (!ctx) return 0;
+  return optim_plan(ctx).total;
+}
+
+int nc_optim_init(nc_ctx* ctx, const void* params, void* state) {
+  if (!ctx || !params || !state) return NC_ERR_NULL;
+  const OptimPlan p = optim_plan(ctx);
+  float* st = (float*)state;
+  TRY(launch_widen(st, params, ctx->nparams, ctx->cfg.dtype, ctx->stream));
+  return launch_zero(st + ctx->nparams, p.state_elems - ctx->nparams, ctx->stream);
+}
+
+int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float* grads, void* params, void* state,
+                  void* workspace, uint64_t ws_bytes, float* grad_norm) {
+  if (!ctx || !cfg || !grads || !params || !state || !workspace) return NC_ERR_NULL;
+  if (step < 0 || !optim_config_ok(*cfg)) return NC_ERR_ARG;
+  const OptimPlan P = optim_plan(ctx);
+  if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = ctx->stream;
+  const int dt = ctx->cfg.dtype;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  char* W = (char*)workspace;
+  float* st = (float*)state;
+  double* partials = (double*)(W + P.partials);
+  float* sc = (float*)(W + P.scalars);  // [0] |g|, [1] clip factor, [2] 1/|U|_F
+  const double mult = optim_lr_mult(*cfg, step);
+
+  // global gradient norm and clip factor
+  TRY(launch_sumsq(grads, ctx->nparams, partials, kNormBlocks, s));
+  TRY(launch_norm_finish(partials, kNormBlocks, cfg->clip, 0, sc, sc + 1, s));
+  if (grad_norm) {
+    if (hipMemcpyAsync(grad_norm, sc, sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess) return NC_ERR_HIP;
+  }
+
+  const double t = step + 1.0;
+  const float bc1 = (float)(1.0 - std::pow((double)cfg->beta1, t));
+  const float bc2 = (float)(1.0 - std::pow((double)cfg->beta2, t));
+  const float lr_a = (float)(cfg->lr_adamw * mult), lr_m = (float)(cfg->lr_muon * mult);
+  const float a = 3.4445f, b = -4.7750f, c = 2.0315f;  // quintic Newton-Schulz coefficients
+  for (size_t ti = 0; ti < ctx->layout.size(); ++ti) {
+    const Desc& d = ctx->layout[ti];
+    const size_t n = (size_t)d.rows * d.cols;
+    float* w = st + d.offset;
+    const float* g = grads + d.offset;
+    char* prm = (char*)params + d.offset * es;
+    if (optim_is_adamw(d)) {
+      float* m1 = st + P.aux[ti];
+      TRY(launch_adamw(w, m1, m1 + n, g, prm, n, sc + 1, lr_a, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
+                       bc1, bc2, dt, s));
+      continue;
+    }
+    // Muon: momentum, then Newton-Schulz on the wide orientation X [r x cc]
+    float* U = (float*)(W + P.U);
+    TRY(launch_muon_momentum(g, st + P.aux[ti], U, n, sc + 1, cfg->momentum, partials, kNormBlocks, s));
+    TRY(launch_norm_finish(partials, kNormBlocks, 0.f, 1, nullptr, sc + 2, s));
+    void* X = W + P.X;
+    TRY(launch_ns_init(U, d.rows, d.cols, sc + 2, X, dt, s));
+    const int r = std::min(d.rows, d.cols), cc = std::max(d.rows, d.cols);
+    void* A = W + P.A;
+    float* AA = (float*)(W + P.AA);
+    void* B2 = W + P.B2;
+    float* BX = (float*)(W + P.BX);
+    for (int k = 0; k < cfg->ns_steps; ++k) {
+      // A = X X^T
+      GemmCall g1 = mk(X, cc, true, X, cc, true, r, r, cc, dt);
+      g1.epi = EPI_LP; g1.e.c_lp = A; g1.e.ld_lp = r;
+      TRY(launch_gemm(g1, s));
+      // AA = A A (A is symmetric, so its rows are also its columns)
+      GemmCall g2 = mk(A, r, true, A, r, true, r, r, r, dt);
+      g2.epi = EPI_F32; g2.e.c32 = AA; g2.e.ldc = r;
+      g2.splitk_ws = (float*)(W + P.splitk); g2.splitk_bytes = P.splitk_bytes;
+      TRY(launch_gemm(g2, s));
+      // B2 = b A + c A A
+      TRY(launch_axpby(B2, A, AA, (size_t)r * r, b, c, dt, s));
+      // BX = B2 X, then X = a X + BX
+      GemmCall g3 = mk(B2, r, true, X, cc, false, r, cc, r, dt);
+      g3.epi = EPI_F32; g3.e.c32 = BX; g3.e.ldc = cc;
+      g3.splitk_ws = (float*)(W + P.splitk); g3.splitk_bytes = P.splitk_bytes;
+      TRY(launch_gemm(g3, s));
+      TRY(launch_axpby(X, X, BX, (size_t)r * cc, a, 1.f, dt, s));
+    }
+    const float adj = (float)std::sqrt(std::max(1.0, (double)d.rows / d.cols));
+    TRY(launch_muon_apply(w, prm, X, d.rows, d.cols, lr_m, adj, cfg->weight_decay, dt, s));
+  }
+  return 0;
 }
 
 }  // extern "C"

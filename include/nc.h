@@ -177,6 +177,69 @@ int nc_profile_enable(nc_ctx* ctx, int on);
 int nc_profile_read(nc_ctx* ctx, nc_prof_entry* out, int cap);
 
 /* ------------------------------------------------------------------------
+ * Optimizer step ("nanochat explainer", The Full Pipeline -> Pretraining:
+ * Muon for the matrix (2-D) weights, AdamW for the embedding and the
+ * unembedding, a cosine learning-rate schedule with warmup, gradient
+ * clipping at 1.0, weight decay 0.1).  The pages give only this outline;
+ * AdamW is the decoupled form of Loshchilov and Hutter, Muon follows its
+ * published description (Jordan et al., 2024).  Groups: AdamW for E and
+ * W_lm; Muon for every layer tensor (W_qkv as one [3*H*hd, d] matrix, W_o,
+ * W_1, W_2).  With s the 0-based step and m the schedule multiplier
+ *   m = (s + 1) / warmup_steps                         for s < warmup_steps,
+ *   m = f + (1 - f) (1 + cos(pi p)) / 2, p = (s - warmup) / max(1, total - warmup),
+ * every gradient is first multiplied by min(1, clip / (|g|_2 + 1e-6)), |g|_2
+ * the norm over all gradients; then
+ *   AdamW (t = s + 1): m1 = b1 m1 + (1-b1) g, m2 = b2 m2 + (1-b2) g^2,
+ *     w -= lr_adamw m (m1/(1-b1^t) / (sqrt(m2/(1-b2^t)) + eps) + wd w);
+ *   Muon: B = mu B + G, U = G + mu B, O = NS(U) (ns_steps quintic
+ *     Newton-Schulz steps with (a, b, c) = (3.4445, -4.7750, 2.0315) on
+ *     U/(|U|_F + 1e-7), run on the wide orientation),
+ *     W -= lr_muon m (sqrt(max(1, rows/cols)) O + wd W).
+ * The weights being updated are fp32 masters kept in the optimizer state;
+ * after the step the model's parameters (element type cfg.dtype) are
+ * rewritten from them.  On the bf16 path the Newton-Schulz operands are
+ * bf16 with fp32 accumulation.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float lr_adamw;      /* peak learning rate of E and W_lm */
+  float lr_muon;       /* peak learning rate of the layer matrices */
+  float beta1, beta2;  /* AdamW moment decays, in [0, 1) */
+  float eps;           /* AdamW denominator term, > 0 */
+  float momentum;      /* Muon (Nesterov) momentum, in [0, 1) */
+  float weight_decay;  /* decoupled, both groups, >= 0 */
+  float clip;          /* global gradient-norm bound, > 0 */
+  float final_frac;    /* learning rate at the end of the decay / peak, in [0, 1] */
+  int32_t warmup_steps;  /* >= 1 */
+  int32_t total_steps;   /* >= warmup_steps */
+  int32_t ns_steps;      /* Newton-Schulz iterations, >= 0 (5) */
+} nc_optim_config;
+
+/*
+ * Bytes of optimizer state (device, fp32, 256-byte aligned, owned by the
+ * caller): the master weights in the flat layout, then the AdamW moments of
+ * E and W_lm, then the Muon momentum of the layer tensors.  0 for a NULL ctx.
+ */
+uint64_t nc_optim_state_bytes(const nc_ctx* ctx);
+/* Bytes of workspace nc_optim_step needs (norm partials, Newton-Schulz temporaries). */
+uint64_t nc_optim_workspace_bytes(const nc_ctx* ctx);
+/*
+ * Start the optimizer: masters = params (element type cfg.dtype, flat
+ * layout), every moment and momentum = 0.  Enqueued on the context's stream.
+ * Errors: NC_ERR_NULL.
+ */
+int nc_optim_init(nc_ctx* ctx, const void* params, void* state);
+/*
+ * One optimizer step `step` (0-based) from the fp32 gradients `grads` (flat
+ * layout): updates the state and rewrites params.  grad_norm (device fp32
+ * scalar, may be NULL) receives |g|_2 before clipping.  Enqueued on the
+ * context's stream; nothing is read back to the host.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (a hyperparameter outside its range, or
+ * step < 0), NC_ERR_WORKSPACE (ws_bytes < nc_optim_workspace_bytes).
+ */
+int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float* grads, void* params,
+                  void* state, void* workspace, uint64_t ws_bytes, float* grad_norm);
+
+/* ------------------------------------------------------------------------
  * Operation entry points (stateless).  Each takes its own workspace; the
  * matching *_workspace_bytes() gives its size.  `dtype` is an nc_dtype and
  * sets the element type of the non-fp32 arguments marked "(dt)".

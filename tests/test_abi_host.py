@@ -143,3 +143,39 @@ def test_strerror_covers_codes():
     for c in range(9):
         assert lib().nc_strerror(c)
     assert lib().nc_strerror(99) == b"unknown status"
+
+
+def test_optim_sizes_and_host_errors():
+    cfg = make()
+    rc, h = init(cfg)
+    assert rc == 0
+    P = lib().nc_param_count(h)
+    n_e = n_lm = 512 * 128
+    # masters, AdamW moments (2x) of E and W_lm, Muon momentum (1x) of the rest
+    assert lib().nc_optim_state_bytes(h) == 4 * (2 * P + n_e + n_lm)
+    assert lib().nc_optim_state_bytes(None) == 0 and lib().nc_optim_workspace_bytes(None) == 0
+    need = lib().nc_optim_workspace_bytes(h)
+    assert need > 0
+    fake = ctypes.c_void_p(0x1000)
+    good = dict(lr_adamw=3e-3, lr_muon=0.02, beta1=0.9, beta2=0.95, eps=1e-8, momentum=0.95, weight_decay=0.1,
+                clip=1.0, final_frac=0.0, warmup_steps=1, total_steps=10, ns_steps=5)
+
+    def step(step_=0, ws=need, null=None, **over):
+        c = _nc.NcOptimConfig(**dict(good, **over))
+        args = [h, ctypes.byref(c), step_, fake, fake, fake, fake, ws, None]
+        if null is not None:
+            args[null] = None
+        return lib().nc_optim_step(*args)
+
+    # every case is rejected on the host, before anything is enqueued
+    assert step(ws=need - 1) == 3
+    assert step(step_=-1) == 8
+    for bad in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(momentum=1.0), dict(clip=0.0),
+                dict(final_frac=1.5), dict(warmup_steps=0), dict(total_steps=0), dict(ns_steps=-1),
+                dict(lr_muon=-1.0), dict(weight_decay=-0.1)):
+        assert step(**bad) == 8, bad
+    for i in (0, 1, 3, 4, 5, 6):
+        assert step(null=i) == 2, i
+    assert lib().nc_optim_init(h, None, fake) == 2
+    assert lib().nc_optim_init(h, fake, None) == 2
+    lib().nc_destroy(h)
