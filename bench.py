@@ -12,7 +12,8 @@ events, and the float64 oracle's throughput on this host (cpu_baseline).
 
 --op attention | lmhead times one operation entry point instead of the step
 (the attention microbenchmark B16 x H10 x T2048 x hd128, or the fused LM head
-+ cross-entropy on 32768 x 1280 x 65536); --op copy times a plain 1 GiB
++ cross-entropy on 32768 x 1280 x 65536); --op optim times the optimizer
+step (nc_optim_step) over the depth-20 parameter set; --op copy times a plain 1 GiB
 device-to-device copy, the reference that scales the HBM byte counters
 (FETCH_SIZE, WRITE_SIZE) behind the roofline's `traffic`.  These lines are
 for profiling and carry their own metric, not the headline one.
@@ -141,6 +142,29 @@ def op_bench(args):
         fn = lambda: dst.copy_(src)  # noqa: E731
         flops = 0.0
         name = "device copy of 1 GiB (byte-counter reference)"
+    elif args.op == "optim":
+        import bwd_step_amd
+        model = bwd_step_amd.Model(20, vocab=65536, seq_len=2048, max_batch=1, dtype="bf16")
+        P = model.param_count
+        flat = (0.02 * torch.randn(P, device=dev, generator=g)).to(torch.bfloat16)
+        grads = 1e-3 * torch.randn(P, device=dev, generator=g)
+        state = torch.empty(model.optim_state_bytes() // 4, dtype=torch.float32, device=dev)
+        ws = torch.empty(model.optim_workspace_bytes(), dtype=torch.uint8, device=dev)
+        model.optim_init(flat, state)
+        gnorm = torch.empty((), dtype=torch.float32, device=dev)
+        hp = dict(warmup_steps=10, total_steps=1000)
+        ctr = [0]
+
+        def fn():
+            model.optim_step(ctr[0], grads, flat, state, ws, grad_norm=gnorm, **hp)
+            ctr[0] += 1
+        lay = model.layout()
+        muon = [(r, c) for n, _, r, c in lay if n not in ("E", "W_lm")]
+        flops = 0.0
+        for r, c in muon:
+            a, b = min(r, c), max(r, c)
+            flops += 5 * (4.0 * a * a * b + 2.0 * a ** 3)  # X X^T, A A, (bA + cAA) X per Newton-Schulz step
+        name = f"optimizer step (AdamW E/W_lm + Muon, 5 Newton-Schulz steps) depth-20, {P} parameters"
     elif args.op == "attention":
         B, H, T, hd = 16, 10, 2048, 128
         q, k, v, do = (torch.randn(B, T, H, hd, device=dev, generator=g).to(torch.bfloat16) for _ in range(4))
@@ -166,6 +190,13 @@ def op_bench(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    if args.op == "optim":
+        print(json.dumps({"metric": name + " ms per step", "value": round(ms, 3), "unit": "ms",
+                          "newton_schulz_tflop": round(flops / 1e12, 3),
+                          "newton_schulz_tflops_if_all_time": round(flops / ms / 1e9, 1),
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16 params, fp32 state",
+                          "data": "synthetic, seeded torch generator", "higher_is_better": False}), flush=True)
+        return
     if args.op == "copy":
         print(json.dumps({"metric": name + " GB/s (read + write)", "value": round(2 * nbytes / ms / 1e6, 1),
                           "unit": "GB/s", "ms_per_call": round(ms, 4), "bytes_read": nbytes, "bytes_written": nbytes,
@@ -184,7 +215,7 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--op", choices=["attention", "lmhead", "copy"], default=None)
+    ap.add_argument("--op", choices=["attention", "lmhead", "copy", "optim"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the data-parallel sharding across "

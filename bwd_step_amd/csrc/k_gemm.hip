@@ -37,6 +37,8 @@ struct GemmParams {
   int splits;
   int tiles_m, tiles_n;
   int group;  // tile-rows per group of the tile walk
+  int batch;  // independent products (1 unless batched)
+  long a_bs, b_bs;  // bytes between consecutive batch members' A and B
   EpiArgs e;
 };
 
@@ -90,6 +92,11 @@ __device__ __forceinline__ void epi_apply4(const EpiArgs& e, int split, long i, 
     store4((T*)e.c_lp + i * e.ld_lp + j, r * r);
   } else if constexpr (EPI == EPI_DRELU2) {
     store4((T*)e.c_lp + i * e.ld_lp + j, drelu2(v, load4((const T*)e.aux + i * e.ld_aux + j)));
+  } else if constexpr (EPI == EPI_AXPBY) {
+    const f32x4 x = load4((const T*)e.aux + i * e.ld_aux + j);
+    store4((T*)e.c_lp + i * e.ld_lp + j,
+           f32x4{fmaf(e.alpha, x.x, e.beta_f * v.x), fmaf(e.alpha, x.y, e.beta_f * v.y),
+                 fmaf(e.alpha, x.z, e.beta_f * v.z), fmaf(e.alpha, x.w, e.beta_f * v.w)});
   }
 }
 
@@ -108,6 +115,9 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int split, long i, l
   } else if constexpr (EPI == EPI_DRELU2) {
     const float g = to_f32(((const T*)e.aux)[i * e.ld_aux + j]);
     ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(2.f * sqrtf(g) * v);
+  } else if constexpr (EPI == EPI_AXPBY) {
+    const float x = to_f32(((const T*)e.aux)[i * e.ld_aux + j]);
+    ((T*)e.c_lp)[i * e.ld_lp + j] = from_f32<T>(fmaf(e.alpha, x, e.beta_f * v));
   }
 }
 
@@ -247,15 +257,18 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   // B columns in the XCD's L2.
   const int G = gridDim.x;
   const int ntiles = p.tiles_m * p.tiles_n;
-  const int nitems = ntiles * p.splits;
+  const int per_batch = ntiles * p.splits;
+  const int nitems = per_batch * p.batch;
   const int wfirst = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   if (wfirst >= nitems) return;
 
   struct Item {
-    int m0, n0, kbeg, kend, nk, split;
+    int m0, n0, kbeg, kend, nk, split, b;
   };
   auto item = [&](int i) {
     Item r;
+    r.b = i / per_batch;
+    i -= r.b * per_batch;
     r.split = i / ntiles;
     const int t = i - r.split * ntiles;
     const int group_span = p.group * p.tiles_n;
@@ -279,6 +292,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     const long sh = live ? (long)k0 * kstep : 0;
     return make_rsrc((const char*)base + sh, live ? bytes - (uint32_t)sh : 0u);
   };
+  auto a_base = [&](const Item& it_) { return (const void*)((const char*)p.A + it_.b * p.a_bs); };
+  auto b_base = [&](const Item& it_) { return (const void*)((const char*)p.B + it_.b * p.b_bs); };
   // per-lane offsets of this wavefront's four blocks of A and B for an item
   auto item_voff = [&](const Item& it_, uint32_t* va, uint32_t* vb) {
 #pragma unroll
@@ -313,8 +328,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   auto load_slice = [&](bf16* an, bf16* bn, const uint32_t* va, const uint32_t* vb, const Item& it_, int j) {
     const int k0 = it_.kbeg + j * kBK;
     const bool live = j < it_.nk;
-    const rsrc_t rsa = slice_rsrc(p.A, p.a_bytes, a_kstep, k0, live);
-    const rsrc_t rsb = slice_rsrc(p.B, p.b_bytes, b_kstep, k0, live);
+    const rsrc_t rsa = slice_rsrc(a_base(it_), p.a_bytes, a_kstep, k0, live);
+    const rsrc_t rsb = slice_rsrc(b_base(it_), p.b_bytes, b_kstep, k0, live);
     issue2(an, bn, va, vb, rsa, rsb, 0, k0, it_.kend);
     issue2(an, bn, va, vb, rsa, rsb, 2, k0, it_.kend);
   };
@@ -354,8 +369,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
                      const uint32_t* va, const uint32_t* vb, const Item& it_, int j, bool alive) {
     const int k0 = it_.kbeg + j * kBK;
     const bool live = alive && j < it_.nk;
-    const rsrc_t rsa = slice_rsrc(p.A, p.a_bytes, a_kstep, k0, live);
-    const rsrc_t rsb = slice_rsrc(p.B, p.b_bytes, b_kstep, k0, live);
+    const rsrc_t rsa = slice_rsrc(a_base(it_), p.a_bytes, a_kstep, k0, live);
+    const rsrc_t rsb = slice_rsrc(b_base(it_), p.b_bytes, b_kstep, k0, live);
     bf16x8 fa1[FM], fb1[FN];
     issue2(an, bn, va, vb, rsa, rsb, 0, k0, it_.kend);
     read_step(as, bs, 1, fa1, fb1);
@@ -379,7 +394,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
         for (int q = 0; q < 4; ++q) {
           const long j = ci.n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
           if (i < p.M && j < p.N)
-            epi_apply4<EPI>(p.e, ci.split, i, j,
+            epi_apply4<EPI>(p.e, ci.split, i + (long)ci.b * p.M, j,
                             f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2],
                                   acc[a][c][4 * q + 3]});
         }
@@ -559,12 +574,13 @@ __global__ void __launch_bounds__(256) gemm_simt_kernel(GemmParams p) {
   const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
   const int m0 = tm * 64, n0 = tn * 64;
   const int split = blockIdx.z;
+  const int bb = blockIdx.y;  // batch member
   const int kbeg = split * p.kchunk;
   const int kend = min(p.K, kbeg + p.kchunk);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4] = {};
-  const float* Ag = (const float*)p.A;
-  const float* Bg = (const float*)p.B;
+  const float* Ag = (const float*)((const char*)p.A + bb * p.a_bs);
+  const float* Bg = (const float*)((const char*)p.B + bb * p.b_bs);
   for (int k0 = kbeg; k0 < kend; k0 += 16) {
     for (int e = threadIdx.x; e < 64 * 16; e += 256) {
       int r, kk;
@@ -591,7 +607,7 @@ __global__ void __launch_bounds__(256) gemm_simt_kernel(GemmParams p) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       const long i = m0 + ty * 4 + x, j = n0 + tx * 4 + y;
-      if (i < p.M && j < p.N) epi_apply<EPI, float>(p.e, split, i, j, acc[x][y]);
+      if (i < p.M && j < p.N) epi_apply<EPI, float>(p.e, split, i + (long)bb * p.M, j, acc[x][y]);
     }
 }
 
@@ -619,8 +635,8 @@ static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, dim3 grid, hipS
 }
 // A k-contiguous operand with K % 32 != 0 needs the per-lane cut of the last
 // slice; the model's layers never do (their widths are multiples of 64), so
-// only the fp32-output products (the general matrix-product entry point)
-// carry that variant.
+// only the fp32-output products (the general matrix-product entry point) and
+// the Newton-Schulz combination (EPI_AXPBY) carry that variant.
 template <int EPI>
 static int launch_mfma(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
   const bool ktail = (ak || bk) && (p.K % kBK) != 0;
@@ -628,7 +644,7 @@ static int launch_mfma(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStre
     launch_mfma_k<EPI, false>(p, ak, bk, grid, s);
     return 0;
   }
-  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC) {
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC || EPI == EPI_AXPBY) {
     launch_mfma_k<EPI, true>(p, ak, bk, grid, s);
     return 0;
   }
@@ -724,8 +740,15 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   p.tiles_m = (g.M + t - 1) / t;
   p.tiles_n = (g.N + t - 1) / t;
   p.e = g.e;
+  if (g.batch < 1) return NC_ERR_ARG;
+  const bool batched = g.batch > 1;
+  if (batched && !(g.epi == EPI_LP || g.epi == EPI_AXPBY || (g.epi == EPI_F32 && !g.e.beta)))
+    return NC_ERR_UNSUPPORTED;
+  p.batch = g.batch;
+  p.a_bs = g.a_bstride * (g.dtype == 0 ? 2 : 4);
+  p.b_bs = g.b_bstride * (g.dtype == 0 ? 2 : 4);
   int splits = 1;
-  if (g.epi == EPI_F32 && g.splitk_ws) splits = gemm_splits(g.M, g.N, g.K, g.dtype);
+  if (g.epi == EPI_F32 && g.splitk_ws && !batched) splits = gemm_splits(g.M, g.N, g.K, g.dtype);
   int kchunk = g.K;
   if (splits > 1) {
     // chunks of a multiple of four 32-deep slices (the kernel runs them in fours)
@@ -745,10 +768,10 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   p.kchunk = kchunk > 0 ? kchunk : 1;
   p.splits = splits;
   p.group = gemm_group(p.tiles_m, p.tiles_n, splits);
-  dim3 grid(p.tiles_m * p.tiles_n, 1, splits);
+  dim3 grid(p.tiles_m * p.tiles_n, g.batch, splits);
   if (g.dtype == 0) {
     // persistent: one workgroup per compute unit (each holds 128 KB of LDS)
-    const long items = (long)p.tiles_m * p.tiles_n * splits;
+    const long items = (long)p.tiles_m * p.tiles_n * splits * g.batch;
     grid = dim3((unsigned)std::min<long>(items, num_cus()), 1, 1);
   }
   // K == 0 runs the kernels with an empty k-loop: the epilogue sees zeros.
@@ -764,6 +787,7 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
       case EPI_RELU2: rc = launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_DRELU2: rc = launch_mfma<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_CE: rc = launch_mfma<EPI_CE>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_AXPBY: rc = launch_mfma<EPI_AXPBY>(p, g.a_k, g.b_k, grid, s); break;
       default: return 8;
     }
     if (rc) return rc;
@@ -774,6 +798,7 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
       case EPI_LP: launch_simt<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_RELU2: launch_simt<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_DRELU2: launch_simt<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
+      case EPI_AXPBY: launch_simt<EPI_AXPBY>(p, g.a_k, g.b_k, grid, s); break;
       default: return 8;
     }
   }

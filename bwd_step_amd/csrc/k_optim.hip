@@ -4,7 +4,8 @@
 // decay 0.1).  AdamW follows Loshchilov and Hutter's decoupled form; Muon
 // follows its published description (Jordan et al., 2024): Nesterov
 // momentum, then the quintic Newton-Schulz orthogonalisation of the update,
-// whose matrix products run on the MFMA GEMM (k_gemm.hip).
+// whose matrix products run, batched over same-shape matrices, on the MFMA
+// GEMM (k_gemm.hip).
 //
 // The state is fp32: master weights of every parameter, AdamW moments, Muon
 // momentum.  The model's parameters (bf16, or fp32 on the debug path) are
@@ -189,24 +190,6 @@ int launch_ns_init(const float* U, int rows, int cols, const float* inv_norm, vo
   const int tr = rows > cols;
   if (dtype == 0) ns_init_kernel<bf16><<<grid, 256, 0, s>>>(U, rows, cols, inv_norm, (bf16*)X, tr);
   else ns_init_kernel<float><<<grid, 256, 0, s>>>(U, rows, cols, inv_norm, (float*)X, tr);
-  NC_LAUNCH_CHECK();
-  return 0;
-}
-
-// out = alpha * x (element type T) + beta * y (fp32), n elements, stored as T.
-template <class T>
-__global__ void __launch_bounds__(256) axpby_kernel(T* __restrict__ out, const T* __restrict__ x,
-                                                    const float* __restrict__ y, size_t n, float alpha, float beta) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    out[i] = from_f32<T>(alpha * to_f32(x[i]) + beta * y[i]);
-}
-
-int launch_axpby(void* out, const void* x, const float* y, size_t n, float alpha, float beta, int dtype,
-                 hipStream_t s) {
-  if (n == 0) return 0;
-  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 16384);
-  if (dtype == 0) axpby_kernel<bf16><<<grid, 256, 0, s>>>((bf16*)out, (const bf16*)x, y, n, alpha, beta);
-  else axpby_kernel<float><<<grid, 256, 0, s>>>((float*)out, (const float*)x, y, n, alpha, beta);
   NC_LAUNCH_CHECK();
   return 0;
 }

@@ -10,7 +10,8 @@ namespace nc {
 // ---- GEMM epilogues
 enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4,
        EPI_F32_ACC = 5 /* internal to the GEMM: EPI_F32 with beta = 1 */,
-       EPI_CE = 6 /* logits: bf16 store + per-row softmax partials + target logit (bf16 path) */ };
+       EPI_CE = 6 /* logits: bf16 store + per-row softmax partials + target logit (bf16 path) */,
+       EPI_AXPBY = 7 /* c_lp = alpha * aux + beta * acc, aux and c_lp in the element type */ };
 
 struct EpiArgs {
   float* c32 = nullptr;  // EPI_F32 (beta selects store / accumulate), EPI_RESID
@@ -29,6 +30,8 @@ struct EpiArgs {
   float* part = nullptr;
   float* tlog = nullptr;
   int nseg = 0;
+  // EPI_AXPBY: the two coefficients (aux is read at the output's position)
+  float alpha = 0.f, beta_f = 1.f;
 };
 
 struct GemmCall {
@@ -44,6 +47,12 @@ struct GemmCall {
   int dtype = 0;
   float* splitk_ws = nullptr;  // fp32 partials for split-K (EPI_F32 only); may be null
   uint64_t splitk_bytes = 0;   // its size: a split that does not fit is not used
+  // Batched products (EPI_F32 without accumulation, EPI_LP, EPI_AXPBY; no
+  // split-K): matrix b uses A + b * a_bstride and B + b * b_bstride
+  // (elements) and writes rows [b * M, (b + 1) * M) of the output (and reads
+  // the same rows of aux), so consecutive outputs are M rows apart.
+  int batch = 1;
+  long a_bstride = 0, b_bstride = 0;
 };
 
 int launch_gemm(const GemmCall& g, hipStream_t s);
@@ -115,9 +124,6 @@ int launch_muon_momentum(const float* g, float* buf, float* U, size_t n, const f
                          double* partials, int nblk, hipStream_t s);
 // X = U * inv_norm in the wide orientation (U^T when rows > cols), element type dtype
 int launch_ns_init(const float* U, int rows, int cols, const float* inv_norm, void* X, int dtype, hipStream_t s);
-// out = alpha x + beta y (x, out: element type dtype; y: fp32)
-int launch_axpby(void* out, const void* x, const float* y, size_t n, float alpha, float beta, int dtype,
-                 hipStream_t s);
 // w -= lr (adj O + wd w), O = X (or X^T for a tall matrix); param = w
 int launch_muon_apply(float* w, void* param, const void* X, int rows, int cols, float lr, float adj, float wd,
                       int dtype, hipStream_t s);

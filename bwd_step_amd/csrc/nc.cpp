@@ -827,51 +827,67 @@ int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb, int b_
 namespace {
 
 constexpr int kNormBlocks = 1024;
+// Most Muon matrices that share one batched Newton-Schulz launch (bounds the
+// workspace: the depth-20 model has 40 matrices of 1280 x 5120).
+constexpr int kMuonBatch = 40;
 
 bool optim_is_adamw(const Desc& t) { return t.name == "E" || t.name == "W_lm"; }
+
+// Muon matrices of one wide-orientation shape [r, cc] (r <= cc), in layout order.
+struct MuonGroup {
+  int r = 0, cc = 0;
+  std::vector<int> members;  // indices into the layout
+};
 
 // State (fp32 elements): masters [nparams], then per tensor in layout order
 // its AdamW moments (2 x size) or its Muon momentum (1 x size).
 struct OptimPlan {
   std::vector<uint64_t> aux;  // per tensor: element offset of its first state array
+  std::vector<MuonGroup> groups;
   uint64_t state_elems = 0;
-  // workspace (bytes)
-  size_t partials = 0, scalars = 0, U = 0, X = 0, A = 0, AA = 0, B2 = 0, BX = 0, splitk = 0, total = 0;
-  uint64_t splitk_bytes = 0;
+  // workspace (bytes): norm partials, scalars, one fp32 update U, and per
+  // batch of up to kMuonBatch matrices the iterates X0 / X1 [r, cc], the Gram
+  // matrices A = X X^T and B = b A + c A A [r, r] (element type)
+  size_t partials = 0, scalars = 0, U = 0, X0 = 0, X1 = 0, A = 0, B2 = 0, total = 0;
 };
 
 OptimPlan optim_plan(const nc_ctx* x) {
   OptimPlan p;
   uint64_t o = x->nparams;
-  size_t max_mn = 0, max_rr = 0;
-  uint64_t sk = 0;
-  const int dt = x->cfg.dtype;
-  for (const Desc& t : x->layout) {
+  size_t max_mn = 0, max_x = 0, max_a = 0;
+  for (size_t ti = 0; ti < x->layout.size(); ++ti) {
+    const Desc& t = x->layout[ti];
     const uint64_t n = (uint64_t)t.rows * t.cols;
     p.aux.push_back(o);
     o += optim_is_adamw(t) ? 2 * n : n;
-    if (!optim_is_adamw(t)) {
-      const int r = std::min(t.rows, t.cols), c = std::max(t.rows, t.cols);
-      max_mn = std::max(max_mn, (size_t)n);
-      max_rr = std::max(max_rr, (size_t)r * r);
-      sk = std::max(sk, gemm_ws_bytes(r, r, r, dt));
-      sk = std::max(sk, gemm_ws_bytes(r, c, r, dt));
+    if (optim_is_adamw(t)) continue;
+    const int r = std::min(t.rows, t.cols), cc = std::max(t.rows, t.cols);
+    max_mn = std::max(max_mn, (size_t)n);
+    MuonGroup* g = nullptr;
+    for (MuonGroup& q : p.groups)
+      if (q.r == r && q.cc == cc) g = &q;
+    if (!g) {
+      p.groups.push_back(MuonGroup{r, cc, {}});
+      g = &p.groups.back();
     }
+    g->members.push_back((int)ti);
+  }
+  for (const MuonGroup& g : p.groups) {
+    const size_t nb = std::min<size_t>(g.members.size(), kMuonBatch);
+    max_x = std::max(max_x, nb * g.r * g.cc);
+    max_a = std::max(max_a, nb * g.r * g.r);
   }
   p.state_elems = o;
-  const size_t es = dt == NC_BF16 ? 2 : 4;
+  const size_t es = x->cfg.dtype == NC_BF16 ? 2 : 4;
   size_t w = 0;
   auto take = [&](size_t b) { size_t r = w; w += al(b); return r; };
   p.partials = take(kNormBlocks * sizeof(double));
   p.scalars = take(4 * sizeof(float));  // grad norm, clip factor, 1/|U|_F
   p.U = take(max_mn * 4);
-  p.X = take(max_mn * es);
-  p.A = take(max_rr * es);
-  p.AA = take(max_rr * 4);
-  p.B2 = take(max_rr * es);
-  p.BX = take(max_mn * 4);
-  p.splitk = take(sk);
-  p.splitk_bytes = sk;
+  p.X0 = take(max_x * es);
+  p.X1 = take(max_x * es);
+  p.A = take(max_a * es);
+  p.B2 = take(max_a * es);
   p.total = w;
   return p;
 }
@@ -940,50 +956,66 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
   const float bc2 = (float)(1.0 - std::pow((double)cfg->beta2, t));
   const float lr_a = (float)(cfg->lr_adamw * mult), lr_m = (float)(cfg->lr_muon * mult);
   const float a = 3.4445f, b = -4.7750f, c = 2.0315f;  // quintic Newton-Schulz coefficients
+  // AdamW tensors
   for (size_t ti = 0; ti < ctx->layout.size(); ++ti) {
     const Desc& d = ctx->layout[ti];
+    if (!optim_is_adamw(d)) continue;
     const size_t n = (size_t)d.rows * d.cols;
-    float* w = st + d.offset;
-    const float* g = grads + d.offset;
-    char* prm = (char*)params + d.offset * es;
-    if (optim_is_adamw(d)) {
-      float* m1 = st + P.aux[ti];
-      TRY(launch_adamw(w, m1, m1 + n, g, prm, n, sc + 1, lr_a, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay,
-                       bc1, bc2, dt, s));
-      continue;
+    float* m1 = st + P.aux[ti];
+    TRY(launch_adamw(st + d.offset, m1, m1 + n, grads + d.offset, (char*)params + d.offset * es, n, sc + 1, lr_a,
+                     cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, bc1, bc2, dt, s));
+  }
+  // Muon: per batch of same-shape matrices, the momentum and the normalised
+  // update of each member into its slot of X0 (wide orientation [r, cc]),
+  // then ns_steps batched iterations X <- a X + (b A + c A A) X with
+  // A = X X^T, as three products per iteration whose epilogues form the
+  // combinations, then each member's weight update from its slot.
+  float* U = (float*)(W + P.U);
+  for (const MuonGroup& grp : P.groups) {
+    const int r = grp.r, cc = grp.cc;
+    const long xs = (long)r * cc, as = (long)r * r;  // elements per member
+    for (size_t b0 = 0; b0 < grp.members.size(); b0 += kMuonBatch) {
+      const int nb = (int)std::min<size_t>(kMuonBatch, grp.members.size() - b0);
+      char* X = W + P.X0;
+      char* Xn = W + P.X1;
+      char* A = W + P.A;
+      char* B2 = W + P.B2;
+      for (int k = 0; k < nb; ++k) {
+        const int ti = grp.members[b0 + k];
+        const Desc& d = ctx->layout[ti];
+        const size_t n = (size_t)d.rows * d.cols;
+        TRY(launch_muon_momentum(grads + d.offset, st + P.aux[ti], U, n, sc + 1, cfg->momentum, partials,
+                                 kNormBlocks, s));
+        TRY(launch_norm_finish(partials, kNormBlocks, 0.f, 1, nullptr, sc + 2, s));
+        TRY(launch_ns_init(U, d.rows, d.cols, sc + 2, X + k * xs * es, dt, s));
+      }
+      for (int it = 0; it < cfg->ns_steps; ++it) {
+        // A = X X^T
+        GemmCall g1 = mk(X, cc, true, X, cc, true, r, r, cc, dt);
+        g1.batch = nb; g1.a_bstride = xs; g1.b_bstride = xs;
+        g1.epi = EPI_LP; g1.e.c_lp = A; g1.e.ld_lp = r;
+        TRY(launch_gemm(g1, s));
+        // B = b A + c A A (A is symmetric: its rows are its columns)
+        GemmCall g2 = mk(A, r, true, A, r, true, r, r, r, dt);
+        g2.batch = nb; g2.a_bstride = as; g2.b_bstride = as;
+        g2.epi = EPI_AXPBY; g2.e.c_lp = B2; g2.e.ld_lp = r; g2.e.aux = A; g2.e.ld_aux = r;
+        g2.e.alpha = b; g2.e.beta_f = c;
+        TRY(launch_gemm(g2, s));
+        // X' = a X + B X
+        GemmCall g3 = mk(B2, r, true, X, cc, false, r, cc, r, dt);
+        g3.batch = nb; g3.a_bstride = as; g3.b_bstride = xs;
+        g3.epi = EPI_AXPBY; g3.e.c_lp = Xn; g3.e.ld_lp = cc; g3.e.aux = X; g3.e.ld_aux = cc;
+        g3.e.alpha = a; g3.e.beta_f = 1.f;
+        TRY(launch_gemm(g3, s));
+        std::swap(X, Xn);
+      }
+      for (int k = 0; k < nb; ++k) {
+        const Desc& d = ctx->layout[grp.members[b0 + k]];
+        const float adj = (float)std::sqrt(std::max(1.0, (double)d.rows / d.cols));
+        TRY(launch_muon_apply(st + d.offset, (char*)params + d.offset * es, X + k * xs * es, d.rows, d.cols, lr_m,
+                              adj, cfg->weight_decay, dt, s));
+      }
     }
-    // Muon: momentum, then Newton-Schulz on the wide orientation X [r x cc]
-    float* U = (float*)(W + P.U);
-    TRY(launch_muon_momentum(g, st + P.aux[ti], U, n, sc + 1, cfg->momentum, partials, kNormBlocks, s));
-    TRY(launch_norm_finish(partials, kNormBlocks, 0.f, 1, nullptr, sc + 2, s));
-    void* X = W + P.X;
-    TRY(launch_ns_init(U, d.rows, d.cols, sc + 2, X, dt, s));
-    const int r = std::min(d.rows, d.cols), cc = std::max(d.rows, d.cols);
-    void* A = W + P.A;
-    float* AA = (float*)(W + P.AA);
-    void* B2 = W + P.B2;
-    float* BX = (float*)(W + P.BX);
-    for (int k = 0; k < cfg->ns_steps; ++k) {
-      // A = X X^T
-      GemmCall g1 = mk(X, cc, true, X, cc, true, r, r, cc, dt);
-      g1.epi = EPI_LP; g1.e.c_lp = A; g1.e.ld_lp = r;
-      TRY(launch_gemm(g1, s));
-      // AA = A A (A is symmetric, so its rows are also its columns)
-      GemmCall g2 = mk(A, r, true, A, r, true, r, r, r, dt);
-      g2.epi = EPI_F32; g2.e.c32 = AA; g2.e.ldc = r;
-      g2.splitk_ws = (float*)(W + P.splitk); g2.splitk_bytes = P.splitk_bytes;
-      TRY(launch_gemm(g2, s));
-      // B2 = b A + c A A
-      TRY(launch_axpby(B2, A, AA, (size_t)r * r, b, c, dt, s));
-      // BX = B2 X, then X = a X + BX
-      GemmCall g3 = mk(B2, r, true, X, cc, false, r, cc, r, dt);
-      g3.epi = EPI_F32; g3.e.c32 = BX; g3.e.ldc = cc;
-      g3.splitk_ws = (float*)(W + P.splitk); g3.splitk_bytes = P.splitk_bytes;
-      TRY(launch_gemm(g3, s));
-      TRY(launch_axpby(X, X, BX, (size_t)r * cc, a, 1.f, dt, s));
-    }
-    const float adj = (float)std::sqrt(std::max(1.0, (double)d.rows / d.cols));
-    TRY(launch_muon_apply(w, prm, X, d.rows, d.cols, lr_m, adj, cfg->weight_decay, dt, s));
   }
   return 0;
 }
