@@ -112,21 +112,43 @@ int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, l
 int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s);
 
 // ---- optimizer (k_optim.hip)
-// deterministic sum of squares: nblk fp64 partials, then one finishing block
+// Vectors are fp32 with 16-byte aligned starts and lengths that are multiples
+// of 4 (every tensor of the layout is a multiple of 64 elements).
+// partials[b] = sum of squares of block b's fixed chunk of x (nblk blocks)
 int launch_sumsq(const float* x, size_t n, double* partials, int nblk, hipStream_t s);
-// mode 0: out0 = sqrt(sum) (may be null), out1 = min(1, clip / (sqrt(sum) + 1e-6));
-// mode 1: out1 = 1 / (sqrt(sum) + 1e-7)
-int launch_norm_finish(const double* partials, int nblk, float clip, int mode, float* out0, float* out1,
-                       hipStream_t s);
+// Per group g of nblk partials (ngroups groups): mode 0: out0 = sqrt(sum)
+// (may be null), out1 = min(1, clip / (sqrt(sum) + 1e-6)); mode 1:
+// out1[g] = 1 / (sqrt(sum) + 1e-7)
+int launch_norm_finish(const double* partials, int nblk, int ngroups, float clip, int mode, float* out0,
+                       float* out1, hipStream_t s);
 int launch_adamw(float* w, float* m, float* v, const float* g, void* param, size_t n, const float* clip_scale,
                  float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, int dtype, hipStream_t s);
-int launch_muon_momentum(const float* g, float* buf, float* U, size_t n, const float* clip_scale, float mu,
-                         double* partials, int nblk, hipStream_t s);
-// X = U * inv_norm in the wide orientation (U^T when rows > cols), element type dtype
-int launch_ns_init(const float* U, int rows, int cols, const float* inv_norm, void* X, int dtype, hipStream_t s);
-// w -= lr (adj O + wd w), O = X (or X^T for a tall matrix); param = w
-int launch_muon_apply(float* w, void* param, const void* X, int rows, int cols, float lr, float adj, float wd,
-                      int dtype, hipStream_t s);
+
+// Up to kMuonBatch Muon matrices sharing one wide orientation [r, cc]
+// (r <= cc), processed together.  A member is either [r, cc] or, when
+// tall, [cc, r] (then its Newton-Schulz iterate is the transpose).
+constexpr int kMuonBatch = 40;
+constexpr int kMuonBlocks = 64;  // reduction blocks per member
+struct MuonBatch {
+  int n = 0;
+  int r = 0, cc = 0;
+  int tall[kMuonBatch];
+  float adj[kMuonBatch];      // sqrt(max(1, rows / cols))
+  uint64_t off[kMuonBatch];   // element offset in the flat layout (grads, params, masters)
+  uint64_t buf[kMuonBatch];   // element offset of the momentum in the state
+};
+// Per member: buf = mu buf + g * clip; partials of |g * clip + mu buf|^2
+// (kMuonBlocks per member, member-major)
+int launch_muon_momentum(const float* grads, float* state, const MuonBatch& mb, const float* clip_scale, float mu,
+                         double* partials, hipStream_t s);
+// Per member: X_k = (g * clip + mu buf) * inv[k] in the wide orientation
+// (element type dtype, members r * cc apart)
+int launch_ns_init(const float* grads, const float* state, const MuonBatch& mb, const float* clip_scale, float mu,
+                   const float* inv, void* X, int dtype, hipStream_t s);
+// Per member: w -= lr (adj O + wd w) with O = X_k in the member's own
+// orientation; param = w
+int launch_muon_apply(float* state, void* params, const void* X, const MuonBatch& mb, float lr, float wd, int dtype,
+                      hipStream_t s);
 int launch_widen(float* out, const void* in, size_t n, int dtype, hipStream_t s);
 int launch_zero(float* p, size_t n, hipStream_t s);
 

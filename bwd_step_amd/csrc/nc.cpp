@@ -827,9 +827,9 @@ int nc_gemm(const void* A, int lda, int a_kmajor, const void* B, int ldb, int b_
 namespace {
 
 constexpr int kNormBlocks = 1024;
-// Most Muon matrices that share one batched Newton-Schulz launch (bounds the
-// workspace: the depth-20 model has 40 matrices of 1280 x 5120).
-constexpr int kMuonBatch = 40;
+// At most kMuonBatch Muon matrices (kernels.h) share one batched launch,
+// which bounds the workspace: the depth-20 model has 40 matrices of
+// 1280 x 5120.
 
 bool optim_is_adamw(const Desc& t) { return t.name == "E" || t.name == "W_lm"; }
 
@@ -845,16 +845,16 @@ struct OptimPlan {
   std::vector<uint64_t> aux;  // per tensor: element offset of its first state array
   std::vector<MuonGroup> groups;
   uint64_t state_elems = 0;
-  // workspace (bytes): norm partials, scalars, one fp32 update U, and per
-  // batch of up to kMuonBatch matrices the iterates X0 / X1 [r, cc], the Gram
-  // matrices A = X X^T and B = b A + c A A [r, r] (element type)
-  size_t partials = 0, scalars = 0, U = 0, X0 = 0, X1 = 0, A = 0, B2 = 0, total = 0;
+  // workspace (bytes): norm partials, scalars, and per batch of up to
+  // kMuonBatch matrices the iterates X0 / X1 [r, cc], the Gram matrices
+  // A = X X^T and B = b A + c A A [r, r] (element type)
+  size_t partials = 0, scalars = 0, X0 = 0, X1 = 0, A = 0, B2 = 0, total = 0;
 };
 
 OptimPlan optim_plan(const nc_ctx* x) {
   OptimPlan p;
   uint64_t o = x->nparams;
-  size_t max_mn = 0, max_x = 0, max_a = 0;
+  size_t max_x = 0, max_a = 0;
   for (size_t ti = 0; ti < x->layout.size(); ++ti) {
     const Desc& t = x->layout[ti];
     const uint64_t n = (uint64_t)t.rows * t.cols;
@@ -862,7 +862,6 @@ OptimPlan optim_plan(const nc_ctx* x) {
     o += optim_is_adamw(t) ? 2 * n : n;
     if (optim_is_adamw(t)) continue;
     const int r = std::min(t.rows, t.cols), cc = std::max(t.rows, t.cols);
-    max_mn = std::max(max_mn, (size_t)n);
     MuonGroup* g = nullptr;
     for (MuonGroup& q : p.groups)
       if (q.r == r && q.cc == cc) g = &q;
@@ -881,9 +880,8 @@ OptimPlan optim_plan(const nc_ctx* x) {
   const size_t es = x->cfg.dtype == NC_BF16 ? 2 : 4;
   size_t w = 0;
   auto take = [&](size_t b) { size_t r = w; w += al(b); return r; };
-  p.partials = take(kNormBlocks * sizeof(double));
-  p.scalars = take(4 * sizeof(float));  // grad norm, clip factor, 1/|U|_F
-  p.U = take(max_mn * 4);
+  p.partials = take(std::max(kNormBlocks, kMuonBatch * kMuonBlocks) * sizeof(double));
+  p.scalars = take((4 + kMuonBatch) * sizeof(float));  // grad norm, clip factor, 1/|U|_F per member
   p.X0 = take(max_x * es);
   p.X1 = take(max_x * es);
   p.A = take(max_a * es);
@@ -933,6 +931,8 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
                   void* workspace, uint64_t ws_bytes, float* grad_norm) {
   if (!ctx || !cfg || !grads || !params || !state || !workspace) return NC_ERR_NULL;
   if (step < 0 || !optim_config_ok(*cfg)) return NC_ERR_ARG;
+  auto misaligned = [](const void* q) { return ((uintptr_t)q & 15) != 0; };
+  if (misaligned(grads) || misaligned(params) || misaligned(state) || misaligned(workspace)) return NC_ERR_ARG;
   const OptimPlan P = optim_plan(ctx);
   if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
   hipStream_t s = ctx->stream;
@@ -946,7 +946,7 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
 
   // global gradient norm and clip factor
   TRY(launch_sumsq(grads, ctx->nparams, partials, kNormBlocks, s));
-  TRY(launch_norm_finish(partials, kNormBlocks, cfg->clip, 0, sc, sc + 1, s));
+  TRY(launch_norm_finish(partials, kNormBlocks, 1, cfg->clip, 0, sc, sc + 1, s));
   if (grad_norm) {
     if (hipMemcpyAsync(grad_norm, sc, sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess) return NC_ERR_HIP;
   }
@@ -965,30 +965,36 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
     TRY(launch_adamw(st + d.offset, m1, m1 + n, grads + d.offset, (char*)params + d.offset * es, n, sc + 1, lr_a,
                      cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay, bc1, bc2, dt, s));
   }
-  // Muon: per batch of same-shape matrices, the momentum and the normalised
-  // update of each member into its slot of X0 (wide orientation [r, cc]),
-  // then ns_steps batched iterations X <- a X + (b A + c A A) X with
-  // A = X X^T, as three products per iteration whose epilogues form the
-  // combinations, then each member's weight update from its slot.
-  float* U = (float*)(W + P.U);
+  // Muon, per batch of same-shape matrices: the momentum (and the norms of
+  // the Nesterov updates), each update normalised into its slot of X0 (wide
+  // orientation [r, cc]), ns_steps batched iterations X <- a X + (b A +
+  // c A A) X with A = X X^T as three products whose epilogues form the
+  // combinations, then every member's weight update from its slot.
+  float* inv = sc + 4;
   for (const MuonGroup& grp : P.groups) {
     const int r = grp.r, cc = grp.cc;
     const long xs = (long)r * cc, as = (long)r * r;  // elements per member
     for (size_t b0 = 0; b0 < grp.members.size(); b0 += kMuonBatch) {
-      const int nb = (int)std::min<size_t>(kMuonBatch, grp.members.size() - b0);
+      MuonBatch mb;
+      mb.n = (int)std::min<size_t>(kMuonBatch, grp.members.size() - b0);
+      mb.r = r;
+      mb.cc = cc;
+      for (int k = 0; k < mb.n; ++k) {
+        const int ti = grp.members[b0 + k];
+        const Desc& d = ctx->layout[ti];
+        mb.tall[k] = d.rows > d.cols;
+        mb.adj[k] = (float)std::sqrt(std::max(1.0, (double)d.rows / d.cols));
+        mb.off[k] = d.offset;
+        mb.buf[k] = P.aux[ti];
+      }
+      const int nb = mb.n;
       char* X = W + P.X0;
       char* Xn = W + P.X1;
       char* A = W + P.A;
       char* B2 = W + P.B2;
-      for (int k = 0; k < nb; ++k) {
-        const int ti = grp.members[b0 + k];
-        const Desc& d = ctx->layout[ti];
-        const size_t n = (size_t)d.rows * d.cols;
-        TRY(launch_muon_momentum(grads + d.offset, st + P.aux[ti], U, n, sc + 1, cfg->momentum, partials,
-                                 kNormBlocks, s));
-        TRY(launch_norm_finish(partials, kNormBlocks, 0.f, 1, nullptr, sc + 2, s));
-        TRY(launch_ns_init(U, d.rows, d.cols, sc + 2, X + k * xs * es, dt, s));
-      }
+      TRY(launch_muon_momentum(grads, st, mb, sc + 1, cfg->momentum, partials, s));
+      TRY(launch_norm_finish(partials, kMuonBlocks, nb, 0.f, 1, nullptr, inv, s));
+      TRY(launch_ns_init(grads, st, mb, sc + 1, cfg->momentum, inv, X, dt, s));
       for (int it = 0; it < cfg->ns_steps; ++it) {
         // A = X X^T
         GemmCall g1 = mk(X, cc, true, X, cc, true, r, r, cc, dt);
@@ -1009,12 +1015,7 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
         TRY(launch_gemm(g3, s));
         std::swap(X, Xn);
       }
-      for (int k = 0; k < nb; ++k) {
-        const Desc& d = ctx->layout[grp.members[b0 + k]];
-        const float adj = (float)std::sqrt(std::max(1.0, (double)d.rows / d.cols));
-        TRY(launch_muon_apply(st + d.offset, (char*)params + d.offset * es, X + k * xs * es, d.rows, d.cols, lr_m,
-                              adj, cfg->weight_decay, dt, s));
-      }
+      TRY(launch_muon_apply(st, params, X, mb, lr_m, cfg->weight_decay, dt, s));
     }
   }
   return 0;

@@ -231,10 +231,12 @@ int nc_optim_init(nc_ctx* ctx, const void* params, void* state);
 /*
  * One optimizer step `step` (0-based) from the fp32 gradients `grads` (flat
  * layout): updates the state and rewrites params.  grad_norm (device fp32
- * scalar, may be NULL) receives |g|_2 before clipping.  Enqueued on the
- * context's stream; nothing is read back to the host.
- * Errors: NC_ERR_NULL, NC_ERR_ARG (a hyperparameter outside its range, or
- * step < 0), NC_ERR_WORKSPACE (ws_bytes < nc_optim_workspace_bytes).
+ * scalar, may be NULL) receives |g|_2 before clipping.  grads, params,
+ * state and workspace are device buffers with 16-byte aligned starts.
+ * Enqueued on the context's stream; nothing is read back to the host.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (a hyperparameter outside its range,
+ * step < 0, or a misaligned buffer), NC_ERR_WORKSPACE (ws_bytes <
+ * nc_optim_workspace_bytes).
  */
 int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float* grads, void* params,
                   void* state, void* workspace, uint64_t ws_bytes, float* grad_norm);

@@ -176,6 +176,10 @@ def test_optim_sizes_and_host_errors():
         assert step(**bad) == 8, bad
     for i in (0, 1, 3, 4, 5, 6):
         assert step(null=i) == 2, i
+    c = _nc.NcOptimConfig(**good)
+    odd = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+    assert lib().nc_optim_step(h, ctypes.byref(c), 0, odd, fake, fake, fake, need, None) == 8
+    assert lib().nc_optim_step(h, ctypes.byref(c), 0, fake, fake, odd, fake, need, None) == 8
     assert lib().nc_optim_init(h, None, fake) == 2
     assert lib().nc_optim_init(h, fake, None) == 2
     lib().nc_destroy(h)
