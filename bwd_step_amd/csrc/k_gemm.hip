@@ -38,6 +38,7 @@ struct GemmParams {
   int tiles_m, tiles_n;
   int group;  // tile-rows per group of the tile walk
   int batch;  // independent products (1 unless batched)
+  int sym;    // symmetric square result: only tiles tm <= tn, each also stored transposed
   long a_bs, b_bs;  // bytes between consecutive batch members' A and B
   EpiArgs e;
 };
@@ -233,7 +234,9 @@ __device__ __forceinline__ void wait_first_slice_and_sync() {
 
 // KTAIL: a k-contiguous operand has K % 32 != 0, so the last slice of the
 // last K split is cut per lane (a k-strided operand ends with its buffer).
-template <bool AK, bool BKM, int EPI, bool KTAIL>
+// BAT: batched / symmetric products (p.batch, p.sym); without it those fields
+// are ignored and the hot-path instantiations carry none of their logic.
+template <bool AK, bool BKM, int EPI, bool KTAIL, bool BAT>
 __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -256,26 +259,44 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
   // walked in column groups of 8 tile-rows so that neighbours share A rows and
   // B columns in the XCD's L2.
   const int G = gridDim.x;
-  const int ntiles = p.tiles_m * p.tiles_n;
+  const int ntiles = (BAT && p.sym) ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int per_batch = ntiles * p.splits;
-  const int nitems = per_batch * p.batch;
+  const int nitems = BAT ? per_batch * p.batch : per_batch;
   const int wfirst = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   if (wfirst >= nitems) return;
 
   struct Item {
     int m0, n0, kbeg, kend, nk, split, b;
+    bool mir;  // off-diagonal tile of a symmetric result: also stored transposed
   };
   auto item = [&](int i) {
     Item r;
-    r.b = i / per_batch;
-    i -= r.b * per_batch;
+    if constexpr (BAT) {
+      r.b = i / per_batch;
+      i -= r.b * per_batch;
+    } else {
+      r.b = 0;
+    }
     r.split = i / ntiles;
-    const int t = i - r.split * ntiles;
-    const int group_span = p.group * p.tiles_n;
-    const int first_m = (t / group_span) * p.group;
-    const int gsize = min(p.tiles_m - first_m, p.group);
-    r.m0 = (first_m + (t % group_span) % gsize) * BM;
-    r.n0 = ((t % group_span) / gsize) * BN;
+    int t = i - r.split * ntiles;
+    if (BAT && p.sym) {
+      // upper triangle, row by row: tile-row tm holds tiles_m - tm tiles
+      int tm = 0;
+      while (t >= p.tiles_m - tm) {
+        t -= p.tiles_m - tm;
+        ++tm;
+      }
+      r.m0 = tm * BM;
+      r.n0 = (tm + t) * BN;
+      r.mir = t != 0;
+    } else {
+      const int group_span = p.group * p.tiles_n;
+      const int first_m = (t / group_span) * p.group;
+      const int gsize = min(p.tiles_m - first_m, p.group);
+      r.m0 = (first_m + (t % group_span) % gsize) * BM;
+      r.n0 = ((t % group_span) / gsize) * BN;
+      r.mir = false;
+    }
     r.kbeg = r.split * p.kchunk;
     r.kend = min(p.K, r.kbeg + p.kchunk);
     r.nk = max((r.kend - r.kbeg + kBK - 1) / kBK, 0);
@@ -292,8 +313,12 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     const long sh = live ? (long)k0 * kstep : 0;
     return make_rsrc((const char*)base + sh, live ? bytes - (uint32_t)sh : 0u);
   };
-  auto a_base = [&](const Item& it_) { return (const void*)((const char*)p.A + it_.b * p.a_bs); };
-  auto b_base = [&](const Item& it_) { return (const void*)((const char*)p.B + it_.b * p.b_bs); };
+  auto a_base = [&](const Item& it_) {
+    return BAT ? (const void*)((const char*)p.A + it_.b * p.a_bs) : p.A;
+  };
+  auto b_base = [&](const Item& it_) {
+    return BAT ? (const void*)((const char*)p.B + it_.b * p.b_bs) : p.B;
+  };
   // per-lane offsets of this wavefront's four blocks of A and B for an item
   auto item_voff = [&](const Item& it_, uint32_t* va, uint32_t* vb) {
 #pragma unroll
@@ -381,6 +406,15 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     mfma_step(fa1, fb1);
   };
 
+  // Transposed copy of four outputs (i, j..j+3) of a symmetric result: C[j+e][i].
+  // The 32 lanes of a half-wavefront hold 32 consecutive i, so each of the
+  // four stores covers 64 contiguous bytes.
+  auto store_mirror = [&](long i, long j, long ib, f32x4 v) {
+    bf16* cb = (bf16*)p.e.c_lp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cb[(j + e + ib) * p.e.ld_lp + i] = from_f32<bf16>(v[e]);
+  };
+
   // Epilogue.  The MFMA computed C^T blocks (B fragment as the row operand), so
   // a lane holds output row m = lane & 31 of its block and, in register
   // group q = r / 4, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
@@ -393,10 +427,30 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const long j = ci.n0 + wn * TN + c * 32 + 8 * q + 4 * (lane >> 5);
-          if (i < p.M && j < p.N)
-            epi_apply4<EPI>(p.e, ci.split, i + (long)ci.b * p.M, j,
-                            f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2],
-                                  acc[a][c][4 * q + 3]});
+          if constexpr (BAT) {
+            // batch member b writes rows b M ..; a symmetric result also its mirror tile
+            const f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+            const long ib = (long)ci.b * p.M;
+            if (i < p.M && j < p.N) {
+              f32x4 o = v;
+              if constexpr (EPI == EPI_AXPBY) {
+                const f32x4 x = load4((const bf16*)p.e.aux + (i + ib) * p.e.ld_aux + j);
+                o = f32x4{fmaf(p.e.alpha, x.x, p.e.beta_f * v.x), fmaf(p.e.alpha, x.y, p.e.beta_f * v.y),
+                          fmaf(p.e.alpha, x.z, p.e.beta_f * v.z), fmaf(p.e.alpha, x.w, p.e.beta_f * v.w)};
+                store4((bf16*)p.e.c_lp + (i + ib) * p.e.ld_lp + j, o);
+              } else {
+                epi_apply4<EPI>(p.e, ci.split, i + ib, j, v);
+              }
+              if constexpr (EPI == EPI_LP || EPI == EPI_AXPBY) {
+                if (ci.mir) store_mirror(i, j, ib, o);
+              }
+            }
+          } else {
+            if (i < p.M && j < p.N)
+              epi_apply4<EPI>(p.e, ci.split, i, j,
+                              f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2],
+                                    acc[a][c][4 * q + 3]});
+          }
         }
         if constexpr (EPI == EPI_F32_ACC) __builtin_amdgcn_sched_barrier(0);
       }
@@ -626,12 +680,24 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ host dispatch
-template <int EPI, bool KTAIL>
+template <int EPI, bool KTAIL, bool BAT>
 static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
-  if (ak && bk) gemm_mfma_kernel<true, true, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
-  else if (ak) gemm_mfma_kernel<true, false, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
-  else if (bk) gemm_mfma_kernel<false, true, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
-  else gemm_mfma_kernel<false, false, EPI, KTAIL><<<grid, 256, 0, s>>>(p);
+  if (ak && bk) gemm_mfma_kernel<true, true, EPI, KTAIL, BAT><<<grid, 256, 0, s>>>(p);
+  else if (ak) gemm_mfma_kernel<true, false, EPI, KTAIL, BAT><<<grid, 256, 0, s>>>(p);
+  else if (bk) gemm_mfma_kernel<false, true, EPI, KTAIL, BAT><<<grid, 256, 0, s>>>(p);
+  else gemm_mfma_kernel<false, false, EPI, KTAIL, BAT><<<grid, 256, 0, s>>>(p);
+}
+template <int EPI, bool KTAIL>
+static int launch_mfma_b(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
+  if (p.batch == 1 && !p.sym) {
+    launch_mfma_k<EPI, KTAIL, false>(p, ak, bk, grid, s);
+    return 0;
+  }
+  if constexpr (EPI == EPI_LP || EPI == EPI_AXPBY || EPI == EPI_F32) {
+    launch_mfma_k<EPI, KTAIL, true>(p, ak, bk, grid, s);
+    return 0;
+  }
+  return NC_ERR_UNSUPPORTED;
 }
 // A k-contiguous operand with K % 32 != 0 needs the per-lane cut of the last
 // slice; the model's layers never do (their widths are multiples of 64), so
@@ -640,14 +706,8 @@ static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, dim3 grid, hipS
 template <int EPI>
 static int launch_mfma(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
   const bool ktail = (ak || bk) && (p.K % kBK) != 0;
-  if (!ktail) {
-    launch_mfma_k<EPI, false>(p, ak, bk, grid, s);
-    return 0;
-  }
-  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC || EPI == EPI_AXPBY) {
-    launch_mfma_k<EPI, true>(p, ak, bk, grid, s);
-    return 0;
-  }
+  if (!ktail) return launch_mfma_b<EPI, false>(p, ak, bk, grid, s);
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F32_ACC || EPI == EPI_AXPBY) return launch_mfma_b<EPI, true>(p, ak, bk, grid, s);
   return NC_ERR_UNSUPPORTED;
 }
 
@@ -745,6 +805,9 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   if (batched && !(g.epi == EPI_LP || g.epi == EPI_AXPBY || (g.epi == EPI_F32 && !g.e.beta)))
     return NC_ERR_UNSUPPORTED;
   p.batch = g.batch;
+  // symmetric results: MFMA path only (the fp32 path computes every tile)
+  if (g.sym && (g.M != g.N || !(g.epi == EPI_LP || g.epi == EPI_AXPBY))) return NC_ERR_UNSUPPORTED;
+  p.sym = g.sym && g.dtype == 0;
   p.a_bs = g.a_bstride * (g.dtype == 0 ? 2 : 4);
   p.b_bs = g.b_bstride * (g.dtype == 0 ? 2 : 4);
   int splits = 1;
@@ -771,7 +834,8 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, g.batch, splits);
   if (g.dtype == 0) {
     // persistent: one workgroup per compute unit (each holds 128 KB of LDS)
-    const long items = (long)p.tiles_m * p.tiles_n * splits * g.batch;
+    const long tiles = p.sym ? (long)p.tiles_m * (p.tiles_m + 1) / 2 : (long)p.tiles_m * p.tiles_n;
+    const long items = tiles * splits * g.batch;
     grid = dim3((unsigned)std::min<long>(items, num_cus()), 1, 1);
   }
   // K == 0 runs the kernels with an empty k-loop: the epilogue sees zeros.

@@ -53,6 +53,10 @@ struct GemmCall {
   // the same rows of aux), so consecutive outputs are M rows apart.
   int batch = 1;
   long a_bstride = 0, b_bstride = 0;
+  // The result is symmetric (M == N; EPI_LP, or EPI_AXPBY with a symmetric
+  // aux): only the tiles on and above the diagonal are computed, each
+  // off-diagonal one stored twice (transposed).
+  bool sym = false;
 };
 
 int launch_gemm(const GemmCall& g, hipStream_t s);

@@ -999,13 +999,13 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
         // A = X X^T
         GemmCall g1 = mk(X, cc, true, X, cc, true, r, r, cc, dt);
         g1.batch = nb; g1.a_bstride = xs; g1.b_bstride = xs;
-        g1.epi = EPI_LP; g1.e.c_lp = A; g1.e.ld_lp = r;
+        g1.epi = EPI_LP; g1.e.c_lp = A; g1.e.ld_lp = r; g1.sym = true;
         TRY(launch_gemm(g1, s));
-        // B = b A + c A A (A is symmetric: its rows are its columns)
+        // B = b A + c A A (A is symmetric: its rows are its columns; so is B)
         GemmCall g2 = mk(A, r, true, A, r, true, r, r, r, dt);
         g2.batch = nb; g2.a_bstride = as; g2.b_bstride = as;
         g2.epi = EPI_AXPBY; g2.e.c_lp = B2; g2.e.ld_lp = r; g2.e.aux = A; g2.e.ld_aux = r;
-        g2.e.alpha = b; g2.e.beta_f = c;
+        g2.e.alpha = b; g2.e.beta_f = c; g2.sym = true;
         TRY(launch_gemm(g2, s));
         // X' = a X + B X
         GemmCall g3 = mk(B2, r, true, X, cc, false, r, cc, r, dt);
