@@ -14,7 +14,11 @@ Design; Pretraining), per sequence b with positions t = 0..T-1:
         x += concat_h(o) W_o^T
         m = rho(x); u = m W_1^T; g = max(u, 0)^2; x += g W_2^T
     z = rho(x); l = z W_lm^T
-    loss = mean_n [logsumexp(l_n) - l_{n, y_n}]
+    loss = mean_n [logsumexp(l_n) - l_{n, y_n}]   over the positions with y_n >= 0
+
+A negative target leaves its position out of the loss (the loss mask of
+supervised fine-tuning, "nanochat explainer", Supervised Fine-Tuning); with
+every target >= 0 the mean runs over all B*T positions, as in pretraining.
 
 Parameters are a dict of float64 arrays named as in ``param_shapes``; every
 weight is [out, in].  W_qkv stacks the q rows, then the k rows, then the v
@@ -133,7 +137,7 @@ def forward_logits(cfg, params, tokens):
 
 
 def forward(cfg, params, tokens, targets):
-    """Mean next-token cross-entropy over all B*T positions (nats)."""
+    """Mean next-token cross-entropy over the positions with a target >= 0 (nats)."""
     _, logits, _ = _forward(cfg, params, tokens, keep=False)
     V = logits.shape[-1]
     loss, _ = ops.cross_entropy(logits.reshape(-1, V), np.asarray(targets).reshape(-1))

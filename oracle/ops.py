@@ -144,10 +144,14 @@ def relu2_bwd(dg, u):
 
 
 # --------------------------------------------------------------------------
-# Next-token softmax cross-entropy ("nanochat explainer", Pretraining).
-# loss = (1/N) sum_n [logsumexp(l_n) - l_{n, y_n}] in nats.
+# Next-token softmax cross-entropy ("nanochat explainer", Pretraining), with
+# the loss mask of supervised fine-tuning ("nanochat explainer", Supervised
+# Fine-Tuning: the same cross-entropy, counted only on the assistant's
+# tokens).  A negative target marks a position outside the loss:
+# loss = (1/|S|) sum_{n in S} [logsumexp(l_n) - l_{n, y_n}] in nats over the
+# set S of positions with a target >= 0; 0 when S is empty.
 # Pinned by: zero logits give ln V exactly; rows of dl sum to 0;
-# torch.nn.functional.cross_entropy; finite differences.
+# torch.nn.functional.cross_entropy (ignore_index=-1); finite differences.
 # --------------------------------------------------------------------------
 def logsumexp(l):
     mx = np.max(l, axis=-1, keepdims=True)
@@ -155,18 +159,26 @@ def logsumexp(l):
 
 
 def cross_entropy(logits, targets):
-    """logits [N, V] float64, targets [N] int. Returns (loss, lse)."""
+    """logits [N, V] float64, targets [N] int (< 0: not counted). Returns (loss, lse)."""
+    targets = np.asarray(targets)
     lse = logsumexp(logits)
-    picked = logits[np.arange(logits.shape[0]), targets]
-    return float(np.mean(lse - picked)), lse
+    rows = np.nonzero(targets >= 0)[0]
+    if rows.size == 0:
+        return 0.0, lse
+    picked = logits[rows, targets[rows]]
+    return float(np.sum(lse[rows] - picked) / rows.size), lse
 
 
 def cross_entropy_bwd(logits, targets, lse):
-    """dl = (softmax(l) - onehot(y)) / N."""
-    N = logits.shape[0]
-    g = np.exp(logits - lse[:, None])
-    g[np.arange(N), targets] -= 1.0
-    return g / N
+    """dl = (softmax(l) - onehot(y)) / |S| on counted rows, 0 on the others."""
+    targets = np.asarray(targets)
+    rows = np.nonzero(targets >= 0)[0]
+    g = np.zeros_like(logits)
+    if rows.size == 0:
+        return g
+    g[rows] = np.exp(logits[rows] - lse[rows, None])
+    g[rows, targets[rows]] -= 1.0
+    return g / rows.size
 
 
 # --------------------------------------------------------------------------

@@ -81,7 +81,7 @@ def test_grads_central_finite_differences(cfg, B):
 
 
 # ---------------------------------------------------------------- torch float64 autograd
-def torch_model_loss(cfg, P, tok, tgt):
+def torch_model_loss(cfg, P, tok, tgt, ignore_index=-100):
     """The same model written with torch library routines; autograd gives grads."""
     B, T = tok.shape
     H, hd = cfg.n_heads, cfg.head_dim
@@ -105,7 +105,7 @@ def torch_model_loss(cfg, P, tok, tgt):
         m = F.rms_norm(x, (d,), eps=cfg.eps)
         x = x + F.linear(F.relu(F.linear(m, P[f"layers.{l}.W_1"])).square(), P[f"layers.{l}.W_2"])
     logits = F.linear(F.rms_norm(x, (d,), eps=cfg.eps), P["W_lm"])
-    return F.cross_entropy(logits.reshape(-1, cfg.vocab), tgt.reshape(-1))
+    return F.cross_entropy(logits.reshape(-1, cfg.vocab), tgt.reshape(-1), ignore_index=ignore_index)
 
 
 def test_matches_torch_float64_autograd_tiny():
@@ -167,3 +167,78 @@ def test_embedding_grad_conservation_full_model():
     _, grads = oracle.forward_backward(TINY, params, tok, tgt)
     absent = np.setdiff1d(np.arange(TINY.vocab), tok)
     assert absent.size > 0 and np.all(grads["E"][absent] == 0.0)
+
+
+# ---------------------------------------------------------------- loss mask
+def masked_targets(tgt, seed, frac=0.5):
+    rng = np.random.default_rng(seed)
+    t = tgt.copy()
+    t[rng.random(t.shape) < frac] = -1
+    return t
+
+
+def test_masked_matches_torch_float64_autograd_and_fd():
+    params, tok, tgt = make(TINY, 2, seed=6)
+    tgt = masked_targets(tgt, 6)
+    tgt[1, :] = -1  # a whole sequence outside the loss
+    loss, grads = oracle.forward_backward(TINY, params, tok, tgt)
+    P2 = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in params.items()}
+    lt = torch_model_loss(TINY, P2, torch.from_numpy(tok).long(), torch.from_numpy(tgt).long(), ignore_index=-1)
+    lt.backward()
+    assert abs(loss - lt.item()) <= 1e-12 * abs(loss)
+    for k, v in grads.items():
+        ref = P2[k].grad.numpy()
+        err = np.linalg.norm(v - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert err <= 1e-10, (k, err)
+    # finite differences of the masked loss along one direction per tensor
+    p2, tok2, tgt2 = make(MICRO, 2, seed=8, std=0.2)
+    tgt2 = masked_targets(tgt2, 8)
+    l2, g2 = oracle.forward_backward(MICRO, p2, tok2, tgt2)
+    rng = np.random.default_rng(9)
+    h = 1e-5
+    for name, _ in oracle.param_shapes(MICRO):
+        d = rng.standard_normal(p2[name].shape)
+        d /= np.linalg.norm(d)
+        pp = dict(p2); pm = dict(p2)
+        pp[name] = p2[name] + h * d
+        pm[name] = p2[name] - h * d
+        fd = (oracle.forward(MICRO, pp, tok2, tgt2) - oracle.forward(MICRO, pm, tok2, tgt2)) / (2 * h)
+        an = float(np.sum(g2[name] * d))
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
+
+
+def test_mask_is_token_weighted_union_of_single_positions():
+    # loss(S) |S| = sum over t in S of loss({t}); the same for every gradient
+    params, tok, tgt = make(MICRO, 2, seed=10, std=0.2)
+    S = [(0, 1), (0, 6), (1, 0), (1, 7)]
+    ts = np.full_like(tgt, -1)
+    for b, t in S:
+        ts[b, t] = tgt[b, t]
+    loss, grads = oracle.forward_backward(MICRO, params, tok, ts)
+    acc_l, acc_g = 0.0, {k: 0.0 for k in grads}
+    for b, t in S:
+        t1 = np.full_like(tgt, -1)
+        t1[b, t] = tgt[b, t]
+        l1, g1 = oracle.forward_backward(MICRO, params, tok, t1)
+        acc_l += l1
+        for k in grads:
+            acc_g[k] = acc_g[k] + g1[k]
+    assert loss * len(S) == pytest.approx(acc_l, rel=1e-12)
+    for k in grads:
+        np.testing.assert_allclose(grads[k] * len(S), acc_g[k], rtol=1e-9, atol=1e-14)
+
+
+def test_masked_batch_is_weighted_mean_of_microbatches_and_empty_mask():
+    # gradient accumulation: the loss of a batch = token-weighted mean of its microbatches
+    params, tok, tgt = make(TINY, 3, seed=11)
+    tgt = masked_targets(tgt, 11, frac=0.3)
+    loss, grads = oracle.forward_backward(TINY, params, tok, tgt)
+    parts = [oracle.forward_backward(TINY, params, tok[i:i + 1], tgt[i:i + 1]) for i in range(3)]
+    n = [(tgt[i] >= 0).sum() for i in range(3)]
+    assert loss == pytest.approx(sum(p[0] * k for p, k in zip(parts, n)) / sum(n), rel=1e-12)
+    for key in grads:
+        np.testing.assert_allclose(grads[key], sum(p[1][key] * k for p, k in zip(parts, n)) / sum(n),
+                                   rtol=1e-9, atol=1e-15)
+    # nothing counted: loss 0 and every gradient 0
+    l0, g0 = oracle.forward_backward(TINY, params, tok, np.full_like(tgt, -1))
+    assert l0 == 0.0 and all(np.all(v == 0.0) for v in g0.values())

@@ -234,3 +234,30 @@ def test_bf16_round_is_rne():
     x = R.standard_normal(100000).astype(np.float32) * 7
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(synth.bf16_round(x), ref)
+
+
+# ---------------------------------------------------------------- masked cross-entropy
+def test_ce_masked_matches_torch_ignore_index_and_fd():
+    l = R.standard_normal((13, 29)) * 3
+    y = R.integers(0, 29, 13)
+    y[[0, 4, 5, 11]] = -1
+    loss, lse = ops.cross_entropy(l, y)
+    lt = F.cross_entropy(torch.from_numpy(l), torch.from_numpy(y), ignore_index=-1).item()
+    assert loss == pytest.approx(lt, rel=1e-13)
+    g = ops.cross_entropy_bwd(l, y, lse)
+    assert np.all(g[y < 0] == 0.0)
+    np.testing.assert_allclose(g.sum(-1), 0.0, atol=1e-16)
+    d = R.standard_normal(l.shape)
+    fd = fd_dir(lambda z: ops.cross_entropy(z, y)[0], l, d)
+    assert abs(np.sum(g * d) - fd) <= 1e-8 * max(1.0, abs(fd))
+    # the masked loss is the unmasked loss of the kept rows alone
+    keep = y >= 0
+    assert loss == pytest.approx(ops.cross_entropy(l[keep], y[keep])[0], rel=1e-14)
+
+
+def test_ce_all_masked_is_zero():
+    l = R.standard_normal((4, 9))
+    y = np.full(4, -1)
+    loss, lse = ops.cross_entropy(l, y)
+    assert loss == 0.0
+    assert np.all(ops.cross_entropy_bwd(l, y, lse) == 0.0)
