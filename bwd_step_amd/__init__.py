@@ -100,6 +100,18 @@ class Model:
                                         _ptr(loss), _ptr(grads), int(bool(accumulate))),
               "nc_forward_backward")
 
+    def forward_backward_accum(self, params, tokens, targets, n_micro, loss, grads):
+        """One step over tokens [n_micro * micro_batch, T] as n_micro microbatches (gradient accumulation)."""
+        rows = tokens.shape[0]
+        if n_micro < 1 or rows % n_micro:
+            raise ValueError(f"{rows} sequences do not split into {n_micro} microbatches")
+        micro = rows // n_micro
+        self.ensure_workspace(micro)
+        self.set_stream()
+        check(lib().nc_forward_backward_accum(self._h, _ptr(params), _ptr(tokens), _ptr(targets), int(n_micro),
+                                              micro, _ptr(loss), _ptr(grads)),
+              "nc_forward_backward_accum")
+
     def forward_logits(self, params, tokens, logits):
         batch = tokens.shape[0]
         self.ensure_workspace(batch)

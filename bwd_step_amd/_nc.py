@@ -63,6 +63,7 @@ SIGNATURES = {
     "nc_workspace_bytes": (_u64, [_vp, _i]),
     "nc_set_workspace": (_i, [_vp, _vp, _u64]),
     "nc_forward_backward": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i]),
+    "nc_forward_backward_accum": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "nc_forward_logits": (_i, [_vp, _vp, _vp, _i, _vp]),
     "nc_check": (_i, [_vp]),
     "nc_profile_enable": (_i, [_vp, _i]),

@@ -4,8 +4,12 @@
 //
 // Per row n of the chunk: lse = log sum_v exp(l_nv) (max-subtracted, fp32),
 // loss_n = lse - l_{n, y_n}, and the gradient of the mean loss
-// G_nv = (exp(l_nv - lse) - [v == y_n]) / N_total, written in the GEMM
-// operand type so that dz = G W and dW = G^T z follow directly.  A
+// G_nv = (exp(l_nv - lse) - [v == y_n]) / count, written in the GEMM
+// operand type so that dz = G W and dW = G^T z follow directly.  The mean
+// runs over the rows whose target is >= 0 (count of them over the whole
+// step, on the device): a negative target is the loss mask of supervised
+// fine-tuning ("nanochat explainer", Supervised Fine-Tuning: the loss
+// counts the assistant's tokens only), and its row gets loss 0 and G 0.  A
 // workgroup owns a row: pass 1 keeps a per-thread online (max, sum), merged
 // across the workgroup; pass 2 re-reads the row (now L2/MALL-resident) and
 // writes G.  The mean loss is reduced over all rows in a fixed order.
@@ -23,13 +27,28 @@ __device__ __forceinline__ void online_merge(float& m, float& s, float m2, float
   m = mn;
 }
 
+__device__ __forceinline__ float inv_count(const int* count) {
+  const int c = *count;
+  return c > 0 ? 1.0f / (float)c : 0.f;
+}
+
 template <class T>
 __global__ void __launch_bounds__(256) ce_row_kernel(const float* __restrict__ logits, long ldl,
                                                      const int32_t* __restrict__ tgt, T* __restrict__ G, long ldg,
-                                                     float* __restrict__ loss_rows, int V, float inv_n,
-                                                     int* __restrict__ status) {
+                                                     float* __restrict__ loss_rows, int V, int* __restrict__ status) {
   const int row = blockIdx.x;
   const float* l = logits + (size_t)row * ldl;
+  T* gr = G + (size_t)row * ldg;
+  int y = tgt[row];
+  if (y < 0) {  // not counted
+    if (threadIdx.x == 0) loss_rows[row] = 0.f;
+    for (int c = threadIdx.x * 4; c < V; c += 1024) {
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x2*>(gr + c) = u32x2{0u, 0u};
+      else *reinterpret_cast<f32x4*>(gr + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const float inv_n = inv_count(blk_count(status));
   float m = -INFINITY, s = 0.f;
   for (int c = threadIdx.x * 4; c < V; c += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(l + c);
@@ -50,13 +69,11 @@ __global__ void __launch_bounds__(256) ce_row_kernel(const float* __restrict__ l
   m = sm[0]; s = ss[0];
   for (int w = 1; w < 4; ++w) online_merge(m, s, sm[w], ss[w]);
   const float lse = m + logf(s);
-  int y = tgt[row];
-  if (y < 0 || y >= V) {
+  if (y >= V) {
     if (threadIdx.x == 0) atomicOr(status, kStatusTokenRange);
-    y = y < 0 ? 0 : V - 1;
+    y = V - 1;
   }
   if (threadIdx.x == 0) loss_rows[row] = lse - l[y];
-  T* gr = G + (size_t)row * ldg;
   for (int c = threadIdx.x * 4; c < V; c += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(l + c);
     float g0 = expf(v.x - lse), g1 = expf(v.y - lse), g2 = expf(v.z - lse), g3 = expf(v.w - lse);
@@ -76,13 +93,12 @@ __global__ void __launch_bounds__(256) ce_row_kernel(const float* __restrict__ l
 }
 
 int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
-                   int V, int n_total, int dtype, int* status, hipStream_t s) {
+                   int V, int dtype, int* status, hipStream_t s) {
   if (rows == 0) return 0;
-  const float inv_n = 1.0f / (float)n_total;
   if (dtype == 0)
-    ce_row_kernel<bf16><<<rows, 256, 0, s>>>(logits, ldl, tgt, (bf16*)G, ldg, loss_rows, V, inv_n, status);
+    ce_row_kernel<bf16><<<rows, 256, 0, s>>>(logits, ldl, tgt, (bf16*)G, ldg, loss_rows, V, status);
   else
-    ce_row_kernel<float><<<rows, 256, 0, s>>>(logits, ldl, tgt, (float*)G, ldg, loss_rows, V, inv_n, status);
+    ce_row_kernel<float><<<rows, 256, 0, s>>>(logits, ldl, tgt, (float*)G, ldg, loss_rows, V, status);
   NC_LAUNCH_CHECK();
   return 0;
 }
@@ -91,13 +107,22 @@ int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, l
 // a workgroup per row combines the (max, sum exp) pairs of its 128-column
 // segments into lse, writes loss_n = lse - l_{n, y_n} (fp32 target logit
 // from the epilogue), then overwrites the row's bf16 logits in place with
-// G_nv = (exp(l_nv - lse) - [v == y_n]) / N_total.
+// G_nv = (exp(l_nv - lse) - [v == y_n]) / count (zeros for a row that is
+// not counted).
 __global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict__ part, int nseg,
                                                         const float* __restrict__ tlog,
                                                         const int32_t* __restrict__ tgt, bf16* __restrict__ LG,
-                                                        long ld, float* __restrict__ loss_rows, int V, float inv_n,
+                                                        long ld, float* __restrict__ loss_rows, int V,
                                                         int* __restrict__ status) {
   const int row = blockIdx.x;
+  bf16* g = LG + (size_t)row * ld;
+  int y = tgt[row];
+  if (y < 0) {  // not counted
+    if (threadIdx.x == 0) loss_rows[row] = 0.f;
+    for (int c = threadIdx.x * 8; c < V; c += 2048) *reinterpret_cast<u32x4*>(g + c) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const float inv_n = inv_count(blk_count(status));
   const float* pr = part + (size_t)row * nseg * 2;
   float m = -INFINITY, s = 0.f;
   for (int k = threadIdx.x; k < nseg; k += 256) online_merge(m, s, pr[2 * k], pr[2 * k + 1]);
@@ -106,10 +131,8 @@ __global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict_
     const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
     online_merge(m, s, m2, s2);
   }
-  bf16* g = LG + (size_t)row * ld;
-  int y = tgt[row];
-  const bool y_ok = y >= 0 && y < V;
-  if (!y_ok) y = y < 0 ? 0 : V - 1;
+  const bool y_ok = y < V;
+  if (!y_ok) y = V - 1;
   // the clamped target of an out-of-range id has no fp32 logit: read the
   // stored one before the row is overwritten
   const float ty = y_ok ? tlog[row] : to_f32(g[y]);
@@ -139,18 +162,41 @@ __global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict_
 }
 
 int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
-                     float* loss_rows, int rows, int V, int n_total, int* status, hipStream_t s) {
+                     float* loss_rows, int rows, int V, int* status, hipStream_t s) {
   if (rows == 0) return 0;
   if (V % 8 || ld % 8) return NC_ERR_ARG;
-  ce_finish_kernel<<<rows, 256, 0, s>>>(part, nseg, tlog, tgt, (bf16*)logits_G, ld, loss_rows, V,
-                                        1.0f / (float)n_total, status);
+  ce_finish_kernel<<<rows, 256, 0, s>>>(part, nseg, tlog, tgt, (bf16*)logits_G, ld, loss_rows, V, status);
   NC_LAUNCH_CHECK();
   return 0;
 }
 
-// Mean of n values in a fixed order (one workgroup), non-finite -> status.
-__global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ v, int n, float* __restrict__ out,
-                                                    int* __restrict__ status) {
+// count = number of ids >= 0 (one workgroup, integer: exact in any order);
+// the loss accumulator starts at 0.
+__global__ void __launch_bounds__(1024) count_targets_kernel(const int32_t* __restrict__ y, long n,
+                                                             int* __restrict__ status) {
+  __shared__ int part[1024];
+  int c = 0;
+  for (long i = threadIdx.x; i < n; i += 1024) c += y[i] >= 0;
+  part[threadIdx.x] = c;
+  __syncthreads();
+  for (int off = 512; off >= 1; off >>= 1) {
+    if ((int)threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *blk_count(status) = part[0];
+    *blk_loss_acc(status) = 0.0;
+  }
+}
+
+int launch_count_targets(const int32_t* y, long n, int* status, hipStream_t s) {
+  count_targets_kernel<<<1, 1024, 0, s>>>(y, n, status);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+// Loss accumulator += sum of n values in a fixed order (one workgroup, fp64).
+__global__ void __launch_bounds__(1024) loss_sum_kernel(const float* __restrict__ v, int n, int* __restrict__ status) {
   __shared__ double part[1024];
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += 1024) s += (double)v[i];
@@ -160,15 +206,24 @@ __global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ v,
     if ((int)threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const float r = n > 0 ? (float)(part[0] / n) : 0.f;
-    *out = r;
-    if (!isfinite(r)) atomicOr(status, kStatusNonFinite);
-  }
+  if (threadIdx.x == 0) *blk_loss_acc(status) += part[0];
 }
 
-int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s) {
-  mean_kernel<<<1, 1024, 0, s>>>(v, n, out, status);
+__global__ void loss_final_kernel(float* __restrict__ out, int* __restrict__ status) {
+  const int c = *blk_count(status);
+  const float r = c > 0 ? (float)(*blk_loss_acc(status) / c) : 0.f;
+  *out = r;
+  if (!isfinite(r)) atomicOr(status, kStatusNonFinite);
+}
+
+int launch_loss_sum(const float* v, int n, int* status, hipStream_t s) {
+  loss_sum_kernel<<<1, 1024, 0, s>>>(v, n, status);
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+int launch_loss_final(float* out, int* status, hipStream_t s) {
+  loss_final_kernel<<<1, 1, 0, s>>>(out, status);
   NC_LAUNCH_CHECK();
   return 0;
 }

@@ -107,13 +107,26 @@ int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 
 // ---- cross-entropy
+// A negative target leaves its row out of the loss (loss row 0, G row 0); a
+// target >= V sets kStatusTokenRange.  Rows are scaled by 1 / count, count =
+// the number of counted targets of the whole step (0 counted: scale 0).
+//
+// The 256-byte status block at the start of a workspace holds the device
+// status word, the count of counted targets and the loss-sum accumulator.
+__host__ __device__ inline int* blk_count(int* status) { return status + 4; }
+__host__ __device__ inline double* blk_loss_acc(int* status) { return reinterpret_cast<double*>(status + 8); }
+// count = number of y[i] >= 0 over n ids; loss accumulator = 0
+int launch_count_targets(const int32_t* y, long n, int* status, hipStream_t s);
 // Finish the cross-entropy of a chunk from the EPI_CE partials: loss_rows,
-// and G = (softmax - onehot) * inv_n written over the bf16 logits in place.
+// and G = (softmax - onehot) / count written over the bf16 logits in place.
 int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
-                     float* loss_rows, int rows, int V, int n_total, int* status, hipStream_t s);
+                     float* loss_rows, int rows, int V, int* status, hipStream_t s);
 int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
-                   int V, int n_total, int dtype, int* status, hipStream_t s);
-int launch_mean(const float* v, int n, float* out, int* status, hipStream_t s);
+                   int V, int dtype, int* status, hipStream_t s);
+// loss accumulator += sum of the n loss rows (fixed order)
+int launch_loss_sum(const float* v, int n, int* status, hipStream_t s);
+// *out = accumulator / count (0 if count is 0); a non-finite result sets kStatusNonFinite
+int launch_loss_final(float* out, int* status, hipStream_t s);
 
 // ---- optimizer (k_optim.hip)
 // Vectors are fp32 with 16-byte aligned starts and lengths that are multiples

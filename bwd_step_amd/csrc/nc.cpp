@@ -301,12 +301,12 @@ int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int 
       lg.e.nseg = nseg;
       PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
       PROF(pf, PC_CE, 0, (double)rows * V * 4 + (double)rows * nseg * 8,
-           launch_ce_finish(part, nseg, tlog, y + c0, G, V, loss_rows + c0, rows, V, N, status, s));
+           launch_ce_finish(part, nseg, tlog, y + c0, G, V, loss_rows + c0, rows, V, status, s));
     } else {
       lg.epi = EPI_F32; lg.e.c32 = aux; lg.e.ldc = V; lg.e.beta = 0;
       PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
       PROF(pf, PC_CE, 0, (double)rows * V * (4 + es),
-           launch_ce_rows(aux, V, y + c0, G, V, loss_rows + c0, rows, V, N, dtype, status, s));
+           launch_ce_rows(aux, V, y + c0, G, V, loss_rows + c0, rows, V, dtype, status, s));
     }
     GemmCall gw = mk(G, V, false, zc, d, false, V, d, rows, dtype);
     gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
@@ -397,8 +397,10 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   return NC_OK;
 }
 
+// The count of counted targets (launch_count_targets) must be in the status
+// block before the first microbatch; `last` writes the loss of the step.
 int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* tokens, const int32_t* targets,
-                 int batch, float* loss, float* grads, int accumulate) {
+                 int batch, float* loss, float* grads, int accumulate, bool last) {
   const nc_config& c = ctx->cfg;
   hipStream_t s = ctx->stream;
   char* W = ctx->ws;
@@ -420,7 +422,8 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   TRY(lmhead_ce(W + P.z, prm + lm.offset * es, targets, N, d, V, (float*)(W + P.loss_rows), tmp,
                 grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, P.splitk_bytes, status, s,
                 pf));
-  PROF(pf, PC_OTHER, 0, 0, launch_mean((float*)(W + P.loss_rows), N, loss, status, s));
+  PROF(pf, PC_OTHER, 0, 0, launch_loss_sum((float*)(W + P.loss_rows), N, status, s));
+  if (last) PROF(pf, PC_OTHER, 0, 0, launch_loss_final(loss, status, s));
   PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 4,
        launch_rmsnorm_bwd(tmp, W + P.z, (float*)(W + P.rf), dx, dx_lp, N, d, 0, dt, s));
 
@@ -596,8 +599,29 @@ int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens, 
   if (!ctx->ws) return NC_ERR_WORKSPACE;
   const Plan P = make_plan(ctx->cfg, batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  TRY(launch_count_targets(targets, (long)batch * ctx->cfg.seq_len, (int*)(ctx->ws + P.status), ctx->stream));
   TRY(run_forward(ctx, P, params, tokens, batch));
-  return run_backward(ctx, P, params, tokens, targets, batch, loss, grads, accumulate);
+  return run_backward(ctx, P, params, tokens, targets, batch, loss, grads, accumulate, true);
+}
+
+int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* targets,
+                              int n_micro, int micro_batch, float* loss, float* grads) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !targets || !loss || !grads) return NC_ERR_NULL;
+  if (n_micro < 1 || micro_batch < 1 || micro_batch > ctx->cfg.max_batch) return NC_ERR_ARG;
+  if (!ctx->ws) return NC_ERR_WORKSPACE;
+  const Plan P = make_plan(ctx->cfg, micro_batch);
+  if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  const long T = ctx->cfg.seq_len;
+  // one count over the whole step: every microbatch is scaled by 1 / (counted targets of the step)
+  TRY(launch_count_targets(targets, (long)n_micro * micro_batch * T, (int*)(ctx->ws + P.status), ctx->stream));
+  for (int m = 0; m < n_micro; ++m) {
+    const size_t o = (size_t)m * micro_batch * T;
+    TRY(run_forward(ctx, P, params, tokens + o, micro_batch));
+    TRY(run_backward(ctx, P, params, tokens + o, targets + o, micro_batch, loss, grads, m > 0 ? 1 : 0,
+                     m == n_micro - 1));
+  }
+  return NC_OK;
 }
 
 int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, int batch, float* logits) {
@@ -754,9 +778,11 @@ int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, 
   const int chunk = ce_chunk(N, V, dtype);
   const uint64_t sk_bytes = std::max(gemm_ws_bytes(chunk, d, V, dtype), gemm_ws_bytes(V, d, chunk, dtype));
   float* sk = sk_bytes ? (float*)(w + off[4]) : nullptr;
+  TRY(launch_count_targets(y, N, status, s));
   TRY(lmhead_ce(z, W, y, N, d, V, (float*)(w + off[3]), dz, dW, 0, dtype, (float*)(w + off[1]), w + off[2], sk,
                 sk_bytes, status, s, nullptr));
-  return launch_mean((float*)(w + off[3]), N, loss, status, s);
+  TRY(launch_loss_sum((float*)(w + off[3]), N, status, s));
+  return launch_loss_final(loss, status, s);
 }
 
 int nc_rmsnorm_fwd(const float* x, void* y, float* r, int N, int d, float eps, int dtype, void* stream) {

@@ -132,17 +132,39 @@ int nc_set_workspace(nc_ctx* ctx, void* dev_ptr, uint64_t bytes);
  * One training step's forward and backward pass.
  *   params  : device, flat layout above, element type cfg.dtype.
  *   tokens  : device int32 [batch, seq_len]; targets: device int32 [batch, seq_len]
- *             (targets[b][t] is the id that follows tokens[b][t]).
- *   loss    : device fp32 scalar; the mean cross-entropy over batch*seq_len
- *             positions, in nats.
- *   grads   : device fp32, flat layout; accumulate = 0 overwrites it,
- *             accumulate = 1 adds this step's gradient to it.
+ *             (targets[b][t] is the id that follows tokens[b][t]; a negative
+ *             target leaves the position out of the loss: the loss mask of
+ *             supervised fine-tuning, "nanochat explainer", Supervised
+ *             Fine-Tuning; a target >= vocab is a status error).
+ *   loss    : device fp32 scalar; the mean cross-entropy over the positions
+ *             whose target is >= 0 (all batch*seq_len in pretraining), in
+ *             nats; 0 when no position counts.
+ *   grads   : device fp32, flat layout, the gradient of that loss;
+ *             accumulate = 0 overwrites it, accumulate = 1 adds to it.
  * Saved activations live in the workspace, which must hold
  * nc_workspace_bytes(ctx, batch) bytes.  Not re-entrant: one context per stream.
  */
 int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens,
                         const int32_t* targets, int batch, float* loss,
                         float* grads, int accumulate);
+
+/*
+ * One step over n_micro * micro_batch sequences run as n_micro microbatches
+ * of micro_batch (gradient accumulation; the workspace only holds one
+ * microbatch: the smaller batch that "nanochat explained: Karpathy's pipeline
+ * from raw text to a chat model", What you need to run it, asks of GPUs with
+ * less memory, at an unchanged step).  tokens, targets: device int32
+ * [n_micro * micro_batch, seq_len], microbatch m in rows m*micro_batch ..
+ * loss and grads (overwritten) are those of the whole step: the mean over
+ * every counted position of all microbatches, so the result equals one
+ * nc_forward_backward over all the sequences.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (n_micro < 1, micro_batch outside
+ * [1, max_batch]), NC_ERR_WORKSPACE (workspace < nc_workspace_bytes(ctx,
+ * micro_batch)).
+ */
+int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* tokens,
+                              const int32_t* targets, int n_micro, int micro_batch,
+                              float* loss, float* grads);
 
 /* Forward pass only; logits: device fp32 [batch, seq_len, vocab]. */
 int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
@@ -270,8 +292,10 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v,
  * Fused LM head + softmax cross-entropy, forward and backward ("nanochat
  * explainer", Pretraining: next-token cross-entropy), processed in chunks of
  * tokens so that the full [N, V] logits never exist:
- *   l = z W^T; loss = mean_n [logsumexp(l_n) - l_{n,y_n}];
- *   G = (softmax(l) - onehot(y)) / N;  dz = G W;  dW = G^T z.
+ *   l = z W^T; loss = mean_n [logsumexp(l_n) - l_{n,y_n}] over the n with
+ *   y_n >= 0 (a negative id is not counted; 0 if none is);
+ *   G = (softmax(l) - onehot(y)) / count (0 on rows not counted);
+ *   dz = G W;  dW = G^T z.
  * z: (dt) [N, d]; W: (dt) [V, d]; y: int32 [N]; loss: fp32 scalar;
  * dz: fp32 [N, d] (overwritten); dW: fp32 [V, d] (overwritten).
  * Errors: NC_ERR_NULL, NC_ERR_ARG, NC_ERR_WORKSPACE.  Ids outside [0, V)

@@ -121,6 +121,11 @@ def test_workspace_sizes_and_host_errors():
     assert lib().nc_forward_backward(h, fake, fake, fake, 3, fake, fake, 0) == 8
     assert lib().nc_forward_backward(h, fake, fake, fake, 1, fake, fake, 2) == 8
     assert lib().nc_forward_logits(h, fake, fake, 0, fake) == 8
+    # gradient accumulation: no workspace yet, then bad counts
+    assert lib().nc_forward_backward_accum(h, fake, fake, fake, 2, 1, fake, fake) == 3
+    assert lib().nc_forward_backward_accum(h, fake, fake, fake, 0, 1, fake, fake) == 8
+    assert lib().nc_forward_backward_accum(h, fake, fake, fake, 2, 3, fake, fake) == 8
+    assert lib().nc_forward_backward_accum(h, fake, None, fake, 2, 1, fake, fake) == 2
     assert lib().nc_set_workspace(h, ctypes.c_void_p(0x1001), 4096) == 8  # misaligned
     lib().nc_destroy(h)
 
