@@ -23,8 +23,9 @@ def _dtype_code(dtype):
 
 
 def _stream(stream=None):
+    """A HIP stream handle: a torch stream, a raw handle, or (None) torch's current stream."""
     if stream is not None:
-        return stream
+        return ctypes.c_void_p(stream.cuda_stream) if hasattr(stream, "cuda_stream") else stream
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -118,6 +119,30 @@ class Model:
         self.set_stream()
         check(lib().nc_forward_logits(self._h, _ptr(params), _ptr(tokens), batch, _ptr(logits)),
               "nc_forward_logits")
+
+    # ---- inference with a KV cache (nc_prefill, nc_decode)
+    def kv_cache_bytes(self, cache_batch, max_len):
+        return int(lib().nc_kv_cache_bytes(self._h, cache_batch, max_len))
+
+    def decode_workspace_bytes(self, batch, max_len):
+        return int(lib().nc_decode_workspace_bytes(self._h, batch, max_len))
+
+    def prefill(self, params, tokens, cache, cache_batch, max_len, logits, slot0=0):
+        """tokens [batch, len] into cache slots slot0..; logits [batch, V] of the last positions."""
+        batch, length = tokens.shape
+        self.ensure_workspace(batch)
+        self.set_stream()
+        check(lib().nc_prefill(self._h, _ptr(params), _ptr(tokens), batch, length, _ptr(cache), int(cache_batch),
+                               int(max_len), int(slot0), _ptr(logits)),
+              "nc_prefill")
+
+    def decode(self, params, tokens, pos, cache, max_len, workspace, logits):
+        """One token per sequence (tokens [B], pos [B] int32 on the device); logits [B, V]."""
+        self.set_stream()
+        check(lib().nc_decode(self._h, _ptr(params), _ptr(tokens), _ptr(pos), tokens.shape[0], _ptr(cache),
+                              int(max_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _ptr(logits)),
+              "nc_decode")
 
     def profile(self, on=True):
         """Enable (and clear) or disable per-kernel-class event timing."""

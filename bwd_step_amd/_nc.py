@@ -65,6 +65,10 @@ SIGNATURES = {
     "nc_forward_backward": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i]),
     "nc_forward_backward_accum": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "nc_forward_logits": (_i, [_vp, _vp, _vp, _i, _vp]),
+    "nc_kv_cache_bytes": (_u64, [_vp, _i, _i]),
+    "nc_decode_workspace_bytes": (_u64, [_vp, _i, _i]),
+    "nc_prefill": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp]),
+    "nc_decode": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _u64, _vp]),
     "nc_check": (_i, [_vp]),
     "nc_profile_enable": (_i, [_vp, _i]),
     "nc_profile_read": (_i, [_vp, ctypes.POINTER(NcProfEntry), _i]),

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libnc.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["nc.cpp", "k_norm.hip", "k_embed.hip", "k_gemm.hip", "k_attn.hip", "k_ce.hip", "k_optim.hip"]
+SOURCES = ["nc.cpp", "k_norm.hip", "k_embed.hip", "k_gemm.hip", "k_attn.hip", "k_ce.hip", "k_optim.hip", "k_infer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

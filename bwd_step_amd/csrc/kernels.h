@@ -128,6 +128,38 @@ int launch_loss_sum(const float* v, int n, int* status, hipStream_t s);
 // *out = accumulator / count (0 if count is 0); a non-finite result sets kStatusNonFinite
 int launch_loss_final(float* out, int* status, hipStream_t s);
 
+// ---- inference (k_infer.hip)
+// Skinny products for a few rows (decode): out[m][n] = sum_k x[m][k] W[n][k],
+// W [N, K] k-contiguous, x [M, ldx]; epilogues EPI_F32 / EPI_RESID (c32),
+// EPI_LP / EPI_RELU2 (c_lp, element type); rows beyond kSkinnyM run in
+// further passes.  K, ldx, ldw multiples of 16 bytes' worth of elements.
+constexpr int kSkinnyM = 16;
+struct SkinnyOut {
+  float* c32 = nullptr;
+  void* c_lp = nullptr;
+  long ld = 0;
+};
+int launch_skinny(const void* x, long ldx, const void* W, long ldw, int M, int N, int K, int epi, SkinnyOut o,
+                  int dtype, hipStream_t s);
+struct DecodeQkArgs {
+  const void* qkv = nullptr;  // [B, 3hh]: q | k | v
+  long ldqkv = 0;
+  void* qhat = nullptr;       // [B, hh]
+  void* kc = nullptr;         // this layer's K cache [slot][H][max_len][hd]
+  void* vc = nullptr;         // this layer's V cache
+  const int32_t* pos = nullptr;
+  int max_len = 0;
+  int* status = nullptr;      // position outside [0, max_len): kStatusTokenRange
+};
+int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int hd, float eps, int dtype,
+                     hipStream_t s);
+// Attention of qhat [B, hh] against cached keys 0 .. pos[b]; out [B, hh].
+// part_o: B*H*nchunk*hd floats, part_ml: B*H*nchunk*2 (nchunk = ceil(max_len / 256)).
+int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int hd,
+                       int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s);
+int launch_cache_fill(const void* qkv, int B, int T, int H, int hd, void* kc, void* vc, int max_len, int slot0,
+                      int dtype, hipStream_t s);
+
 // ---- optimizer (k_optim.hip)
 // Vectors are fp32 with 16-byte aligned starts and lengths that are multiples
 // of 4 (every tensor of the layout is a multiple of 64 elements).

@@ -37,6 +37,8 @@ inline int ce_chunk(int N, int V, int dtype) {
 
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+// Longest KV cache (positions) the inference entry points accept.
+constexpr int kMaxCacheLen = 1 << 16;
 
 // LM-head chunk scratch besides G: bf16 path, the GEMM epilogue's per-row
 // softmax partials (max, sum exp) over 128-column segments and the target
@@ -320,11 +322,13 @@ int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int 
   return NC_OK;
 }
 
-int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* tokens, int batch) {
+// Forward over batch sequences of T tokens (T <= seq_len; the plan is sized
+// for seq_len), saving what the backward and the cache fill read.
+int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* tokens, int batch, int T) {
   const nc_config& c = ctx->cfg;
   hipStream_t s = ctx->stream;
   char* W = ctx->ws;
-  const int N = batch * c.seq_len, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
+  const int N = batch * T, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
   const int V = c.vocab, dt = c.dtype;
   const size_t es = dt == NC_BF16 ? 2 : 4;
   const char* prm = (const char*)params;
@@ -333,9 +337,9 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   float* cs = (float*)(W + P.rope);
 
   Prof* pf = &ctx->prof;
-  const double pairs = (double)batch * H * c.seq_len * (c.seq_len + 1) / 2.0;  // causal (query, key) pairs
+  const double pairs = (double)batch * H * T * (T + 1) / 2.0;  // causal (query, key) pairs
   PROF(pf, PC_EMB_FWD, 0, (double)N * d * (es + 4) + N * 4.0, launch_embed_fwd(prm, tokens, x, N, d, V, dt, status, s));
-  PROF(pf, PC_OTHER, 0, 0, launch_rope_table(cs, c.seq_len, hd, c.rope_base, s));
+  PROF(pf, PC_OTHER, 0, 0, launch_rope_table(cs, T, hd, c.rope_base, s));
   // bf16 path: the output projections store their sublayer output y in bf16
   // and the next RMSNorm adds it to the fp32 stream x (x += y, then the norm);
   // fp32 path: the projections add into x in their epilogue.
@@ -373,14 +377,14 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
     PROF(pf, PC_GEMM, gflops(g1), gbytes(g1), launch_gemm(g1, s));
     PROF(pf, PC_QK_FWD, 0, 4.0 * N * hh * es + 2.0 * N * H * 4, launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
-                               (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, c.seq_len, c.norm_eps, dt, s));
+                               (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, T, c.norm_eps, dt, s));
     AttnArgs a;
     a.q = qkv; a.ldq = 3 * hh;
     a.k = qkv + hh * es; a.ldk = 3 * hh;
     a.v = qkv + 2 * hh * es; a.ldv = 3 * hh;
     a.o = L + P.O; a.ldo = hh;
     a.lse = (float*)(L + P.lse);
-    a.B = batch; a.H = H; a.T = c.seq_len;
+    a.B = batch; a.H = H; a.T = T;
     PROF(pf, PC_ATTN_FWD, 4.0 * hd * pairs, 0, launch_attn_fwd(a, hd, dt, s));
     GemmCall g2 = mk(L + P.O, hh, true, Wo, hh, true, N, d, hh, dt);
     proj_out(g2);
@@ -600,7 +604,7 @@ int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens, 
   const Plan P = make_plan(ctx->cfg, batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
   TRY(launch_count_targets(targets, (long)batch * ctx->cfg.seq_len, (int*)(ctx->ws + P.status), ctx->stream));
-  TRY(run_forward(ctx, P, params, tokens, batch));
+  TRY(run_forward(ctx, P, params, tokens, batch, ctx->cfg.seq_len));
   return run_backward(ctx, P, params, tokens, targets, batch, loss, grads, accumulate, true);
 }
 
@@ -617,7 +621,7 @@ int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* to
   TRY(launch_count_targets(targets, (long)n_micro * micro_batch * T, (int*)(ctx->ws + P.status), ctx->stream));
   for (int m = 0; m < n_micro; ++m) {
     const size_t o = (size_t)m * micro_batch * T;
-    TRY(run_forward(ctx, P, params, tokens + o, micro_batch));
+    TRY(run_forward(ctx, P, params, tokens + o, micro_batch, (int)T));
     TRY(run_backward(ctx, P, params, tokens + o, targets + o, micro_batch, loss, grads, m > 0 ? 1 : 0,
                      m == n_micro - 1));
   }
@@ -631,7 +635,7 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, in
   if (!ctx->ws) return NC_ERR_WORKSPACE;
   const Plan P = make_plan(ctx->cfg, batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
-  TRY(run_forward(ctx, P, params, tokens, batch));
+  TRY(run_forward(ctx, P, params, tokens, batch, ctx->cfg.seq_len));
   const nc_config& c = ctx->cfg;
   const size_t es = c.dtype == NC_BF16 ? 2 : 4;
   const int N = batch * c.seq_len;
@@ -639,6 +643,131 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, in
                    true, N, c.vocab, c.d_model, c.dtype);
   lg.epi = EPI_F32; lg.e.c32 = logits; lg.e.ldc = c.vocab; lg.e.beta = 0;
   return launch_gemm(lg, ctx->stream);
+}
+
+// ---------------------------------------------------------------- inference
+// KV cache: per layer K then V, each [cache_batch][H][max_len][hd].
+static uint64_t kv_layer_elems(const nc_config& c, int cache_batch, int max_len) {
+  return (uint64_t)cache_batch * c.n_heads * max_len * c.head_dim;
+}
+
+uint64_t nc_kv_cache_bytes(const nc_ctx* ctx, int cache_batch, int max_len) {
+  if (!ctx || cache_batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return 0;
+  const size_t es = ctx->cfg.dtype == NC_BF16 ? 2 : 4;
+  return (uint64_t)ctx->cfg.depth * 2 * kv_layer_elems(ctx->cfg, cache_batch, max_len) * es;
+}
+
+namespace {
+struct DecodePlan {
+  size_t x = 0, r = 0, a = 0, qkv = 0, qhat = 0, o = 0, g = 0, cs = 0, part_o = 0, part_ml = 0, total = 0;
+};
+DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
+  DecodePlan p;
+  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+  const size_t B = batch, d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff;
+  const size_t nchunk = (max_len + 255) / 256;
+  size_t o = 0;
+  auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
+  take(256);  // status block
+  p.x = take(B * d * 4);
+  p.r = take(B * 4);
+  p.a = take(B * std::max(d, F) * es);  // normed rows, and g = relu(u)^2 of the MLP
+  p.qkv = take(B * 3 * hh * es);
+  p.qhat = take(B * hh * es);
+  p.o = take(B * hh * es);
+  p.g = take(B * F * es);
+  p.cs = take((size_t)max_len * c.head_dim * 4);
+  p.part_o = take(B * c.n_heads * nchunk * c.head_dim * 4);
+  p.part_ml = take(B * c.n_heads * nchunk * 2 * 4);
+  p.total = o;
+  return p;
+}
+}  // namespace
+
+uint64_t nc_decode_workspace_bytes(const nc_ctx* ctx, int batch, int max_len) {
+  if (!ctx || batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return 0;
+  return decode_plan(ctx->cfg, batch, max_len).total;
+}
+
+int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* tokens, int batch, int len, void* cache,
+               int cache_batch, int max_len, int slot0, float* logits) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !cache || !logits) return NC_ERR_NULL;
+  const nc_config& c = ctx->cfg;
+  if (batch < 1 || batch > c.max_batch || len < 1 || len > c.seq_len || max_len < len ||
+      max_len > kMaxCacheLen || slot0 < 0 || cache_batch < slot0 + batch)
+    return NC_ERR_ARG;
+  if (!ctx->ws) return NC_ERR_WORKSPACE;
+  const Plan P = make_plan(c, batch);
+  if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = ctx->stream;
+  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+  TRY(run_forward(ctx, P, params, tokens, batch, len));
+  const uint64_t le = kv_layer_elems(c, cache_batch, max_len);
+  for (int l = 0; l < c.depth; ++l) {
+    char* kc = (char*)cache + (size_t)l * 2 * le * es;
+    TRY(launch_cache_fill(ctx->ws + P.layers_base + (size_t)l * P.layer_stride + P.qkv, batch, len, c.n_heads,
+                          c.head_dim, kc, kc + le * es, max_len, slot0, c.dtype, s));
+  }
+  // logits of each sequence's last position: rows len-1, 2 len-1, ... of z
+  SkinnyOut o;
+  o.c32 = logits;
+  o.ld = c.vocab;
+  return launch_skinny(ctx->ws + P.z + (size_t)(len - 1) * c.d_model * es, (long)len * c.d_model,
+                       (const char*)params + ctx->layout.back().offset * es, c.d_model, batch, c.vocab, c.d_model,
+                       EPI_F32, o, c.dtype, s);
+}
+
+int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* pos, int batch, void* cache,
+              int max_len, void* workspace, uint64_t ws_bytes, float* logits) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !pos || !cache || !workspace || !logits) return NC_ERR_NULL;
+  const nc_config& c = ctx->cfg;
+  if (batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return NC_ERR_ARG;
+  if ((uintptr_t)workspace & 255) return NC_ERR_ARG;
+  const DecodePlan D = decode_plan(c, batch, max_len);
+  if (ws_bytes < D.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = ctx->stream;
+  const int d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff, V = c.vocab, dt = c.dtype;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  char* w = (char*)workspace;
+  int* status = (int*)w;
+  float* x = (float*)(w + D.x);
+  float* r = (float*)(w + D.r);
+  float* cs = (float*)(w + D.cs);
+  const char* prm = (const char*)params;
+  const uint64_t le = kv_layer_elems(c, batch, max_len);
+  TRY(launch_rope_table(cs, max_len, hd, c.rope_base, s));
+  TRY(launch_embed_fwd(prm, tokens, x, batch, d, V, dt, status, s));
+  auto gemv = [&](const void* in, long ldin, const char* Wt, int N, int K, int epi, float* c32, void* clp,
+                  long ld) {
+    SkinnyOut o;
+    o.c32 = c32;
+    o.c_lp = clp;
+    o.ld = ld;
+    return launch_skinny(in, ldin, Wt, K, batch, N, K, epi, o, dt, s);
+  };
+  for (int l = 0; l < c.depth; ++l) {
+    const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
+    const char* Wo = prm + ctx->layout[2 + 4 * l].offset * es;
+    const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
+    const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
+    char* kc = (char*)cache + (size_t)l * 2 * le * es;
+    TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
+    TRY(gemv(w + D.a, d, Wqkv, 3 * hh, d, EPI_LP, nullptr, w + D.qkv, 3 * hh));
+    DecodeQkArgs q;
+    q.qkv = w + D.qkv; q.ldqkv = 3 * hh; q.qhat = w + D.qhat;
+    q.kc = kc; q.vc = kc + le * es; q.pos = pos; q.max_len = max_len; q.status = status;
+    TRY(launch_decode_qk(q, cs, batch, H, hd, c.norm_eps, dt, s));
+    TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, hd, max_len, (float*)(w + D.part_o),
+                           (float*)(w + D.part_ml), w + D.o, dt, s));
+    TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d));
+    TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
+    TRY(gemv(w + D.a, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F));
+    TRY(gemv(w + D.g, F, W2, d, F, EPI_RESID, x, nullptr, d));
+  }
+  TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
+  return gemv(w + D.a, d, prm + ctx->layout.back().offset * es, V, d, EPI_F32, logits, nullptr, V);
 }
 
 int nc_check(nc_ctx* ctx) {

@@ -170,6 +170,47 @@ int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* to
 int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
                       int batch, float* logits);
 
+/* ------------------------------------------------------------------------
+ * Inference with a KV cache ("nanochat explainer", Inference & KV Cache):
+ * prefill runs prompts through the forward and stores every layer's keys
+ * and values; decode runs one new token per sequence against them.
+ *
+ * Cache (caller-owned device memory, nc_kv_cache_bytes): per layer K, then
+ * V, each [cache_batch][n_heads][max_len][head_dim] in the element type;
+ * keys are stored QK-normalised and rotated.  Slot b of the cache holds
+ * sequence b; 1 <= max_len <= 65536.
+ * ------------------------------------------------------------------------ */
+uint64_t nc_kv_cache_bytes(const nc_ctx* ctx, int cache_batch, int max_len);
+/* Workspace of nc_decode for `batch` sequences and a cache of max_len. */
+uint64_t nc_decode_workspace_bytes(const nc_ctx* ctx, int batch, int max_len);
+/*
+ * Prefill: tokens int32 [batch, len] (1 <= len <= seq_len <= max_len) run
+ * through the forward (the context's workspace, nc_workspace_bytes(ctx,
+ * batch)); their keys and values go to cache slots slot0 .. slot0+batch-1,
+ * positions 0 .. len-1; logits fp32 [batch, vocab] receives the logits of
+ * each sequence's last position.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG, NC_ERR_WORKSPACE.
+ */
+int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* tokens, int batch, int len,
+               void* cache, int cache_batch, int max_len, int slot0, float* logits);
+/*
+ * Decode one token per sequence: tokens int32 [batch], pos int32 [batch]
+ * (device; the position of each token, i.e. its sequence's length so far;
+ * may differ per sequence).  The token's key and value are written to the
+ * cache (cache_batch == batch) at pos[b], it attends to positions 0..pos[b],
+ * and logits fp32 [batch, vocab] receives the next-token logits.  workspace:
+ * device, 256-byte aligned, nc_decode_workspace_bytes(ctx, batch, max_len)
+ * bytes; its first word is a status word that the caller zeroes before the
+ * first call and reads (and clears) with nc_op_status: a position outside
+ * [0, max_len) or an id outside [0, vocab) sets it.
+ * Enqueued on the context's stream with no host synchronisation and no
+ * allocation, so the call can be captured in a HIP graph.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG, NC_ERR_WORKSPACE.
+ */
+int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* pos,
+              int batch, void* cache, int max_len, void* workspace, uint64_t ws_bytes,
+              float* logits);
+
 /*
  * Synchronise the context's stream, then read and clear the device status
  * word.  Returns NC_OK, NC_ERR_TOKEN_RANGE, NC_ERR_NONFINITE or NC_ERR_HIP.

@@ -188,3 +188,34 @@ def test_optim_sizes_and_host_errors():
     assert lib().nc_optim_init(h, None, fake) == 2
     assert lib().nc_optim_init(h, fake, None) == 2
     lib().nc_destroy(h)
+
+
+def test_kv_cache_size_matches_the_pages_example():
+    # "nanochat explainer", Inference & KV Cache: 16 layers, 16 heads, head
+    # dim 64, sequence 2048 hold 128 MB of keys and values (bf16, one sequence)
+    g = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "kv_cache_size.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            g[k] = int(v)
+    rc, h = init(make(depth=g["layers"], d_model=g["heads"] * g["head_dim"], n_heads=g["heads"],
+                      head_dim=g["head_dim"], vocab=512, seq_len=g["seq"]))
+    assert rc == 0
+    assert lib().nc_kv_cache_bytes(h, 1, g["seq"]) == g["mha_bytes"]
+    assert lib().nc_kv_cache_bytes(h, 3, g["seq"]) == 3 * g["mha_bytes"]
+    assert lib().nc_kv_cache_bytes(h, 0, g["seq"]) == 0
+    assert lib().nc_kv_cache_bytes(h, 1, 70000) == 0
+    assert lib().nc_decode_workspace_bytes(h, 4, 2048) > 0
+    fake = ctypes.c_void_p(0x1000)
+    # prefill: len beyond seq_len, slots beyond the cache, no workspace
+    assert lib().nc_prefill(h, fake, fake, 1, g["seq"] + 1, fake, 1, g["seq"] + 1, 0, fake) == 8
+    assert lib().nc_prefill(h, fake, fake, 2, 16, fake, 2, 64, 1, fake) == 8
+    assert lib().nc_prefill(h, fake, fake, 1, 16, fake, 1, 64, 0, fake) == 3
+    assert lib().nc_prefill(h, None, fake, 1, 16, fake, 1, 64, 0, fake) == 2
+    # decode: workspace too small or misaligned
+    need = lib().nc_decode_workspace_bytes(h, 2, 64)
+    assert lib().nc_decode(h, fake, fake, fake, 2, fake, 64, fake, need - 1, fake) == 3
+    assert lib().nc_decode(h, fake, fake, fake, 2, fake, 64, ctypes.c_void_p(0x1010), need, fake) == 8
+    assert lib().nc_decode(h, fake, fake, None, 2, fake, 64, fake, need, fake) == 2
+    lib().nc_destroy(h)
