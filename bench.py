@@ -13,7 +13,9 @@ events, and the float64 oracle's throughput on this host (cpu_baseline).
 --op attention | lmhead times one operation entry point instead of the step
 (the attention microbenchmark B16 x H10 x T2048 x hd128, or the fused LM head
 + cross-entropy on 32768 x 1280 x 65536); --op optim times the optimizer
-step (nc_optim_step) over the depth-20 parameter set; --op copy times a plain 1 GiB
+step (nc_optim_step) over the depth-20 parameter set; --op decode times one
+KV-cache decode step (nc_decode, captured in a HIP graph) for
+--decode-batch sequences after a --context-token prefill; --op copy times a plain 1 GiB
 device-to-device copy, the reference that scales the HBM byte counters
 (FETCH_SIZE, WRITE_SIZE) behind the roofline's `traffic`.  These lines are
 for profiling and carry their own metric, not the headline one.
@@ -165,6 +167,40 @@ def op_bench(args):
             a, b = min(r, c), max(r, c)
             flops += 5 * (4.0 * a * a * b + 2.0 * a ** 3)  # X X^T, A A, (bA + cAA) X per Newton-Schulz step
         name = f"optimizer step (AdamW E/W_lm + Muon, 5 Newton-Schulz steps) depth-20, {P} parameters"
+    elif args.op == "decode":
+        import numpy as np
+
+        import bwd_step_amd
+        B, ctx = args.decode_batch, args.context
+        model = bwd_step_amd.Model(20, vocab=65536, seq_len=2048, max_batch=B, dtype="bf16")
+        c = model.config
+        P, d, V, L = model.param_count, c["d_model"], c["vocab"], c["depth"]
+        hh = c["n_heads"] * c["head_dim"]
+        flat = (0.02 * torch.randn(P, device=dev, generator=g)).to(torch.bfloat16)
+        max_len = 2048
+        cache = torch.zeros(model.kv_cache_bytes(B, max_len) // 2, dtype=torch.bfloat16, device=dev)
+        ws = torch.zeros(model.decode_workspace_bytes(B, max_len), dtype=torch.uint8, device=dev)
+        logits = torch.empty(B, V, dtype=torch.float32, device=dev)
+        prompt = torch.randint(0, V, (B, ctx), device=dev, generator=g, dtype=torch.int32)
+        model.prefill(flat, prompt, cache, B, max_len, logits)
+        tok = torch.randint(0, V, (B,), device=dev, generator=g, dtype=torch.int32)
+        pos = torch.full((B,), ctx, device=dev, dtype=torch.int32)
+        # one decode step captured in a HIP graph (the step at position ctx, replayed)
+        side = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            model.decode(flat, tok, pos, cache, max_len, ws, logits)  # warm the launch path
+            side.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                model.decode(flat, tok, pos, cache, max_len, ws, logits)
+        model.set_stream()
+        fn = graph.replay
+        # algorithmic bytes per step: every weight but E once, B rows of E, the
+        # cached keys and values of positions 0..ctx read, one position written
+        kv = L * B * hh * 2 * 2 * (ctx + 1)
+        decode_bytes = (P - V * d) * 2 + B * d * 2 + kv + B * V * 4
+        flops = 0.0
+        name = f"decode step (KV cache, HIP graph) depth-20, {B} sequences at position {ctx}"
     elif args.op == "attention":
         B, H, T, hd = 16, 10, 2048, 128
         q, k, v, do = (torch.randn(B, T, H, hd, device=dev, generator=g).to(torch.bfloat16) for _ in range(4))
@@ -190,6 +226,17 @@ def op_bench(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    if args.op == "decode":
+        st = ops.status(ws)
+        if st != 0:
+            raise RuntimeError(f"decode status {st}")
+        print(json.dumps({"metric": name + " tokens/s", "value": round(args.decode_batch / (ms / 1e3), 1),
+                          "unit": "tokens/s", "ms_per_step": round(ms, 4),
+                          "algorithmic_bytes_per_step": decode_bytes,
+                          "hbm_gbps": round(decode_bytes / ms / 1e6, 1), "hbm_frac": round(decode_bytes / (ms / 1e3) / PEAK_HBM_BYTES, 4),
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "data": "synthetic, seeded torch generator", "higher_is_better": True}), flush=True)
+        return
     if args.op == "optim":
         print(json.dumps({"metric": name + " ms per step", "value": round(ms, 3), "unit": "ms",
                           "newton_schulz_tflop": round(flops / 1e12, 3),
@@ -215,7 +262,9 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--op", choices=["attention", "lmhead", "copy", "optim"], default=None)
+    ap.add_argument("--op", choices=["attention", "lmhead", "copy", "optim", "decode"], default=None)
+    ap.add_argument("--decode-batch", type=int, default=1, help="sequences per decode step (--op decode)")
+    ap.add_argument("--context", type=int, default=1024, help="prompt length before the timed decode step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the data-parallel sharding across "

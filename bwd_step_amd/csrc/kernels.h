@@ -139,8 +139,10 @@ struct SkinnyOut {
   void* c_lp = nullptr;
   long ld = 0;
 };
+// norm_eps > 0: x is the fp32 residual stream [M, ldx] and the product takes
+// its RMS-normalised rows (the forward's parameter-free RMSNorm, fused).
 int launch_skinny(const void* x, long ldx, const void* W, long ldw, int M, int N, int K, int epi, SkinnyOut o,
-                  int dtype, hipStream_t s);
+                  int dtype, hipStream_t s, float norm_eps = 0.f);
 struct DecodeQkArgs {
   const void* qkv = nullptr;  // [B, 3hh]: q | k | v
   long ldqkv = 0;
@@ -154,7 +156,8 @@ struct DecodeQkArgs {
 int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int hd, float eps, int dtype,
                      hipStream_t s);
 // Attention of qhat [B, hh] against cached keys 0 .. pos[b]; out [B, hh].
-// part_o: B*H*nchunk*hd floats, part_ml: B*H*nchunk*2 (nchunk = ceil(max_len / 256)).
+// part_o: B*H*nchunk*hd floats, part_ml: B*H*nchunk*2 (nchunk = ceil(max_len / kDecodeKeys)).
+constexpr int kDecodeKeys = 64;
 int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int hd,
                        int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s);
 int launch_cache_fill(const void* qkv, int B, int T, int H, int hd, void* kc, void* vc, int max_len, int slot0,

@@ -659,19 +659,17 @@ uint64_t nc_kv_cache_bytes(const nc_ctx* ctx, int cache_batch, int max_len) {
 
 namespace {
 struct DecodePlan {
-  size_t x = 0, r = 0, a = 0, qkv = 0, qhat = 0, o = 0, g = 0, cs = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t x = 0, qkv = 0, qhat = 0, o = 0, g = 0, cs = 0, part_o = 0, part_ml = 0, total = 0;
 };
 DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
   DecodePlan p;
   const size_t es = c.dtype == NC_BF16 ? 2 : 4;
   const size_t B = batch, d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff;
-  const size_t nchunk = (max_len + 255) / 256;
+  const size_t nchunk = (max_len + kDecodeKeys - 1) / kDecodeKeys;
   size_t o = 0;
   auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
   take(256);  // status block
   p.x = take(B * d * 4);
-  p.r = take(B * 4);
-  p.a = take(B * std::max(d, F) * es);  // normed rows, and g = relu(u)^2 of the MLP
   p.qkv = take(B * 3 * hh * es);
   p.qhat = take(B * hh * es);
   p.o = take(B * hh * es);
@@ -733,41 +731,39 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
   char* w = (char*)workspace;
   int* status = (int*)w;
   float* x = (float*)(w + D.x);
-  float* r = (float*)(w + D.r);
   float* cs = (float*)(w + D.cs);
   const char* prm = (const char*)params;
   const uint64_t le = kv_layer_elems(c, batch, max_len);
   TRY(launch_rope_table(cs, max_len, hd, c.rope_base, s));
   TRY(launch_embed_fwd(prm, tokens, x, batch, d, V, dt, status, s));
-  auto gemv = [&](const void* in, long ldin, const char* Wt, int N, int K, int epi, float* c32, void* clp,
-                  long ld) {
+  auto gemv = [&](const void* in, long ldin, const char* Wt, int N, int K, int epi, float* c32, void* clp, long ld,
+                  float norm_eps) {
     SkinnyOut o;
     o.c32 = c32;
     o.c_lp = clp;
     o.ld = ld;
-    return launch_skinny(in, ldin, Wt, K, batch, N, K, epi, o, dt, s);
+    return launch_skinny(in, ldin, Wt, K, batch, N, K, epi, o, dt, s, norm_eps);
   };
+  // the RMSNorms before the QKV, MLP and LM-head products are fused into them (x fp32)
+  const float ne = c.norm_eps;
   for (int l = 0; l < c.depth; ++l) {
     const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
     const char* Wo = prm + ctx->layout[2 + 4 * l].offset * es;
     const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
     const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
     char* kc = (char*)cache + (size_t)l * 2 * le * es;
-    TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
-    TRY(gemv(w + D.a, d, Wqkv, 3 * hh, d, EPI_LP, nullptr, w + D.qkv, 3 * hh));
+    TRY(gemv(x, d, Wqkv, 3 * hh, d, EPI_LP, nullptr, w + D.qkv, 3 * hh, ne));
     DecodeQkArgs q;
     q.qkv = w + D.qkv; q.ldqkv = 3 * hh; q.qhat = w + D.qhat;
     q.kc = kc; q.vc = kc + le * es; q.pos = pos; q.max_len = max_len; q.status = status;
     TRY(launch_decode_qk(q, cs, batch, H, hd, c.norm_eps, dt, s));
     TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, hd, max_len, (float*)(w + D.part_o),
                            (float*)(w + D.part_ml), w + D.o, dt, s));
-    TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d));
-    TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
-    TRY(gemv(w + D.a, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F));
-    TRY(gemv(w + D.g, F, W2, d, F, EPI_RESID, x, nullptr, d));
+    TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d, 0.f));
+    TRY(gemv(x, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F, ne));
+    TRY(gemv(w + D.g, F, W2, d, F, EPI_RESID, x, nullptr, d, 0.f));
   }
-  TRY(launch_rmsnorm_fwd(x, w + D.a, r, batch, d, c.norm_eps, dt, s));
-  return gemv(w + D.a, d, prm + ctx->layout.back().offset * es, V, d, EPI_F32, logits, nullptr, V);
+  return gemv(x, d, prm + ctx->layout.back().offset * es, V, d, EPI_F32, logits, nullptr, V, ne);
 }
 
 int nc_check(nc_ctx* ctx) {
