@@ -95,12 +95,17 @@ def torch_model_loss(cfg, P, tok, tgt, ignore_index=-100):
         c = torch.complex(u[..., : hd // 2], u[..., hd // 2:]) * rot
         return torch.cat([c.real, c.imag], -1)
 
+    Hk = cfg.kv_heads
     for l in range(cfg.depth):
         a = F.rms_norm(x, (d,), eps=cfg.eps)
-        qkv = F.linear(a, P[f"layers.{l}.W_qkv"]).view(B, T, 3, H, hd).permute(2, 0, 3, 1, 4)
-        q = rotate(F.rms_norm(qkv[0], (hd,), eps=cfg.eps))
-        k = rotate(F.rms_norm(qkv[1], (hd,), eps=cfg.eps))
-        o = F.scaled_dot_product_attention(q, k, qkv[2], is_causal=True)
+        qkv = F.linear(a, P[f"layers.{l}.W_qkv"])
+        q, k, v = torch.split(qkv, [H * hd, Hk * hd, Hk * hd], dim=-1)
+        q = q.view(B, T, H, hd).transpose(1, 2)
+        k = k.view(B, T, Hk, hd).transpose(1, 2)
+        v = v.view(B, T, Hk, hd).transpose(1, 2)
+        q = rotate(F.rms_norm(q, (hd,), eps=cfg.eps))
+        k = rotate(F.rms_norm(k, (hd,), eps=cfg.eps))
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=Hk != H)
         x = x + F.linear(o.transpose(1, 2).reshape(B, T, H * hd), P[f"layers.{l}.W_o"])
         m = F.rms_norm(x, (d,), eps=cfg.eps)
         x = x + F.linear(F.relu(F.linear(m, P[f"layers.{l}.W_1"])).square(), P[f"layers.{l}.W_2"])
@@ -242,3 +247,64 @@ def test_masked_batch_is_weighted_mean_of_microbatches_and_empty_mask():
     # nothing counted: loss 0 and every gradient 0
     l0, g0 = oracle.forward_backward(TINY, params, tok, np.full_like(tgt, -1))
     assert l0 == 0.0 and all(np.all(v == 0.0) for v in g0.values())
+
+
+
+# ---------------------------------------------------------------- grouped-query attention
+GQA = oracle.derive_config(2, vocab=512, seq_len=64, d_model=256, n_heads=4, head_dim=64, d_ff=512, n_kv_heads=2)
+MQA_MICRO = oracle.derive_config(2, vocab=40, seq_len=8, d_model=64, n_heads=4, head_dim=16, d_ff=64, n_kv_heads=1)
+
+
+def test_gqa_matches_torch_sdpa_enable_gqa_autograd():
+    params, tok, tgt = make(GQA, 2, seed=12)
+    assert params["layers.0.W_qkv"].shape == ((4 + 2 * 2) * 64, 256)
+    loss, grads = oracle.forward_backward(GQA, params, tok, tgt)
+    P = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in params.items()}
+    lt = torch_model_loss(GQA, P, torch.from_numpy(tok).long(), torch.from_numpy(tgt).long())
+    lt.backward()
+    assert abs(loss - lt.item()) <= 1e-12 * abs(loss)
+    for k, v in grads.items():
+        ref = P[k].grad.numpy()
+        assert np.linalg.norm(v - ref) <= 1e-10 * np.linalg.norm(ref), k
+
+
+def test_mqa_finite_differences():
+    params, tok, tgt = make(MQA_MICRO, 2, seed=13, std=0.2)
+    loss, grads = oracle.forward_backward(MQA_MICRO, params, tok, tgt)
+    rng = np.random.default_rng(14)
+    h = 1e-5
+    for name, _ in oracle.param_shapes(MQA_MICRO):
+        d = rng.standard_normal(params[name].shape)
+        if name == "E":
+            d *= np.isin(np.arange(MQA_MICRO.vocab), tok)[:, None]
+        d /= np.linalg.norm(d)
+        pp = dict(params); pm = dict(params)
+        pp[name] = params[name] + h * d
+        pm[name] = params[name] - h * d
+        fd = (oracle.forward(MQA_MICRO, pp, tok, tgt) - oracle.forward(MQA_MICRO, pm, tok, tgt)) / (2 * h)
+        an = float(np.sum(grads[name] * d))
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    # a GQA model is the MHA model whose key/value heads are copies within each
+    # group; its key/value weight gradients are the sums over the copies
+    params, tok, tgt = make(GQA, 2, seed=15)
+    H, Hk, hd = GQA.n_heads, GQA.kv_heads, GQA.head_dim
+    G = H // Hk
+    mha = oracle.derive_config(2, vocab=512, seq_len=64, d_model=256, n_heads=4, head_dim=64, d_ff=512)
+    pm = dict(params)
+    for l in range(GQA.depth):
+        W = params[f"layers.{l}.W_qkv"]
+        q, k, v = W[:H * hd], W[H * hd:(H + Hk) * hd], W[(H + Hk) * hd:]
+        rep = lambda m: np.repeat(m.reshape(Hk, hd, -1), G, axis=0).reshape(H * hd, -1)  # noqa: E731
+        pm[f"layers.{l}.W_qkv"] = np.concatenate([q, rep(k), rep(v)])
+    lg, gg = oracle.forward_backward(GQA, params, tok, tgt)
+    lm, gm = oracle.forward_backward(mha, pm, tok, tgt)
+    assert lg == pytest.approx(lm, rel=1e-13)
+    for l in range(GQA.depth):
+        a, b = gg[f"layers.{l}.W_qkv"], gm[f"layers.{l}.W_qkv"]
+        fold = lambda m: m.reshape(Hk, G, hd, -1).sum(axis=1).reshape(Hk * hd, -1)  # noqa: E731
+        np.testing.assert_allclose(a[:H * hd], b[:H * hd], rtol=1e-10, atol=1e-16)
+        np.testing.assert_allclose(a[H * hd:(H + Hk) * hd], fold(b[H * hd:2 * H * hd]), rtol=1e-10, atol=1e-16)
+        np.testing.assert_allclose(a[(H + Hk) * hd:], fold(b[2 * H * hd:]), rtol=1e-10, atol=1e-16)
