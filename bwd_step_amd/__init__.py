@@ -38,13 +38,14 @@ class Model:
     """One nc context: configuration, parameter layout and workspace.
 
     depth drives d_model = 64*depth, n_heads = d_model/128, head_dim = 128 and
-    d_ff = 4*d_model unless overridden.
+    d_ff = 4*d_model unless overridden; n_kv_heads < n_heads gives grouped-query
+    attention.
     """
 
     def __init__(self, depth, vocab=65536, seq_len=2048, max_batch=1, dtype="bf16", d_model=0,
-                 n_heads=0, head_dim=0, d_ff=0, rope_base=10000.0, eps=1e-6, stream=None):
+                 n_heads=0, head_dim=0, d_ff=0, rope_base=10000.0, eps=1e-6, stream=None, n_kv_heads=0):
         cfg = NcConfig(depth, d_model, n_heads, head_dim, d_ff, vocab, seq_len, max_batch,
-                       rope_base, eps, _dtype_code(dtype))
+                       rope_base, eps, _dtype_code(dtype), n_kv_heads)
         h = ctypes.c_void_p()
         s = stream if stream is not None else None
         check(lib().nc_init(ctypes.byref(cfg), s, ctypes.byref(h)), "nc_init")

@@ -30,6 +30,7 @@ class NcConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
         ("seq_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
         ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
     ]
 
 

@@ -136,8 +136,8 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
   const size_t tok0 = (size_t)b * T;
 
   const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
-  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
+  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
+  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
 
   bf16x8 qf[KS];
 #pragma unroll
@@ -306,11 +306,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
   const int q0 = qb * 128;
   const int qi = q0 + wv * 32 + li;
   const size_t tok0 = (size_t)b * T;
-  const uint32_t kbytes = (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2);
-  const uint32_t vbytes = (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2);
+  const uint32_t kbytes = (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2);
+  const uint32_t vbytes = (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)(p.H / p.G) * HD) * 2);
   const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk, kbytes);
   const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv, vbytes);
-  const long colk = (long)h * HD;
+  const long colk = (long)(h / p.G) * HD;  // this query head's key/value head
 
   const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
   bf16x8 qf[KS];
@@ -514,10 +514,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
 
   const size_t tok0 = (size_t)b * T;
   const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
-                              (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)p.H * HD) * 2));
+                              (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2));
   const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv,
-                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)p.H * HD) * 2));
-  const long col = (long)h * HD;
+                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)(p.H / p.G) * HD) * 2));
+  const long col = (long)(h / p.G) * HD;  // this query head's key/value head
   const int nkv = min(T - 1, q0 + 127) / 64 + 1;  // key blocks up to the diagonal
 
   uint32_t toff_k[4], toff_v[4];
@@ -764,8 +764,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
 
   load_block(0, 0);
   load_block(1, 1);
-  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
-  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
+  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
+  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
   bf16x8 kf[KS], vn[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -966,8 +966,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_mfma(AttnArgs p) {
   (void)nkb;
 
   const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
-  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
+  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
+  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
   const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
   const float* lsep = p.lse + (size_t)bh * T;
   const float* Dp = p.Dbuf + (size_t)bh * T;
@@ -1091,8 +1091,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_mfma(AttnArgs p) {
   const size_t tok0 = (size_t)b * T;
 
   const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + h * HD;
-  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + h * HD;
+  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
+  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
   const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
 
   bf16x8 qf[KS], df[KS];
@@ -1193,8 +1193,8 @@ __global__ void __launch_bounds__(256) attn_fwd_simt(AttnArgs p, int hd) {
   float q0 = lane < hd ? to_f32(qrow[lane]) : 0.f, q1 = lane + 64 < hd ? to_f32(qrow[lane + 64]) : 0.f;
   float a0 = 0.f, a1 = 0.f, m = -INFINITY, l = 0.f;
   for (int j = 0; j <= qi; ++j) {
-    const T* kr = (const T*)p.k + (tok0 + j) * p.ldk + h * hd;
-    const T* vr = (const T*)p.v + (tok0 + j) * p.ldv + h * hd;
+    const T* kr = (const T*)p.k + (tok0 + j) * p.ldk + (h / p.G) * hd;
+    const T* vr = (const T*)p.v + (tok0 + j) * p.ldv + (h / p.G) * hd;
     float s = (lane < hd ? q0 * to_f32(kr[lane]) : 0.f) + (lane + 64 < hd ? q1 * to_f32(kr[lane + 64]) : 0.f);
     s = wave_sum(s) * sc;
     const float mn = fmaxf(m, s);
@@ -1228,8 +1228,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_simt(AttnArgs p, int hd) {
   const float sc = p.scale;
   float g0 = 0.f, g1 = 0.f;
   for (int j = 0; j <= qi; ++j) {
-    const T* kr = (const T*)p.k + (tok0 + j) * p.ldk + h * hd;
-    const T* vr = (const T*)p.v + (tok0 + j) * p.ldv + h * hd;
+    const T* kr = (const T*)p.k + (tok0 + j) * p.ldk + (h / p.G) * hd;
+    const T* vr = (const T*)p.v + (tok0 + j) * p.ldv + (h / p.G) * hd;
     const float k0 = e0 ? to_f32(kr[lane]) : 0.f, k1 = e1 ? to_f32(kr[lane + 64]) : 0.f;
     const float v0 = e0 ? to_f32(vr[lane]) : 0.f, v1 = e1 ? to_f32(vr[lane + 64]) : 0.f;
     const float s = wave_sum(q0 * k0 + q1 * k1) * sc;
@@ -1253,8 +1253,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_simt(AttnArgs p, int hd) {
   const int bh = wid / T_, b = bh / p.H, h = bh % p.H;
   const size_t tok0 = (size_t)b * T_;
   const bool e0 = lane < hd, e1 = lane + 64 < hd;
-  const T* kr = (const T*)p.k + (tok0 + kj) * p.ldk + h * hd;
-  const T* vr = (const T*)p.v + (tok0 + kj) * p.ldv + h * hd;
+  const T* kr = (const T*)p.k + (tok0 + kj) * p.ldk + (h / p.G) * hd;
+  const T* vr = (const T*)p.v + (tok0 + kj) * p.ldv + (h / p.G) * hd;
   const float k0 = e0 ? to_f32(kr[lane]) : 0.f, k1 = e1 ? to_f32(kr[lane + 64]) : 0.f;
   const float v0 = e0 ? to_f32(vr[lane]) : 0.f, v1 = e1 ? to_f32(vr[lane + 64]) : 0.f;
   const float sc = p.scale;
@@ -1320,6 +1320,46 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
     attn_bwd_dq_simt<float><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(p, hd);
     attn_bwd_dkdv_simt<float><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>(p, hd);
   }
+  NC_LAUNCH_CHECK();
+  return 0;
+}
+
+// Grouped-query attention backward: the gradient of a shared key/value head
+// is the sum over the G query heads that read it (fixed order g = 0..G-1).
+// dk_q, dv_q hold one gradient per query head; dk (fp32) and dv (element
+// type) one per key/value head.
+template <class T>
+__global__ void __launch_bounds__(256) kv_group_sum_kernel(const float* __restrict__ dk_q, long ldq_k,
+                                                           const T* __restrict__ dv_q, long ldq_v,
+                                                           float* __restrict__ dk, long ldk, T* __restrict__ dv,
+                                                           long ldv, long N, int Hk, int G, int hd) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long per = (long)Hk * hd;
+  if (i >= N * per) return;
+  const long n = i / per;
+  const int c = (int)(i - n * per);  // kv head * hd + e
+  const int hk = c / hd, e = c - hk * hd;
+  float sk = 0.f, sv = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const long col = (long)(hk * G + g) * hd + e;
+    sk += dk_q[n * ldq_k + col];
+    sv += to_f32(dv_q[n * ldq_v + col]);
+  }
+  dk[n * ldk + c] = sk;
+  dv[n * ldv + c] = from_f32<T>(sv);
+}
+
+int launch_kv_group_sum(const float* dk_q, long ldq_k, const void* dv_q, long ldq_v, float* dk, long ldk, void* dv,
+                        long ldv, long N, int Hk, int G, int hd, int dtype, hipStream_t s) {
+  const long total = N * Hk * hd;
+  if (total == 0) return 0;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (dtype == 0)
+    kv_group_sum_kernel<bf16><<<grid, 256, 0, s>>>(dk_q, ldq_k, (const bf16*)dv_q, ldq_v, dk, ldk, (bf16*)dv, ldv,
+                                                   N, Hk, G, hd);
+  else
+    kv_group_sum_kernel<float><<<grid, 256, 0, s>>>(dk_q, ldq_k, (const float*)dv_q, ldq_v, dk, ldk, (float*)dv,
+                                                    ldv, N, Hk, G, hd);
   NC_LAUNCH_CHECK();
   return 0;
 }

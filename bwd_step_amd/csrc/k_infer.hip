@@ -242,16 +242,18 @@ int launch_skinny(const void* x, long ldx, const void* W, long ldw, int M, int N
 // 2 v.  A lane owns 4 pairs as in the training kernel.
 template <class T, int HALF>
 __global__ void __launch_bounds__(256) decode_qk_kernel(DecodeQkArgs a, const float* __restrict__ cs, int B, int H,
-                                                        float eps) {
+                                                        int Hk, float eps) {
   constexpr int LPV = HALF / 4, VPW = 64 / LPV;
   const int w = blockIdx.y;
+  const int Hw = w == 0 ? H : Hk;  // heads of this tensor
   const int lane = threadIdx.x & 63;
   const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
   const int i = (lane % LPV) * 4;
-  const bool ok = vec < B * H;
-  const int b = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
-  const int hh = H * 2 * HALF;
-  const T* src = (const T*)a.qkv + (size_t)b * a.ldqkv + w * hh + h * (2 * HALF);
+  const bool ok = vec < B * Hw;
+  const int b = ok ? vec / Hw : 0, h = ok ? vec - (vec / Hw) * Hw : 0;
+  const int hh = H * 2 * HALF, hk = Hk * 2 * HALF;
+  const int col0 = w == 0 ? 0 : (w == 1 ? hh : hh + hk);  // q | k | v columns of the qkv row
+  const T* src = (const T*)a.qkv + (size_t)b * a.ldqkv + col0 + h * (2 * HALF);
   f32x4 u0{0.f, 0.f, 0.f, 0.f}, u1{0.f, 0.f, 0.f, 0.f};
   if (ok) {
     const T* s0 = src + i;
@@ -281,7 +283,7 @@ __global__ void __launch_bounds__(256) decode_qk_kernel(DecodeQkArgs a, const fl
   }
   T* dst;
   if (w == 0) dst = (T*)a.qhat + (size_t)b * hh + h * (2 * HALF);
-  else dst = (T*)(w == 1 ? a.kc : a.vc) + (((size_t)b * H + h) * a.max_len + p) * (2 * HALF);
+  else dst = (T*)(w == 1 ? a.kc : a.vc) + (((size_t)b * Hk + h) * a.max_len + p) * (2 * HALF);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     dst[i + e] = from_f32<T>(y0[e]);
@@ -289,14 +291,14 @@ __global__ void __launch_bounds__(256) decode_qk_kernel(DecodeQkArgs a, const fl
   }
 }
 
-int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int hd, float eps, int dtype,
+int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int Hk, int hd, float eps, int dtype,
                      hipStream_t s) {
   const int vpw = 64 / (hd / 8);
   const dim3 grid((B * H + 4 * vpw - 1) / (4 * vpw), 3);
 #define NC_QK(HALF)                                                                                   \
   do {                                                                                                \
-    if (dtype == 0) decode_qk_kernel<bf16, HALF><<<grid, 256, 0, s>>>(a, cs, B, H, eps);             \
-    else decode_qk_kernel<float, HALF><<<grid, 256, 0, s>>>(a, cs, B, H, eps);                       \
+    if (dtype == 0) decode_qk_kernel<bf16, HALF><<<grid, 256, 0, s>>>(a, cs, B, H, Hk, eps);         \
+    else decode_qk_kernel<float, HALF><<<grid, 256, 0, s>>>(a, cs, B, H, Hk, eps);                   \
   } while (0)
   switch (hd) {
     case 16: NC_QK(8); break;
@@ -324,7 +326,7 @@ constexpr int kDecKeys = kDecodeKeys;
 template <class T, int HD>
 __global__ void __launch_bounds__(256) decode_attn_kernel(const T* __restrict__ qhat, const T* __restrict__ kc,
                                                           const T* __restrict__ vc, const int32_t* __restrict__ pos,
-                                                          int H, int max_len, int nchunk, float scale_log2,
+                                                          int H, int Hk, int max_len, int nchunk, float scale_log2,
                                                           float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int P = V16<T>::P;
   constexpr int LPR = HD / P;                 // lanes per key row (scores)
@@ -351,7 +353,7 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(const T* __restrict__ 
   const int h = bh - b * H;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane % LPR;  // this lane's 16-byte piece of a row
-  const size_t base = (size_t)bh * max_len;
+  const size_t base = ((size_t)b * Hk + h / (H / Hk)) * max_len;  // this query head's cache head
   float qf[P];
   ld16f(qhat + (size_t)b * H * HD + h * HD + g * P, qf);
 #pragma unroll
@@ -443,7 +445,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
 
 template <class T, int HD>
 static int decode_attn_t(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H,
-                         int max_len, float* part_o, float* part_ml, void* out, hipStream_t s) {
+                         int Hk, int max_len, float* part_o, float* part_ml, void* out, hipStream_t s) {
   // a wavefront's 16 keys must be whole multiples of its per-load rows
   if constexpr ((kDecKeys / 4) % (64 / (HD / V16<T>::P)) != 0) {
     return NC_ERR_UNSUPPORTED;
@@ -451,18 +453,20 @@ static int decode_attn_t(const void* qhat, const void* kc, const void* vc, const
     const int nchunk = (max_len + kDecKeys - 1) / kDecKeys;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
     decode_attn_kernel<T, HD><<<dim3(nchunk, B * H), 256, 0, s>>>((const T*)qhat, (const T*)kc, (const T*)vc, pos,
-                                                                  H, max_len, nchunk, scale_log2, part_o, part_ml);
+                                                                  H, Hk, max_len, nchunk, scale_log2, part_o,
+                                                                  part_ml);
     decode_combine_kernel<T, HD><<<B * H, 128, 0, s>>>(part_o, part_ml, pos, max_len, nchunk, (T*)out, H);
     NC_LAUNCH_CHECK();
     return 0;
   }
 }
 
-int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int hd,
-                       int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s) {
+int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int Hk,
+                       int hd, int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s) {
+  if (Hk < 1 || H % Hk) return NC_ERR_ARG;
 #define NC_DA(HD)                                                                                    \
-  return dtype == 0 ? decode_attn_t<bf16, HD>(qhat, kc, vc, pos, B, H, max_len, part_o, part_ml, out, s) \
-                    : decode_attn_t<float, HD>(qhat, kc, vc, pos, B, H, max_len, part_o, part_ml, out, s)
+  return dtype == 0 ? decode_attn_t<bf16, HD>(qhat, kc, vc, pos, B, H, Hk, max_len, part_o, part_ml, out, s) \
+                    : decode_attn_t<float, HD>(qhat, kc, vc, pos, B, H, Hk, max_len, part_o, part_ml, out, s)
   switch (hd) {
     case 16: NC_DA(16);
     case 32: NC_DA(32);
@@ -474,39 +478,39 @@ int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const i
 }
 
 // ---------------------------------------------------------------- prefill cache fill
-// k̂ and v of rows (b, t) of the forward's qkv buffer [B*T, 3hh] (q̂, k̂
-// already normalised and rotated in place) into cache slots slot0 + b,
-// positions 0 .. T-1; 16-byte units.
+// k̂ and v of rows (b, t) of the forward's qkv buffer [B*T, H*hd + 2*Hk*hd]
+// (q̂, k̂ already normalised and rotated in place) into cache slots
+// slot0 + b, positions 0 .. T-1; 16-byte units.
 template <class E>
-__global__ void __launch_bounds__(256) cache_fill_kernel(const E* __restrict__ qkv, int T, int H, int hd,
+__global__ void __launch_bounds__(256) cache_fill_kernel(const E* __restrict__ qkv, int T, int H, int Hk, int hd,
                                                          E* __restrict__ kc, E* __restrict__ vc, int max_len,
                                                          int slot0, long units) {
   constexpr int P = V16<E>::P;
   const long u = (long)blockIdx.x * 256 + threadIdx.x;
   if (u >= units) return;
-  const int hh = H * hd, per = hh / P;
+  const int hh = H * hd, hk = Hk * hd, per = hk / P;
   const long row = u / (2 * per);
   const int rem = (int)(u - row * 2 * per);
   const int w = rem / per, e0 = (rem - w * per) * P;
   const int b = (int)(row / T), t = (int)(row - (long)b * T);
   const int h = e0 / hd, e = e0 - h * hd;
-  const E* src = qkv + row * 3 * hh + (1 + w) * hh + e0;
-  E* dst = (w ? vc : kc) + (((size_t)(slot0 + b) * H + h) * max_len + t) * hd + e;
+  const E* src = qkv + row * (hh + 2 * hk) + hh + w * hk + e0;
+  E* dst = (w ? vc : kc) + (((size_t)(slot0 + b) * Hk + h) * max_len + t) * hd + e;
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
-int launch_cache_fill(const void* qkv, int B, int T, int H, int hd, void* kc, void* vc, int max_len, int slot0,
-                      int dtype, hipStream_t s) {
+int launch_cache_fill(const void* qkv, int B, int T, int H, int Hk, int hd, void* kc, void* vc, int max_len,
+                      int slot0, int dtype, hipStream_t s) {
   const int P = dtype == 0 ? 8 : 4;
   if (hd % P) return NC_ERR_UNSUPPORTED;
-  const long units = (long)B * T * 2 * (H * hd / P);
+  const long units = (long)B * T * 2 * (Hk * hd / P);
   if (units == 0) return 0;
   const unsigned grid = (unsigned)((units + 255) / 256);
   if (dtype == 0)
-    cache_fill_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, T, H, hd, (bf16*)kc, (bf16*)vc, max_len, slot0,
-                                                  units);
+    cache_fill_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, T, H, Hk, hd, (bf16*)kc, (bf16*)vc, max_len,
+                                                  slot0, units);
   else
-    cache_fill_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, T, H, hd, (float*)kc, (float*)vc, max_len,
+    cache_fill_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, T, H, Hk, hd, (float*)kc, (float*)vc, max_len,
                                                    slot0, units);
   NC_LAUNCH_CHECK();
   return 0;

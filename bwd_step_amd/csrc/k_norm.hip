@@ -277,7 +277,8 @@ struct QkArgs {
   void* out[2];
   int ld_in[2];
   int ld_out[2];
-  float* r[2];  // [N, H]
+  float* r[2];  // [N, heads]
+  int heads[2];  // q heads, k heads (fewer with grouped-query attention)
 };
 
 // A lane owns 4 consecutive pairs (i .. i+3, i+HALF .. i+HALF+3), so a
@@ -297,8 +298,9 @@ __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(QkArgs a, const fl
   const int lane = threadIdx.x & 63;
   const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
   const int i = (lane % LPV) * 4;
-  const bool ok = vec < N * H;
-  const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
+  const int Hw = a.heads[w];  // heads of this tensor (H >= Hw sizes the grid)
+  const bool ok = vec < N * Hw;
+  const int n = ok ? vec / Hw : 0, h = ok ? vec - (vec / Hw) * Hw : 0;
   const T* src = (const T*)a.in[w] + (size_t)n * a.ld_in[w] + h * (2 * HALF);
   f32x4 u0 = ok ? load4(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 u1 = ok ? load4(src + i + HALF) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -330,6 +332,7 @@ struct QkBwdArgs {
   const float* r[2];
   void* du[2];
   int ld_du[2];
+  int heads[2];
 };
 
 template <class T, int HALF>
@@ -340,8 +343,9 @@ __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const
   const int lane = threadIdx.x & 63;
   const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
   const int i = (lane % LPV) * 4;
-  const bool ok = vec < N * H;
-  const int n = ok ? vec / H : 0, h = ok ? vec - (vec / H) * H : 0;
+  const int Hw = a.heads[w];  // heads of this tensor (H >= Hw sizes the grid)
+  const bool ok = vec < N * Hw;
+  const int n = ok ? vec / Hw : 0, h = ok ? vec - (vec / Hw) * Hw : 0;
   const int t = n % Tseq;
   const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
   const f32x4 cs01 = csp[0], cs23 = csp[1];
@@ -406,8 +410,9 @@ static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, in
 
 int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
                            void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
-                           int T, float eps, int dtype, hipStream_t s) {
+                           int T, float eps, int dtype, hipStream_t s, int Hk) {
   QkArgs a;
+  a.heads[0] = H; a.heads[1] = Hk > 0 ? Hk : H;
   a.in[0] = q_in; a.in[1] = k_in;
   a.out[0] = q_out; a.out[1] = k_out;
   a.ld_in[0] = ldq_in; a.ld_in[1] = ldk_in;
@@ -420,8 +425,9 @@ int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int l
 int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s) {
+                           hipStream_t s, int Hk) {
   QkBwdArgs a;
+  a.heads[0] = H; a.heads[1] = Hk > 0 ? Hk : H;
   a.dv[0] = dq; a.dv[1] = dk;
   a.ld_dv[0] = lddq; a.ld_dv[1] = lddk;
   a.v[0] = qh; a.v[1] = kh;

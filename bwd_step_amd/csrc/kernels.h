@@ -73,13 +73,14 @@ int launch_rmsnorm_add_fwd(float* x, const void* res, void* y, float* r, int N, 
 int launch_rmsnorm_bwd_lpdy(const void* dy, const void* y, const float* r, float* dx, void* dx_lp, int N, int d,
                             int accumulate, hipStream_t s);
 int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s);
+// q has H heads, k has Hk (0: H) heads.
 int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
                            void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
-                           int T, float eps, int dtype, hipStream_t s);
+                           int T, float eps, int dtype, hipStream_t s, int Hk = 0);
 int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s);
+                           hipStream_t s, int Hk = 0);
 
 // ---- embedding
 int launch_embed_fwd(const void* E, const int32_t* tok, float* x, int N, int d, int V, int dtype, int* status,
@@ -101,10 +102,16 @@ struct AttnArgs {
   float* dk32 = nullptr; long lddk = 0;
   void* dv = nullptr; long lddv = 0;        // grad w.r.t. v, element type
   int B = 0, H = 0, T = 0;
+  int G = 1;  // query heads per key/value head: head h reads K/V head h / G (grouped-query attention)
+              // dk32 / dv stay per query head (the caller sums each group)
   float scale = 0.f, scale_log2 = 0.f;      // set by the launchers
 };
 int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s);
+// dk (fp32 [N, Hk*hd], ld ldk) and dv (element type, ld ldv) of the key/value
+// heads = sums over each head's G query heads of dk_q / dv_q ([N, Hk*G*hd]).
+int launch_kv_group_sum(const float* dk_q, long ldq_k, const void* dv_q, long ldq_v, float* dk, long ldk, void* dv,
+                        long ldv, long N, int Hk, int G, int hd, int dtype, hipStream_t s);
 
 // ---- cross-entropy
 // A negative target leaves its row out of the loss (loss row 0, G row 0); a
@@ -153,15 +160,18 @@ struct DecodeQkArgs {
   int max_len = 0;
   int* status = nullptr;      // position outside [0, max_len): kStatusTokenRange
 };
-int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int hd, float eps, int dtype,
+// q has H heads, k and v Hk (the cache holds Hk heads)
+int launch_decode_qk(const DecodeQkArgs& a, const float* cs, int B, int H, int Hk, int hd, float eps, int dtype,
                      hipStream_t s);
 // Attention of qhat [B, hh] against cached keys 0 .. pos[b]; out [B, hh].
 // part_o: B*H*nchunk*hd floats, part_ml: B*H*nchunk*2 (nchunk = ceil(max_len / kDecodeKeys)).
 constexpr int kDecodeKeys = 64;
-int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int hd,
-                       int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s);
-int launch_cache_fill(const void* qkv, int B, int T, int H, int hd, void* kc, void* vc, int max_len, int slot0,
-                      int dtype, hipStream_t s);
+// query head h reads cache head h / (H / Hk)
+int launch_decode_attn(const void* qhat, const void* kc, const void* vc, const int32_t* pos, int B, int H, int Hk,
+                       int hd, int max_len, float* part_o, float* part_ml, void* out, int dtype, hipStream_t s);
+// qkv rows [H q heads | Hk k heads | Hk v heads]; the cache holds Hk heads
+int launch_cache_fill(const void* qkv, int B, int T, int H, int Hk, int hd, void* kc, void* vc, int max_len,
+                      int slot0, int dtype, hipStream_t s);
 
 // ---- optimizer (k_optim.hip)
 // Vectors are fp32 with 16-byte aligned starts and lengths that are multiples

@@ -61,7 +61,8 @@ struct Plan {
   size_t a1, r1, qkv, rq, rk, O, lse, m, r2, g, layer_stride;
   size_t layers_base;
   // step-global buffers
-  size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, Dbuf, rope, logits, G, loss_rows, splitk, embed_ws;
+  size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, gq_dk, gq_dv, Dbuf, rope, logits, G, loss_rows, splitk,
+      embed_ws;
   uint64_t splitk_bytes = 0;
   size_t total;
 };
@@ -130,6 +131,8 @@ int validate(nc_config* c) {
   if (c->d_ff <= 0 || c->d_ff % 64) return NC_ERR_CONFIG;
   if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return NC_ERR_CONFIG;
   if (c->n_heads < 1) return NC_ERR_CONFIG;
+  if (c->n_kv_heads == 0) c->n_kv_heads = c->n_heads;
+  if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return NC_ERR_CONFIG;
   if (c->vocab < 64 || c->vocab % 64) return NC_ERR_CONFIG;
   if (c->seq_len < 1 || c->max_batch < 1) return NC_ERR_CONFIG;
   if (!(c->rope_base > 1.f) || !(c->norm_eps > 0.f)) return NC_ERR_CONFIG;
@@ -144,6 +147,8 @@ Plan make_plan(const nc_config& c, int batch) {
   p.batch = batch;
   const size_t N = (size_t)batch * c.seq_len;
   const size_t d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff, V = c.vocab, H = c.n_heads;
+  const size_t hk = (size_t)c.n_kv_heads * c.head_dim, nq = hh + 2 * hk;  // QKV width
+  const bool grouped = c.n_kv_heads != c.n_heads;
   const size_t es = c.dtype == NC_BF16 ? 2 : 4;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o += al(bytes); return r; };
@@ -156,8 +161,11 @@ Plan make_plan(const nc_config& c, int batch) {
   p.tmp_d = take(N * d * 4);
   p.du = take(N * F * es);
   p.dO = take(N * hh * es);
-  p.dqkv = take(N * 3 * hh * es);
-  p.dqk32 = take(N * 2 * hh * 4);
+  p.dqkv = take(N * nq * es);
+  p.dqk32 = take(N * (hh + hk) * 4);
+  // grouped-query attention: per-query-head dk (fp32) and dv before the group sums
+  p.gq_dk = grouped ? take(N * hh * 4) : 0;
+  p.gq_dv = grouped ? take(N * hh * es) : 0;
   p.Dbuf = take(N * H * 4);
   p.rope = take((size_t)c.seq_len * c.head_dim * 4);
   const size_t chunk = (size_t)ce_chunk((int)N, (int)V, c.dtype);
@@ -166,7 +174,7 @@ Plan make_plan(const nc_config& c, int batch) {
   p.loss_rows = take(N * 4);
   uint64_t sk = 0;
   const int n = (int)N;
-  sk = std::max(sk, gemm_ws_bytes(3 * (int)hh, (int)d, n, c.dtype));
+  sk = std::max(sk, gemm_ws_bytes((int)nq, (int)d, n, c.dtype));
   sk = std::max(sk, gemm_ws_bytes((int)d, (int)hh, n, c.dtype));
   sk = std::max(sk, gemm_ws_bytes((int)F, (int)d, n, c.dtype));
   sk = std::max(sk, gemm_ws_bytes((int)d, (int)F, n, c.dtype));
@@ -181,9 +189,9 @@ Plan make_plan(const nc_config& c, int batch) {
   auto ltake = [&](size_t bytes) { size_t r = lo; lo += al(bytes); return r; };
   p.a1 = ltake(N * d * es);
   p.r1 = ltake(N * 4);
-  p.qkv = ltake(N * 3 * hh * es);
+  p.qkv = ltake(N * nq * es);
   p.rq = ltake(N * H * 4);
-  p.rk = ltake(N * H * 4);
+  p.rk = ltake(N * c.n_kv_heads * 4);
   p.O = ltake(N * hh * es);
   p.lse = ltake(N * H * 4);
   p.m = ltake(N * d * es);
@@ -198,6 +206,7 @@ Plan make_plan(const nc_config& c, int batch) {
 void build_layout(nc_ctx* x) {
   const nc_config& c = x->cfg;
   const uint64_t d = c.d_model, hh = (uint64_t)c.n_heads * c.head_dim, F = c.d_ff, V = c.vocab;
+  const uint64_t hk = (uint64_t)c.n_kv_heads * c.head_dim;
   uint64_t off = 0;
   auto add = [&](const std::string& n, uint64_t r, uint64_t cl) {
     x->layout.push_back({n, off, (int)r, (int)cl});
@@ -206,7 +215,7 @@ void build_layout(nc_ctx* x) {
   add("E", V, d);
   for (int l = 0; l < c.depth; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
-    add(p + "W_qkv", 3 * hh, d);
+    add(p + "W_qkv", hh + 2 * hk, d);  // query heads, then key heads, then value heads
     add(p + "W_o", d, hh);
     add(p + "W_1", F, d);
     add(p + "W_2", d, F);
@@ -329,6 +338,7 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   hipStream_t s = ctx->stream;
   char* W = ctx->ws;
   const int N = batch * T, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
+  const int Hk = c.n_kv_heads, hk = Hk * hd, nq = hh + 2 * hk;
   const int V = c.vocab, dt = c.dtype;
   const size_t es = dt == NC_BF16 ? 2 : 4;
   const char* prm = (const char*)params;
@@ -373,15 +383,16 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     void* a1 = L + P.a1;
     char* qkv = L + P.qkv;
     TRY(norm(a1, (float*)(L + P.r1)));
-    GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, 3 * hh, d, dt);
-    g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = 3 * hh;
+    GemmCall g1 = mk(a1, d, true, Wqkv, d, true, N, nq, d, dt);
+    g1.epi = EPI_LP; g1.e.c_lp = qkv; g1.e.ld_lp = nq;
     PROF(pf, PC_GEMM, gflops(g1), gbytes(g1), launch_gemm(g1, s));
-    PROF(pf, PC_QK_FWD, 0, 4.0 * N * hh * es + 2.0 * N * H * 4, launch_qknorm_rope_fwd(qkv, 3 * hh, qkv + hh * es, 3 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
-                               (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, T, c.norm_eps, dt, s));
+    PROF(pf, PC_QK_FWD, 0, 2.0 * N * (hh + hk) * es + N * (H + Hk) * 4.0, launch_qknorm_rope_fwd(qkv, nq, qkv + hh * es, nq, qkv, nq, qkv + hh * es, nq,
+                               (float*)(L + P.rq), (float*)(L + P.rk), cs, N, H, hd, T, c.norm_eps, dt, s, Hk));
     AttnArgs a;
-    a.q = qkv; a.ldq = 3 * hh;
-    a.k = qkv + hh * es; a.ldk = 3 * hh;
-    a.v = qkv + 2 * hh * es; a.ldv = 3 * hh;
+    a.q = qkv; a.ldq = nq;
+    a.k = qkv + hh * es; a.ldk = nq;
+    a.v = qkv + (hh + hk) * es; a.ldv = nq;
+    a.G = H / Hk;
     a.o = L + P.O; a.ldo = hh;
     a.lse = (float*)(L + P.lse);
     a.B = batch; a.H = H; a.T = T;
@@ -409,6 +420,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   hipStream_t s = ctx->stream;
   char* W = ctx->ws;
   const int N = batch * c.seq_len, d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff;
+  const int Hk = c.n_kv_heads, hk = Hk * hd, nq = hh + 2 * hk;
   const int V = c.vocab, dt = c.dtype;
   const size_t es = dt == NC_BF16 ? 2 : 4;
   const char* prm = (const char*)params;
@@ -489,27 +501,37 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     PROF(pf, PC_GEMM, gflops(b6), gbytes(b6), launch_gemm(b6, s));
 
     AttnArgs a;
-    a.q = qkv; a.ldq = 3 * hh;
-    a.k = qkv + hh * es; a.ldk = 3 * hh;
-    a.v = qkv + 2 * hh * es; a.ldv = 3 * hh;
+    a.q = qkv; a.ldq = nq;
+    a.k = qkv + hh * es; a.ldk = nq;
+    a.v = qkv + (hh + hk) * es; a.ldv = nq;
     a.o = L + P.O; a.ldo = hh;
     a.dout = W + P.dO; a.lddo = hh;
     a.lse = (float*)(L + P.lse);
     a.Dbuf = (float*)(W + P.Dbuf);
-    a.dq32 = dqk32; a.lddq = 2 * hh;
-    a.dk32 = dqk32 + hh; a.lddk = 2 * hh;
-    a.dv = dqkv + 2 * hh * es; a.lddv = 3 * hh;
+    a.dq32 = dqk32; a.lddq = hh + hk;
     a.B = batch; a.H = H; a.T = c.seq_len;
+    a.G = H / Hk;
+    if (a.G == 1) {
+      a.dk32 = dqk32 + hh; a.lddk = hh + hk;
+      a.dv = dqkv + (hh + hk) * es; a.lddv = nq;
+    } else {  // per query head first, then the sums over each group
+      a.dk32 = (float*)(W + P.gq_dk); a.lddk = hh;
+      a.dv = W + P.gq_dv; a.lddv = hh;
+    }
     PROF(pf, PC_ATTN_BWD, 8.0 * hd * pairs, 0, launch_attn_bwd(a, hd, dt, s));
-    PROF(pf, PC_QK_BWD, 0, 2.0 * N * hh * (4 + 2 * es) + 2.0 * N * H * 4, launch_qknorm_rope_bwd(dqk32, 2 * hh, dqk32 + hh, 2 * hh, qkv, 3 * hh, qkv + hh * es, 3 * hh,
-                               (float*)(L + P.rq), (float*)(L + P.rk), dqkv, 3 * hh, dqkv + hh * es, 3 * hh, cs, N, H,
-                               hd, c.seq_len, dt, s));
+    if (a.G > 1)
+      PROF(pf, PC_OTHER, 0, (double)N * hh * (4 + es) + (double)N * hk * (4 + es),
+           launch_kv_group_sum((float*)(W + P.gq_dk), hh, W + P.gq_dv, hh, dqk32 + hh, hh + hk,
+                               dqkv + (hh + hk) * es, nq, N, Hk, a.G, hd, dt, s));
+    PROF(pf, PC_QK_BWD, 0, (double)N * (hh + hk) * (4 + 2 * es) + (double)N * (H + Hk) * 4, launch_qknorm_rope_bwd(dqk32, hh + hk, dqk32 + hh, hh + hk, qkv, nq, qkv + hh * es, nq,
+                               (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
+                               hd, c.seq_len, dt, s, Hk));
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
-    GemmCall b7 = mk(dqkv, 3 * hh, true, Wqkv, d, false, N, d, 3 * hh, dt);
+    GemmCall b7 = mk(dqkv, nq, true, Wqkv, d, false, N, d, nq, dt);
     dgrad_out(b7);
     PROF(pf, PC_GEMM, gflops(b7), gbytes(b7), launch_gemm(b7, s));
-    GemmCall b8 = mk(dqkv, 3 * hh, false, L + P.a1, d, false, 3 * hh, d, N, dt);
+    GemmCall b8 = mk(dqkv, nq, false, L + P.a1, d, false, nq, d, N, dt);
     b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b8), gbytes(b8), launch_gemm(b8, s));
     TRY(norm_bwd(L + P.a1, (float*)(L + P.r1)));
@@ -648,7 +670,7 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, in
 // ---------------------------------------------------------------- inference
 // KV cache: per layer K then V, each [cache_batch][H][max_len][hd].
 static uint64_t kv_layer_elems(const nc_config& c, int cache_batch, int max_len) {
-  return (uint64_t)cache_batch * c.n_heads * max_len * c.head_dim;
+  return (uint64_t)cache_batch * c.n_kv_heads * max_len * c.head_dim;
 }
 
 uint64_t nc_kv_cache_bytes(const nc_ctx* ctx, int cache_batch, int max_len) {
@@ -665,12 +687,13 @@ DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
   DecodePlan p;
   const size_t es = c.dtype == NC_BF16 ? 2 : 4;
   const size_t B = batch, d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff;
+  const size_t nq = hh + 2 * (size_t)c.n_kv_heads * c.head_dim;
   const size_t nchunk = (max_len + kDecodeKeys - 1) / kDecodeKeys;
   size_t o = 0;
   auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
   take(256);  // status block
   p.x = take(B * d * 4);
-  p.qkv = take(B * 3 * hh * es);
+  p.qkv = take(B * nq * es);
   p.qhat = take(B * hh * es);
   p.o = take(B * hh * es);
   p.g = take(B * F * es);
@@ -705,7 +728,7 @@ int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* tokens, int batch
   for (int l = 0; l < c.depth; ++l) {
     char* kc = (char*)cache + (size_t)l * 2 * le * es;
     TRY(launch_cache_fill(ctx->ws + P.layers_base + (size_t)l * P.layer_stride + P.qkv, batch, len, c.n_heads,
-                          c.head_dim, kc, kc + le * es, max_len, slot0, c.dtype, s));
+                          c.n_kv_heads, c.head_dim, kc, kc + le * es, max_len, slot0, c.dtype, s));
   }
   // logits of each sequence's last position: rows len-1, 2 len-1, ... of z
   SkinnyOut o;
@@ -727,6 +750,7 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
   if (ws_bytes < D.total) return NC_ERR_WORKSPACE;
   hipStream_t s = ctx->stream;
   const int d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff, V = c.vocab, dt = c.dtype;
+  const int Hk = c.n_kv_heads, nq = hh + 2 * Hk * hd;
   const size_t es = dt == NC_BF16 ? 2 : 4;
   char* w = (char*)workspace;
   int* status = (int*)w;
@@ -752,12 +776,12 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
     const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
     const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
     char* kc = (char*)cache + (size_t)l * 2 * le * es;
-    TRY(gemv(x, d, Wqkv, 3 * hh, d, EPI_LP, nullptr, w + D.qkv, 3 * hh, ne));
+    TRY(gemv(x, d, Wqkv, nq, d, EPI_LP, nullptr, w + D.qkv, nq, ne));
     DecodeQkArgs q;
-    q.qkv = w + D.qkv; q.ldqkv = 3 * hh; q.qhat = w + D.qhat;
+    q.qkv = w + D.qkv; q.ldqkv = nq; q.qhat = w + D.qhat;
     q.kc = kc; q.vc = kc + le * es; q.pos = pos; q.max_len = max_len; q.status = status;
-    TRY(launch_decode_qk(q, cs, batch, H, hd, c.norm_eps, dt, s));
-    TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, hd, max_len, (float*)(w + D.part_o),
+    TRY(launch_decode_qk(q, cs, batch, H, Hk, hd, c.norm_eps, dt, s));
+    TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, Hk, hd, max_len, (float*)(w + D.part_o),
                            (float*)(w + D.part_ml), w + D.o, dt, s));
     TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d, 0.f));
     TRY(gemv(x, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F, ne));

@@ -60,10 +60,13 @@ typedef enum { NC_BF16 = 0, NC_FP32 = 1 } nc_dtype;
  * Model configuration.  A zero in d_model / n_heads / head_dim / d_ff is
  * derived from `depth` by the depth dial ("nanochat explainer", How
  * dimensions are derived); a nonzero value overrides it.  Zero rope_base
- * means 10000, zero norm_eps means 1e-6.
+ * means 10000, zero norm_eps means 1e-6.  n_kv_heads (zero: n_heads) below
+ * n_heads is grouped-query attention, 1 multi-query attention ("nanochat
+ * explainer", Inference & KV Cache): query head h uses key/value head
+ * h / (n_heads / n_kv_heads), and the KV cache holds n_kv_heads heads.
  * Constraints: depth >= 1; head_dim in {16, 32, 64, 128} (the bf16 path:
  * 64 or 128); d_model, d_ff multiples of 64; vocab >= 64 and a multiple of
- * 64; seq_len >= 1; max_batch >= 1.
+ * 64; seq_len >= 1; max_batch >= 1; n_kv_heads divides n_heads.
  */
 typedef struct {
   int32_t depth;
@@ -77,13 +80,16 @@ typedef struct {
   float rope_base;
   float norm_eps;
   int32_t dtype; /* nc_dtype */
+  int32_t n_kv_heads;
 } nc_config;
 
 typedef struct nc_ctx nc_ctx;
 
 /* One parameter tensor inside the flat parameter / gradient buffers. */
 typedef struct {
-  char name[48];   /* "E", "layers.<l>.W_qkv", "layers.<l>.W_o",
+  char name[48];   /* "E", "layers.<l>.W_qkv" (rows: n_heads query heads,
+                      then n_kv_heads key heads, then n_kv_heads value
+                      heads, head_dim rows each), "layers.<l>.W_o",
                       "layers.<l>.W_1", "layers.<l>.W_2", "W_lm" */
   uint64_t offset; /* in elements from the start of the flat buffer */
   int32_t rows;    /* out features (vocab for E and W_lm) */

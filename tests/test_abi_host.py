@@ -207,6 +207,12 @@ def test_kv_cache_size_matches_the_pages_example():
     assert lib().nc_kv_cache_bytes(h, 0, g["seq"]) == 0
     assert lib().nc_kv_cache_bytes(h, 1, 70000) == 0
     assert lib().nc_decode_workspace_bytes(h, 4, 2048) > 0
+    rc, hm = init(make(depth=g["layers"], d_model=g["heads"] * g["head_dim"], n_heads=g["heads"],
+                       head_dim=g["head_dim"], vocab=512, seq_len=g["seq"], n_kv_heads=g["mqa_kv_heads"]))
+    assert rc == 0
+    assert lib().nc_kv_cache_bytes(hm, 1, g["seq"]) == g["mqa_bytes"]
+    assert g["mha_bytes"] == 16 * g["mqa_bytes"]
+    lib().nc_destroy(hm)
     fake = ctypes.c_void_p(0x1000)
     # prefill: len beyond seq_len, slots beyond the cache, no workspace
     assert lib().nc_prefill(h, fake, fake, 1, g["seq"] + 1, fake, 1, g["seq"] + 1, 0, fake) == 8
@@ -218,4 +224,26 @@ def test_kv_cache_size_matches_the_pages_example():
     assert lib().nc_decode(h, fake, fake, fake, 2, fake, 64, fake, need - 1, fake) == 3
     assert lib().nc_decode(h, fake, fake, fake, 2, fake, 64, ctypes.c_void_p(0x1010), need, fake) == 8
     assert lib().nc_decode(h, fake, fake, None, 2, fake, 64, fake, need, fake) == 2
+    lib().nc_destroy(h)
+
+
+def test_grouped_query_layout_and_config_checks():
+    cfg = oracle.derive_config(2, vocab=512, seq_len=64, d_model=256, n_heads=4, head_dim=64, d_ff=512, n_kv_heads=2)
+    rc, h = init(make(depth=2, d_model=256, n_heads=4, head_dim=64, d_ff=512, n_kv_heads=2))
+    assert rc == 0
+    out = NcConfig()
+    assert lib().nc_get_config(h, ctypes.byref(out)) == 0
+    assert out.n_kv_heads == 2
+    n = lib().nc_param_layout(h, None, 0)
+    arr = (_nc.NcTensorDesc * n)()
+    lib().nc_param_layout(h, arr, n)
+    assert [(a.name.decode(), a.rows, a.cols) for a in arr] == [(k, r, c) for k, (r, c) in oracle.param_shapes(cfg)]
+    assert lib().nc_param_count(h) == oracle.param_count(cfg)
+    lib().nc_destroy(h)
+    # n_kv_heads must divide n_heads; 0 means n_heads
+    assert init(make(depth=2, d_model=256, n_heads=4, head_dim=64, n_kv_heads=3))[0] == 1
+    rc, h = init(make(depth=2, d_model=256, n_heads=4, head_dim=64))
+    out = NcConfig()
+    lib().nc_get_config(h, ctypes.byref(out))
+    assert out.n_kv_heads == 4
     lib().nc_destroy(h)
