@@ -268,7 +268,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the data-parallel sharding across "
-              "GPUs is described in DESIGN.md but not run", file=sys.stderr)
+              "GPUs (one all-reduce of the gradients per step) is a design, not something this script runs", file=sys.stderr)
         sys.exit(2)
     if args.op:
         op_bench(args)

@@ -22,7 +22,7 @@ pages this project was built from):
   matrices, AdamW for the embedding and unembedding, cosine schedule with
   warmup, clipping at 1.0, weight decay 0.1) is in ``optim.py``.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 parameter-free RMSNorm with eps = 1e-6 inside the square root; pre-norm
 residual blocks plus one final norm before the LM head; QK-norm then RoPE
 (the order is immaterial because the rotation is orthogonal); split-half RoPE

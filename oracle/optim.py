@@ -9,7 +9,7 @@ at 1.0 and weight decay 0.1.  "Karpathy Built a Full ChatGPT Clone in 8,000
 Lines of Code" (What the Community Is Saying) attributes Muon to Bernstein,
 in Keller Jordan's implementation, and has AdamW handle the embeddings.  The
 pages give no further detail; the rest follows the optimizers' published
-descriptions and the plainest readings, each listed in the design doc:
+descriptions and the plainest readings:
 
 * groups: AdamW for E and W_lm; Muon for every weight tensor of the layers
   (W_qkv taken as one [3*H*hd, d] matrix, W_o, W_1, W_2);
