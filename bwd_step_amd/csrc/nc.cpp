@@ -543,6 +543,38 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
 
 }  // namespace
 
+namespace {
+// ---------------------------------------------------------------- inference
+// KV cache: per layer K then V, each [cache_batch][H][max_len][hd].
+uint64_t kv_layer_elems(const nc_config& c, int cache_batch, int max_len) {
+  return (uint64_t)cache_batch * c.n_kv_heads * max_len * c.head_dim;
+}
+
+struct DecodePlan {
+  size_t x = 0, qkv = 0, qhat = 0, o = 0, g = 0, cs = 0, part_o = 0, part_ml = 0, total = 0;
+};
+DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
+  DecodePlan p;
+  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+  const size_t B = batch, d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff;
+  const size_t nq = hh + 2 * (size_t)c.n_kv_heads * c.head_dim;
+  const size_t nchunk = (max_len + kDecodeKeys - 1) / kDecodeKeys;
+  size_t o = 0;
+  auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
+  take(256);  // status block
+  p.x = take(B * d * 4);
+  p.qkv = take(B * nq * es);
+  p.qhat = take(B * hh * es);
+  p.o = take(B * hh * es);
+  p.g = take(B * F * es);
+  p.cs = take((size_t)max_len * c.head_dim * 4);
+  p.part_o = take(B * c.n_heads * nchunk * c.head_dim * 4);
+  p.part_ml = take(B * c.n_heads * nchunk * 2 * 4);
+  p.total = o;
+  return p;
+}
+}  // namespace
+
 // =================================================================== C ABI
 extern "C" {
 
@@ -667,43 +699,12 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, in
   return launch_gemm(lg, ctx->stream);
 }
 
-// ---------------------------------------------------------------- inference
-// KV cache: per layer K then V, each [cache_batch][H][max_len][hd].
-static uint64_t kv_layer_elems(const nc_config& c, int cache_batch, int max_len) {
-  return (uint64_t)cache_batch * c.n_kv_heads * max_len * c.head_dim;
-}
-
 uint64_t nc_kv_cache_bytes(const nc_ctx* ctx, int cache_batch, int max_len) {
   if (!ctx || cache_batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return 0;
   const size_t es = ctx->cfg.dtype == NC_BF16 ? 2 : 4;
   return (uint64_t)ctx->cfg.depth * 2 * kv_layer_elems(ctx->cfg, cache_batch, max_len) * es;
 }
 
-namespace {
-struct DecodePlan {
-  size_t x = 0, qkv = 0, qhat = 0, o = 0, g = 0, cs = 0, part_o = 0, part_ml = 0, total = 0;
-};
-DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
-  DecodePlan p;
-  const size_t es = c.dtype == NC_BF16 ? 2 : 4;
-  const size_t B = batch, d = c.d_model, hh = (size_t)c.n_heads * c.head_dim, F = c.d_ff;
-  const size_t nq = hh + 2 * (size_t)c.n_kv_heads * c.head_dim;
-  const size_t nchunk = (max_len + kDecodeKeys - 1) / kDecodeKeys;
-  size_t o = 0;
-  auto take = [&](size_t b) { size_t r = o; o += al(b); return r; };
-  take(256);  // status block
-  p.x = take(B * d * 4);
-  p.qkv = take(B * nq * es);
-  p.qhat = take(B * hh * es);
-  p.o = take(B * hh * es);
-  p.g = take(B * F * es);
-  p.cs = take((size_t)max_len * c.head_dim * 4);
-  p.part_o = take(B * c.n_heads * nchunk * c.head_dim * 4);
-  p.part_ml = take(B * c.n_heads * nchunk * 2 * 4);
-  p.total = o;
-  return p;
-}
-}  // namespace
 
 uint64_t nc_decode_workspace_bytes(const nc_ctx* ctx, int batch, int max_len) {
   if (!ctx || batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return 0;
