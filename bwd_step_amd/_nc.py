@@ -104,6 +104,12 @@ def lib():
     """Load libnc.so (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
+        # torch first: its HIP runtime must be the one libnc.so binds to, or the
+        # streams and memory torch hands over belong to another runtime
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with bwd_step_amd/build.py "
                               "(or __graft_entry__.build())")

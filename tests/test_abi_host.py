@@ -247,3 +247,17 @@ def test_grouped_query_layout_and_config_checks():
     lib().nc_get_config(h, ctypes.byref(out))
     assert out.n_kv_heads == 4
     lib().nc_destroy(h)
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    # loading libnc.so before torch would bind it to another libamdhip64 than
+    # the one torch's streams and allocations belong to; lib() imports torch first
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from bwd_step_amd import _nc\n"
+            "_nc.lib()\n"
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
