@@ -127,6 +127,27 @@ def test_gemm_split_k_bf16(ak, bk):
     assert rel_l2(to_np(C), ref) < 1e-5
 
 
+@pytest.mark.parametrize("ak,bk", [(1, 1), (1, 0)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 704), (4104, 4360, 640), (264, 136, 9280)])
+def test_gemm_pair_loop_bf16(ak, bk, M, N, K):
+    # Both operands k-contiguous with K a multiple of 64 of at least 640: the
+    # 64-deep pair loop (ak=1, bk=0 runs the 32-deep loop on the same shapes).
+    # Ragged M and N; 306 tiles (some workgroups run two, the second
+    # prefetched under the first); K = 9280 splits over K into chunks of 1152
+    # with a last chunk of one pair.
+    banner(f"gemm pair loop ak={ak} bk={bk} {M}x{N}x{K}")
+    A = prep(synth.normal((M, K), 2, 44), "bf16")
+    B = prep(synth.normal((N, K), 2, 45), "bf16")
+    Ast = A if ak else np.ascontiguousarray(A.T)
+    Bst = B if bk else np.ascontiguousarray(B.T)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    C = ops.gemm(to_dev(Ast, "bf16"), ak, to_dev(Bst, "bf16"), bk, M, N, K)
+    assert rel_l2(to_np(C), ref) < 1e-5
+    C0 = synth.normal((M, N), 1, 46)
+    C1 = ops.gemm(to_dev(Ast, "bf16"), ak, to_dev(Bst, "bf16"), bk, M, N, K, C=to_dev(C0), beta=1)
+    assert rel_l2(to_np(C1), ref + C0) < 1e-5
+
+
 # ------------------------------------------------------------------ attention
 def attention_oracle(q, k, v, do, base, eps):
     """q, k, v, do: [B, T, H, hd] float64 -> out, dq, dk, dv in the same layout."""
