@@ -646,6 +646,66 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       for (int q = q0; q < q0 + nq; ++q) dma_lds(rs, voff, s0 + (uint32_t)q * sq, m0 + (uint32_t)q * 4096u);
     };
 
+    // bf16 epilogue staged through LDS (16 KB per wavefront at element offset
+    // e): each half of the wavefront's 128 x 128 block (64 rows) is written
+    // as 8-byte pieces in the accumulator layout, then read back as 16-byte
+    // row chunks, so that every store covers four 256-byte row segments
+    // (whole 128-byte lines) instead of 32 rows x 16 bytes.  The 16-byte
+    // chunk index of row r is XOR-ed with r & 15.  A barrier at the end lets
+    // the next loads into these slots go ahead.
+    auto epilogue_lds = [&](const Item& I, int e) {
+      bf16* st = ring + e;
+      // the swizzle term, opaque to the compiler so that the sixteen staging
+      // addresses are formed here rather than hoisted out of the loop (where
+      // they would occupy registers for the whole kernel)
+      int sw = lane & 15, sx = (lane & 15) ^ (lane >> 4);
+      asm volatile("" : "+v"(sw), "+v"(sx));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+          const int a = 2 * hf + a2;
+          const int r = a2 * 32 + (lane & 31);
+#pragma unroll
+          for (int c = 0; c < FN; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+              if constexpr (EPI == EPI_RELU2) {
+                const f32x4 rl{fmaxf(v.x, 0.f), fmaxf(v.y, 0.f), fmaxf(v.z, 0.f), fmaxf(v.w, 0.f)};
+                v = rl * rl;
+              }
+              const int ch = (4 * c + q) ^ sw;  // r & 15 == lane & 15
+              *reinterpret_cast<u32x2*>(st + r * 128 + ch * 8 + 4 * (lane >> 5)) =
+                  u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          if ((t & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // four reads and stores in flight
+          const int r = 4 * t + (lane >> 4), ch = lane & 15;
+          // r & 15 = 4 (t & 3) + lane / 16, so ch ^ (r & 15) = sx ^ 4 (t & 3)
+          const u32x4 w = *reinterpret_cast<const u32x4*>(st + r * 128 + ((sx ^ (4 * (t & 3))) << 3));
+          const long i = I.m0 + wm * TM + hf * 64 + r;
+          const long j = I.n0 + wn * TN + ch * 8;
+          bf16* dst = (bf16*)p.e.c_lp + i * p.e.ld_lp + j;
+          if (i < p.M) {
+            if (j + 8 <= p.N) {
+              *reinterpret_cast<u32x4*>(dst) = w;
+            } else if (j < p.N) {
+              *reinterpret_cast<u32x2*>(dst) = u32x2{w.x, w.y};  // N is a multiple of 4
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
     int it = wfirst;
     Item ci = item(it);
     int nit = it + G;
@@ -694,9 +754,15 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
         mstep(fa1, fb1);
         cs = cs >= 3 ? cs - 3 : cs + 2;
       }
-      if constexpr (EPI == EPI_CE) epilogue_ce(ci);
-      else if constexpr (EPI == EPI_DRELU2) epilogue_drelu2(ci);
-      else epilogue(ci);
+      if constexpr (EPI == EPI_LP || EPI == EPI_RELU2) {
+        // the two slots of the pair just finished are free until the next
+        // item's first pair loads into them
+        epilogue_lds(ci, slot_el(wv < 2 ? cs + 3 : cs + 4) + (wv & 1) * 8192);
+      } else if constexpr (EPI == EPI_CE) {
+        epilogue_ce(ci);
+      } else {
+        epilogue(ci);
+      }
       if (!has_next) break;
       it = nit;
       ci = nx;
