@@ -706,6 +706,60 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
+    // ReLU² backward staged the same way: the fp32 dg of one 32-row block
+    // ([32][128] floats, 16 KB per wavefront, 16-byte chunk XOR row & 15) is
+    // read back as four consecutive columns per lane, two rows per
+    // instruction, and combined with g loaded in that layout (one block
+    // ahead); du goes out as 8-byte pieces that cover two 256-byte row
+    // segments per instruction.
+    auto epilogue_drelu2_lds = [&](const Item& I, int e) {
+      float* st = reinterpret_cast<float*>(ring + e);
+      // opaque swizzle terms (see epilogue_lds)
+      int sw = (lane & 15) ^ (lane >> 5), sy = (lane & 31) ^ (lane >> 5);
+      asm volatile("" : "+v"(sw), "+v"(sy));
+      const int jl = I.n0 + wn * TN + 4 * (lane & 31);
+      u32x2 gv[2][16];
+      auto load_g = [&](int a, u32x2 (&dst)[16]) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const long i = I.m0 + wm * TM + a * 32 + 2 * t + (lane >> 5);
+          dst[t] = (i < p.M && jl < p.N)
+                       ? *reinterpret_cast<const u32x2*>((const bf16*)p.e.aux + i * p.e.ld_aux + jl)
+                       : u32x2{0u, 0u};
+        }
+      };
+      load_g(0, gv[0]);
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        if (a + 1 < FM) load_g(a + 1, gv[(a + 1) & 1]);
+        // row lane & 31, chunk (8 c + 2 q + lane / 32) ^ (row & 15) = (8 c + 2 q) ^ sw
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(st + (lane & 31) * 128 + (((8 * c + 2 * q) ^ sw) << 2)) =
+                f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          if ((t & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+          // row 2 t + lane / 32, chunk (lane & 31) ^ (row & 15) = sy ^ (2 t & 14)
+          const int r = 2 * t + (lane >> 5);
+          const f32x4 dg = *reinterpret_cast<const f32x4*>(st + r * 128 + ((sy ^ ((2 * t) & 14)) << 2));
+          const u32x2 w = gv[a & 1][t];
+          const f32x4 g{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
+          const long i = I.m0 + wm * TM + a * 32 + r;
+          if (i < p.M && jl < p.N) store4((bf16*)p.e.c_lp + i * p.e.ld_lp + jl, drelu2(dg, g));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
     int it = wfirst;
     Item ci = item(it);
     int nit = it + G;
@@ -758,6 +812,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
         // the two slots of the pair just finished are free until the next
         // item's first pair loads into them
         epilogue_lds(ci, slot_el(wv < 2 ? cs + 3 : cs + 4) + (wv & 1) * 8192);
+      } else if constexpr (EPI == EPI_DRELU2) {
+        epilogue_drelu2_lds(ci, slot_el(wv < 2 ? cs + 3 : cs + 4) + (wv & 1) * 8192);
       } else if constexpr (EPI == EPI_CE) {
         epilogue_ce(ci);
       } else {
@@ -891,6 +947,35 @@ __global__ void __launch_bounds__(256) gemm_simt_kernel(GemmParams p) {
       const long i = m0 + ty * 4 + x, j = n0 + tx * 4 + y;
       if (i < p.M && j < p.N) epi_apply<EPI, float>(p.e, split, i + (long)bb * p.M, j, acc[x][y]);
     }
+}
+
+// ------------------------------------------------------------------ transpose
+// 64 x 64 tiles through LDS (rows padded by one 4-byte word); each thread
+// moves 16 elements.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16* __restrict__ src, int R, int C, long lds,
+                                                             bf16* __restrict__ dst, long ldd) {
+  __shared__ bf16 tile[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + ty * 16 + k, c = c0 + tx;
+    if (r < R && c < C) tile[ty * 16 + k][tx] = src[(size_t)r * lds + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + ty * 16 + k, r = r0 + tx;
+    if (r < R && c < C) dst[(size_t)c * ldd + r] = tile[tx][ty * 16 + k];
+  }
+}
+
+int launch_transpose_bf16(const void* src, int R, int C, long lds, void* dst, long ldd, hipStream_t s) {
+  if (R <= 0 || C <= 0) return 0;
+  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+  transpose_bf16_kernel<<<grid, 256, 0, s>>>((const bf16*)src, R, C, lds, (bf16*)dst, ldd);
+  NC_LAUNCH_CHECK();
+  return 0;
 }
 
 // ------------------------------------------------------------------ split-K reduce

@@ -59,6 +59,9 @@ struct GemmCall {
   bool sym = false;
 };
 
+// dst[c][r] = src[r][c] for a bf16 matrix of R rows and C columns (row
+// strides lds, ldd in elements).
+int launch_transpose_bf16(const void* src, int R, int C, long lds, void* dst, long ldd, hipStream_t s);
 int launch_gemm(const GemmCall& g, hipStream_t s);
 int gemm_splits(int M, int N, int K, int dtype);
 uint64_t gemm_ws_bytes(int M, int N, int K, int dtype);

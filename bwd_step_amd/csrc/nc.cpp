@@ -61,6 +61,7 @@ struct Plan {
   size_t a1, r1, qkv, rq, rk, O, lse, m, r2, g, layer_stride;
   size_t layers_base;
   // step-global buffers
+  size_t w2t = 0;  // bf16: W_2 transposed ([F][d]), rewritten per layer in the backward
   size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, gq_dk, gq_dv, Dbuf, rope, logits, G, loss_rows, splitk,
       embed_ws;
   uint64_t splitk_bytes = 0;
@@ -160,6 +161,7 @@ Plan make_plan(const nc_config& c, int batch) {
   p.dx_lp = take(N * d * es);
   p.tmp_d = take(N * d * 4);
   p.du = take(N * F * es);
+  p.w2t = c.dtype == NC_BF16 ? take(F * d * 2) : 0;
   p.dO = take(N * hh * es);
   p.dqkv = take(N * nq * es);
   p.dqk32 = take(N * (hh + hk) * 4);
@@ -478,7 +480,13 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     float* dqk32 = (float*)(W + P.dqk32);
 
     // MLP: du = (dx W_2) * 2 relu(u), with relu(u) = sqrt(g); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
+    // bf16: the product reads W_2 transposed, so that both operands are
+    // k-contiguous (the pair loop and its staged ReLU²-backward epilogue)
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
+    if (dt == NC_BF16) {
+      TRY(launch_transpose_bf16(W2, d, F, F, W + P.w2t, d, s));
+      b1 = mk(dx_lp, d, true, W + P.w2t, d, true, N, F, d, dt);
+    }
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.g; b1.e.ld_aux = F;
     PROF(pf, PC_GEMM, gflops(b1), gbytes(b1), launch_gemm(b1, s));
     GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
