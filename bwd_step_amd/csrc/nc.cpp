@@ -61,7 +61,7 @@ struct Plan {
   size_t a1, r1, qkv, rq, rk, O, lse, m, r2, g, layer_stride;
   size_t layers_base;
   // step-global buffers
-  size_t w2t = 0;  // bf16: W_2 transposed ([F][d]), rewritten per layer in the backward
+  size_t wT = 0;  // bf16: one weight matrix transposed, rewritten before each input-gradient product
   size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, gq_dk, gq_dv, Dbuf, rope, logits, G, loss_rows, splitk,
       embed_ws;
   uint64_t splitk_bytes = 0;
@@ -161,7 +161,7 @@ Plan make_plan(const nc_config& c, int batch) {
   p.dx_lp = take(N * d * es);
   p.tmp_d = take(N * d * 4);
   p.du = take(N * F * es);
-  p.w2t = c.dtype == NC_BF16 ? take(F * d * 2) : 0;
+  p.wT = c.dtype == NC_BF16 ? take(std::max(std::max(F * d, d * hh), nq * d) * 2) : 0;
   p.dO = take(N * hh * es);
   p.dqkv = take(N * nq * es);
   p.dqk32 = take(N * (hh + hk) * 4);
@@ -484,8 +484,8 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     // k-contiguous (the pair loop and its staged ReLU²-backward epilogue)
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
     if (dt == NC_BF16) {
-      TRY(launch_transpose_bf16(W2, d, F, F, W + P.w2t, d, s));
-      b1 = mk(dx_lp, d, true, W + P.w2t, d, true, N, F, d, dt);
+      TRY(launch_transpose_bf16(W2, d, F, F, W + P.wT, d, s));
+      b1 = mk(dx_lp, d, true, W + P.wT, d, true, N, F, d, dt);
     }
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.g; b1.e.ld_aux = F;
     PROF(pf, PC_GEMM, gflops(b1), gbytes(b1), launch_gemm(b1, s));
@@ -493,6 +493,10 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
     PROF(pf, PC_GEMM, gflops(b2), gbytes(b2), launch_gemm(b2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
+    if (dt == NC_BF16) {
+      TRY(launch_transpose_bf16(W1, F, d, d, W + P.wT, F, s));
+      b3 = mk(W + P.du, F, true, W + P.wT, F, true, N, d, F, dt);
+    }
     dgrad_out(b3);
     PROF(pf, PC_GEMM, gflops(b3), gbytes(b3), launch_gemm(b3, s));
     GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
@@ -502,6 +506,10 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
 
     // attention output projection: dO = dx W_o; dW_o = dx^T O
     GemmCall b5 = mk(dx_lp, d, true, Wo, hh, false, N, hh, d, dt);
+    if (dt == NC_BF16) {
+      TRY(launch_transpose_bf16(Wo, d, hh, hh, W + P.wT, d, s));
+      b5 = mk(dx_lp, d, true, W + P.wT, d, true, N, hh, d, dt);
+    }
     b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
     PROF(pf, PC_GEMM, gflops(b5), gbytes(b5), launch_gemm(b5, s));
     GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
@@ -537,6 +545,10 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
     GemmCall b7 = mk(dqkv, nq, true, Wqkv, d, false, N, d, nq, dt);
+    if (dt == NC_BF16) {
+      TRY(launch_transpose_bf16(Wqkv, nq, d, d, W + P.wT, nq, s));
+      b7 = mk(dqkv, nq, true, W + P.wT, nq, true, N, d, nq, dt);
+    }
     dgrad_out(b7);
     PROF(pf, PC_GEMM, gflops(b7), gbytes(b7), launch_gemm(b7, s));
     GemmCall b8 = mk(dqkv, nq, false, L + P.a1, d, false, nq, d, N, dt);
