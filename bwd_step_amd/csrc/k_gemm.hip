@@ -950,13 +950,33 @@ __global__ void __launch_bounds__(256) gemm_simt_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------ transpose
-// 64 x 64 tiles through LDS (rows padded by one 4-byte word); each thread
-// moves 16 elements.
+// 64 x 64 tiles through LDS.  Full tiles with 16-byte aligned rows move
+// 16-byte pieces (a thread loads two 8-element row chunks and stores two
+// 8-element chunks of a transposed row); edge tiles move single elements.
 __global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16* __restrict__ src, int R, int C, long lds,
-                                                             bf16* __restrict__ dst, long ldd) {
-  __shared__ bf16 tile[64][66];
+                                                             bf16* __restrict__ dst, long ldd, int vec) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  if (vec && r0 + 64 <= R && c0 + 64 <= C) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = t / 8 + 32 * k, ch = t % 8;
+      *reinterpret_cast<u32x4*>(&tile[r][ch * 8]) =
+          *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + r) * lds + c0 + ch * 8);
+    }
+    __syncthreads();
+    const int c = t / 4, rb = (t % 4) * 16;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[rb + 8 * k + e][c];
+      *reinterpret_cast<u32x4*>(dst + (size_t)(c0 + c) * ldd + r0 + rb + 8 * k) = __builtin_bit_cast(u32x4, v);
+    }
+    return;
+  }
+  const int tx = t & 63, ty = t >> 6;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int r = r0 + ty * 16 + k, c = c0 + tx;
@@ -973,7 +993,8 @@ __global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16* __restr
 int launch_transpose_bf16(const void* src, int R, int C, long lds, void* dst, long ldd, hipStream_t s) {
   if (R <= 0 || C <= 0) return 0;
   dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-  transpose_bf16_kernel<<<grid, 256, 0, s>>>((const bf16*)src, R, C, lds, (bf16*)dst, ldd);
+  const int vec = ((uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && lds % 8 == 0 && ldd % 8 == 0) ? 1 : 0;
+  transpose_bf16_kernel<<<grid, 256, 0, s>>>((const bf16*)src, R, C, lds, (bf16*)dst, ldd, vec);
   NC_LAUNCH_CHECK();
   return 0;
 }
