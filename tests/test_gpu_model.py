@@ -65,12 +65,17 @@ def compare(cfg, dt, loss, grads, shapes, ref_loss, ref_grads):
 
 TINY = oracle.derive_config(2, vocab=512, seq_len=64, d_model=128, n_heads=2, head_dim=64, d_ff=512)
 RAGGED = oracle.derive_config(3, vocab=576, seq_len=100, d_model=192, n_heads=3, head_dim=64, d_ff=320)
+# d = 640, d_ff = 2560: every bf16 product with a k-contiguous A runs the
+# 64-deep pair loop (the forward ones, the LM-head logits, the input
+# gradients on transposed weights), with ragged row tiles (272 tokens) and a
+# ragged LM-head column tile (V = 1088)
+MID = oracle.derive_config(2, vocab=1088, seq_len=136, d_model=640, n_heads=5, head_dim=128, d_ff=2560)
 
 
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
-@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3)])
+@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3), ("mid", 2)])
 def test_step_matches_oracle_small(dt, which, B):
-    cfg = TINY if which == "tiny" else RAGGED
+    cfg = {"tiny": TINY, "ragged": RAGGED, "mid": MID}[which]
     banner(f"step {which} {dt} B={B}")
     model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, dt)
     loss, grads = run_step(model, flat, tok_d, tgt_d)
