@@ -161,7 +161,7 @@ Plan make_plan(const nc_config& c, int batch) {
   p.dx_lp = take(N * d * es);
   p.tmp_d = take(N * d * 4);
   p.du = take(N * F * es);
-  p.wT = c.dtype == NC_BF16 ? take(std::max(std::max(F * d, d * hh), nq * d) * 2) : 0;
+  p.wT = c.dtype == NC_BF16 ? take(std::max(std::max(std::max(F * d, d * hh), nq * d), V * d) * 2) : 0;
   p.dO = take(N * hh * es);
   p.dqkv = take(N * nq * es);
   p.dqk32 = take(N * (hh + hk) * 4);
@@ -296,13 +296,16 @@ GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, 
 // dW (fp32 [V,d]; overwritten or accumulated).  G and the scratch `aux`
 // (ce_aux_bytes) are chunk-sized.  bf16: the logits GEMM writes bf16 logits
 // into G with the softmax partials (EPI_CE), ce_finish turns them into G in
-// place; fp32: fp32 logits, then ce_rows.
+// place; fp32: fp32 logits, then ce_rows.  wT (bf16, optional, V*d
+// elements): W is transposed into it once so that dz = G W reads both
+// operands k-contiguous.
 int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss_rows, float* dz,
               float* dW, int accumulate, int dtype, float* aux, void* G, float* splitk, uint64_t splitk_bytes,
-              int* status, hipStream_t s, Prof* pf) {
+              int* status, hipStream_t s, Prof* pf, void* wT = nullptr) {
   const size_t es = dtype == NC_BF16 ? 2 : 4;
   const int nseg = (V + 127) / 128;
   const int chunk = ce_chunk(N, V, dtype);
+  if (wT && dtype == NC_BF16) TRY(launch_transpose_bf16(W, V, d, d, wT, V, s));
   for (int c0 = 0; c0 < N; c0 += chunk) {
     const int rows = std::min(chunk, N - c0);
     const char* zc = (const char*)z + (size_t)c0 * d * es;
@@ -325,7 +328,8 @@ int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int 
     gw.epi = EPI_F32; gw.e.c32 = dW; gw.e.ldc = d; gw.e.beta = (c0 > 0 || accumulate) ? 1 : 0;
     gw.splitk_ws = splitk; gw.splitk_bytes = splitk_bytes;
     PROF(pf, PC_GEMM, gflops(gw), gbytes(gw), launch_gemm(gw, s));
-    GemmCall gz = mk(G, V, true, W, d, false, rows, d, V, dtype);
+    GemmCall gz = (wT && dtype == NC_BF16) ? mk(G, V, true, wT, V, true, rows, d, V, dtype)
+                                           : mk(G, V, true, W, d, false, rows, d, V, dtype);
     gz.epi = EPI_F32; gz.e.c32 = dz + (size_t)c0 * d; gz.e.ldc = d; gz.e.beta = 0;
     gz.splitk_ws = splitk; gz.splitk_bytes = splitk_bytes;
     PROF(pf, PC_GEMM, gflops(gz), gbytes(gz), launch_gemm(gz, s));
@@ -439,7 +443,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
   const double rms_bwd_bytes = (double)N * d * (4 + es + 4 + 4 + es) + N * 4.0;
   TRY(lmhead_ce(W + P.z, prm + lm.offset * es, targets, N, d, V, (float*)(W + P.loss_rows), tmp,
                 grads + lm.offset, accumulate, dt, (float*)(W + P.logits), W + P.G, splitk, P.splitk_bytes, status, s,
-                pf));
+                pf, dt == NC_BF16 ? W + P.wT : nullptr));
   PROF(pf, PC_OTHER, 0, 0, launch_loss_sum((float*)(W + P.loss_rows), N, status, s));
   if (last) PROF(pf, PC_OTHER, 0, 0, launch_loss_final(loss, status, s));
   PROF(pf, PC_RMS_BWD, 0, rms_bwd_bytes - (double)N * d * 4,
