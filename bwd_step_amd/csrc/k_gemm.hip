@@ -247,7 +247,11 @@ __device__ __forceinline__ void wait_first_slice_and_sync() {
 // blocks b = wv + 4 q (q = 0..7) of 1 KB, rows 8 b + lane / 8; the swizzle
 // of block b depends on b only through b & 1 = wv & 1, so one per-lane
 // offset serves all eight and block b adds the scalar b * 16 ld bytes.
-// Rows past the operand lie past the end of its buffer (ld >= K) and read 0.
+// The buffer range check covers the per-lane offset only, not that scalar
+// part, so no row of a pair-loop tile may lie past the operand: a tile that
+// would cross the end of M (or N) is moved back to end at the last row
+// (the operands have at least 256 rows), and its epilogue writes only the
+// rows (columns) from the unmoved tile start on, which no other tile owns.
 __device__ __forceinline__ uint32_t pair_voff(long ld, int row0, int wv, int lane) {
   const int kc = (lane & 7) ^ ((4 * (wv & 1) + (lane >> 4)) & 7);
   return (uint32_t)((((long)row0 + (lane >> 3)) * ld + kc * 8) * 2);
@@ -296,6 +300,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
 
   struct Item {
     int m0, n0, kbeg, kend, nk, split, b;
+    int mlo, nlo;  // first row / column the epilogue writes (m0, n0 unless the tile was moved back)
     bool mir;  // off-diagonal tile of a symmetric result: also stored transposed
   };
   auto item = [&](int i) {
@@ -325,6 +330,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       r.m0 = (first_m + (t % group_span) % gsize) * BM;
       r.n0 = ((t % group_span) / gsize) * BN;
       r.mir = false;
+    }
+    r.mlo = r.m0;
+    r.nlo = r.n0;
+    if constexpr (P64) {
+      // the last tile-row / tile-column ends at the operand's last row
+      r.m0 = min(r.m0, p.M - BM);
+      r.n0 = min(r.n0, p.N - BN);
     }
     r.kbeg = r.split * p.kchunk;
     r.kend = min(p.K, r.kbeg + p.kchunk);
@@ -475,7 +487,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
               }
             }
           } else {
-            if (i < p.M && j < p.N)
+            if (i < p.M && j < p.N && i >= ci.mlo && j >= ci.nlo)
               epi_apply4<EPI>(p.e, ci.split, i, j,
                               f32x4{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2],
                                     acc[a][c][4 * q + 3]});
@@ -538,10 +550,13 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     const int jw = ci.n0 + wn * TN;        // the wavefront's first column (N < 2^31)
     const int jb = jw + 4 * (lane >> 5);   // column of acc[a][c][4 q + e] is jb + 32 c + 8 q + e
     const bool full = ci.n0 + BN <= p.N;   // uniform: every column of the tile exists
+    // a moved-back tile (N a multiple of 128): a wavefront whose 128 columns
+    // precede nlo belongs to the previous tile and writes nothing
+    const bool cols_own = jw >= ci.nlo;
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
       const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
-      const bool row_ok = i < p.M;
+      const bool row_ok = i < p.M && i >= ci.mlo && cols_own;
       const int yc = (row_ok ? p.e.tgt[i] : -1) - jb;  // target column relative to jb
       bf16* crow = (bf16*)p.e.c_lp + i * p.e.ld_lp + jb;
       // pass 1: bf16 logits out, the fp32 target logit, the row maximum
@@ -690,7 +705,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
           const long i = I.m0 + wm * TM + hf * 64 + r;
           const long j = I.n0 + wn * TN + ch * 8;
           bf16* dst = (bf16*)p.e.c_lp + i * p.e.ld_lp + j;
-          if (i < p.M) {
+          if (i < p.M && i >= I.mlo && j >= I.nlo) {
             if (j + 8 <= p.N) {
               *reinterpret_cast<u32x4*>(dst) = w;
             } else if (j < p.N) {
@@ -749,7 +764,8 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
           const u32x2 w = gv[a & 1][t];
           const f32x4 g{bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y)};
           const long i = I.m0 + wm * TM + a * 32 + r;
-          if (i < p.M && jl < p.N) store4((bf16*)p.e.c_lp + i * p.e.ld_lp + jl, drelu2(dg, g));
+          if (i < p.M && jl < p.N && i >= I.mlo && jl >= I.nlo)
+            store4((bf16*)p.e.c_lp + i * p.e.ld_lp + jl, drelu2(dg, g));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1031,14 +1047,18 @@ static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, bool p64, dim3 
 // k-contiguous (the forward products and the LM-head logits; measured 5-10%
 // faster there, no gain or a loss where B is m-contiguous, whose rows are
 // already 512 bytes) with K a multiple of 64 of at least 640 and row
-// strides of at least K (rows past an operand then lie past its buffer).
-static bool use_pairs(const GemmParams& p, bool ak, bool bk) {
-  return ak && bk && p.batch == 1 && !p.sym && p.K % 64 == 0 && p.K >= 640 && p.lda >= p.K && p.ldb >= p.K;
+// strides of at least K.  Its last tile-row and tile-column are moved back
+// inside the operands, so M and N are at least 256; N is a multiple of 8
+// (whole 16-byte column chunks in the staged epilogues), of 128 for the
+// cross-entropy epilogue (whole 128-column softmax segments per wavefront).
+static bool use_pairs(const GemmParams& p, bool ak, bool bk, int epi) {
+  return ak && bk && p.batch == 1 && !p.sym && p.K % 64 == 0 && p.K >= 640 && p.lda >= p.K && p.ldb >= p.K &&
+         p.M >= 256 && p.N >= 256 && p.N % (epi == EPI_CE ? 128 : 8) == 0;
 }
 template <int EPI, bool KTAIL>
 static int launch_mfma_b(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
   if (p.batch == 1 && !p.sym) {
-    launch_mfma_k<EPI, KTAIL, false>(p, ak, bk, !KTAIL && use_pairs(p, ak, bk), grid, s);
+    launch_mfma_k<EPI, KTAIL, false>(p, ak, bk, !KTAIL && use_pairs(p, ak, bk, EPI), grid, s);
     return 0;
   }
   if constexpr (EPI == EPI_LP || EPI == EPI_AXPBY || EPI == EPI_F32) {

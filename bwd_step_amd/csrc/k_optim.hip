@@ -1,7 +1,10 @@
 // Optimizer-step kernels ("nanochat explainer", The Full Pipeline ->
-// Pretraining: Muon for the 2-D weights, AdamW for the embedding and the
-// unembedding, cosine schedule with warmup, gradient clipping at 1.0, weight
-// decay 0.1).  AdamW follows Loshchilov and Hutter's decoupled form; Muon
+// Pretraining, where the optimizer is outlined).  Settings taken from there:
+//   groups        AdamW: E, W_lm;  Muon: every layer matrix
+//   lr schedule   linear warmup, then cosine decay
+//   grad clipping global L2 norm, bound 1.0
+//   weight decay  0.1, decoupled
+// AdamW follows Loshchilov and Hutter's decoupled form; Muon
 // follows its published description (Jordan et al., 2024): Nesterov
 // momentum, then the quintic Newton-Schulz orthogonalisation of the update,
 // whose matrix products run, batched over same-shape matrices, on the MFMA

@@ -157,7 +157,7 @@ struct DecodeQkArgs {
   const void* qkv = nullptr;  // [B, 3hh]: q | k | v
   long ldqkv = 0;
   void* qhat = nullptr;       // [B, hh]
-  void* kc = nullptr;         // this layer's K cache [slot][H][max_len][hd]
+  void* kc = nullptr;         // this layer's K cache [slot][Hk][max_len][hd]
   void* vc = nullptr;         // this layer's V cache
   const int32_t* pos = nullptr;
   int max_len = 0;

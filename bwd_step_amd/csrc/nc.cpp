@@ -569,7 +569,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
 
 namespace {
 // ---------------------------------------------------------------- inference
-// KV cache: per layer K then V, each [cache_batch][H][max_len][hd].
+// KV cache: per layer K then V, each [cache_batch][n_kv_heads][max_len][hd].
 uint64_t kv_layer_elems(const nc_config& c, int cache_batch, int max_len) {
   return (uint64_t)cache_batch * c.n_kv_heads * max_len * c.head_dim;
 }
@@ -930,12 +930,15 @@ static size_t ce_ws_parts(int N, int d, int V, int dtype, size_t* off) {
   off[2] = take(chunk * V * es);
   off[3] = take((size_t)N * 4);
   off[4] = take(std::max(gemm_ws_bytes((int)chunk, d, V, dtype), gemm_ws_bytes(V, d, (int)chunk, dtype)));
+  // bf16: W transposed once, so that dz = G W reads both operands k-contiguous
+  // (the same product as in the training step)
+  off[5] = take(dtype == NC_BF16 ? (size_t)V * d * 2 : 0);
   return o;
 }
 
 uint64_t nc_lmhead_ce_workspace_bytes(int N, int d, int V, int dtype) {
   if (N < 1 || d < 8 || d % 8 || V < 8 || V % 8) return 0;
-  size_t off[5];
+  size_t off[6];
   return ce_ws_parts(N, d, V, dtype, off);
 }
 
@@ -944,7 +947,7 @@ int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, 
   if (!z || !W || !y || !loss || !dz || !dW || !workspace) return NC_ERR_NULL;
   if (N < 1 || d < 8 || d % 8 || V < 8 || V % 8) return NC_ERR_ARG;
   if (dtype != NC_BF16 && dtype != NC_FP32) return NC_ERR_ARG;
-  size_t off[5];
+  size_t off[6];
   if (ws_bytes < ce_ws_parts(N, d, V, dtype, off)) return NC_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)workspace;
@@ -954,7 +957,7 @@ int nc_lmhead_ce_fwd_bwd(const void* z, const void* W, const int32_t* y, int N, 
   float* sk = sk_bytes ? (float*)(w + off[4]) : nullptr;
   TRY(launch_count_targets(y, N, status, s));
   TRY(lmhead_ce(z, W, y, N, d, V, (float*)(w + off[3]), dz, dW, 0, dtype, (float*)(w + off[1]), w + off[2], sk,
-                sk_bytes, status, s, nullptr));
+                sk_bytes, status, s, nullptr, dtype == NC_BF16 ? w + off[5] : nullptr));
   TRY(launch_loss_sum((float*)(w + off[3]), N, status, s));
   return launch_loss_final(loss, status, s);
 }

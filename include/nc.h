@@ -172,7 +172,15 @@ int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* to
                               const int32_t* targets, int n_micro, int micro_batch,
                               float* loss, float* grads);
 
-/* Forward pass only; logits: device fp32 [batch, seq_len, vocab]. */
+/*
+ * Forward pass only ("nanochat explainer", The Full Pipeline -> Pretraining:
+ * the next-token logits the cross-entropy is taken over; Modern architecture
+ * choices: the untied LM head).  tokens: device int32 [batch, seq_len];
+ * logits: device fp32 [batch, seq_len, vocab], overwritten (caller-owned).
+ * Uses the context's workspace (nc_workspace_bytes(ctx, batch)).
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (batch outside [1, max_batch]),
+ * NC_ERR_WORKSPACE; an id outside [0, vocab) sets the status word.
+ */
 int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
                       int batch, float* logits);
 
@@ -182,7 +190,7 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens,
  * and values; decode runs one new token per sequence against them.
  *
  * Cache (caller-owned device memory, nc_kv_cache_bytes): per layer K, then
- * V, each [cache_batch][n_heads][max_len][head_dim] in the element type;
+ * V, each [cache_batch][n_kv_heads][max_len][head_dim] in the element type;
  * keys are stored QK-normalised and rotated.  Slot b of the cache holds
  * sequence b; 1 <= max_len <= 65536.
  * ------------------------------------------------------------------------ */
@@ -219,7 +227,10 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
 
 /*
  * Synchronise the context's stream, then read and clear the device status
- * word.  Returns NC_OK, NC_ERR_TOKEN_RANGE, NC_ERR_NONFINITE or NC_ERR_HIP.
+ * word.  Returns NC_OK, NC_ERR_TOKEN_RANGE (an id outside the vocabulary of
+ * "nanochat explainer", Tokenizer Training), NC_ERR_NONFINITE (the loss of
+ * The Full Pipeline -> Pretraining came out NaN or infinite) or NC_ERR_HIP.
+ * Errors: NC_ERR_NULL, NC_ERR_WORKSPACE (no workspace attached).
  */
 int nc_check(nc_ctx* ctx);
 
@@ -246,10 +257,10 @@ int nc_profile_enable(nc_ctx* ctx, int on);
 int nc_profile_read(nc_ctx* ctx, nc_prof_entry* out, int cap);
 
 /* ------------------------------------------------------------------------
- * Optimizer step ("nanochat explainer", The Full Pipeline -> Pretraining:
- * Muon for the matrix (2-D) weights, AdamW for the embedding and the
- * unembedding, a cosine learning-rate schedule with warmup, gradient
- * clipping at 1.0, weight decay 0.1).  The pages give only this outline;
+ * Optimizer step ("nanochat explainer", The Full Pipeline -> Pretraining,
+ * which outlines the optimizer; settings taken: two groups, Muon and AdamW;
+ * warmup then cosine learning-rate decay; gradient-norm bound 1.0; weight
+ * decay 0.1).  The pages give only this outline;
  * AdamW is the decoupled form of Loshchilov and Hutter, Muon follows its
  * published description (Jordan et al., 2024).  Groups: AdamW for E and
  * W_lm; Muon for every layer tensor (W_qkv as one [3*H*hd, d] matrix, W_o,

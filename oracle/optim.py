@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-What the pages fix ("nanochat explainer", The Full Pipeline -> Pretraining):
-Muon for the matrix (2-D) weights, AdamW for the embedding and the
-unembedding, a cosine learning-rate schedule with warmup, gradient clipping
-at 1.0 and weight decay 0.1.  "Karpathy Built a Full ChatGPT Clone in 8,000
+What the pages fix ("nanochat explainer", The Full Pipeline -> Pretraining),
+as settings: optimizer groups Muon (layer matrices) and AdamW (E, W_lm);
+learning rate warmed up, then cosine-decayed; global gradient-norm bound 1.0;
+weight decay 0.1.  "Karpathy Built a Full ChatGPT Clone in 8,000
 Lines of Code" (What the Community Is Saying) attributes Muon to Bernstein,
 in Keller Jordan's implementation, and has AdamW handle the embeddings.  The
 pages give no further detail; the rest follows the optimizers' published

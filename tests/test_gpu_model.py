@@ -4,9 +4,10 @@ against the float64 oracle.
 Tolerances: loss within 1e-2 relative and every gradient tensor within 3e-2
 relative L2 on the bf16 path; both within 1e-4 on the fp32 debug path.
 The tiny model is checked in full, ragged shapes exercise partial tiles, the
-depth-20 and depth-26 widths are checked at two layers and one sequence of
-2048, and the full depth-20 bench configuration is checked through properties
-that hold at any size plus oracle losses of sampled sequences.
+depth-20 and depth-26 widths are checked at two layers and at full depth
+(20 and 26 layers) on one sequence of 2048, and the full depth-20 bench
+configuration is checked through properties that hold at any size plus
+oracle losses of sampled sequences.
 """
 
 import math
@@ -68,8 +69,9 @@ RAGGED = oracle.derive_config(3, vocab=576, seq_len=100, d_model=192, n_heads=3,
 # d = 640, d_ff = 2560: every bf16 product with a k-contiguous A runs the
 # 64-deep pair loop (the forward ones, the LM-head logits, the input
 # gradients on transposed weights), with ragged row tiles (272 tokens) and a
-# ragged LM-head column tile (V = 1088)
-MID = oracle.derive_config(2, vocab=1088, seq_len=136, d_model=640, n_heads=5, head_dim=128, d_ff=2560)
+# ragged LM-head column tile (V = 1152: its last tile is moved back by one
+# 128-column softmax segment)
+MID = oracle.derive_config(2, vocab=1152, seq_len=136, d_model=640, n_heads=5, head_dim=128, d_ff=2560)
 
 
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
@@ -212,3 +214,49 @@ def test_full_depth20_one_sequence_matches_oracle(dt):
     loss, grads = run_step(model, flat, to_dev(R["tok"]), to_dev(R["tgt"]))
     worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, R["loss"], R["grads"])
     print(f"worst rel-L2 {worst}", flush=True)
+
+
+_FULL26 = {}
+
+
+def _full_depth26_reference():
+    """Oracle loss and gradients of one 2048-token sequence at full depth 26
+    (d 1664, 13 heads of 128, F 6656, V 65536), Zipf(1.1) ids (computed once)."""
+    if not _FULL26:
+        cfg = oracle.derive_config(26)
+        shapes = oracle.param_shapes(cfg)
+        params = synth.weights(shapes, seed=6, bf16=True)
+        tok, tgt = synth.zipf_tokens(1, cfg.seq_len, cfg.vocab, seed=6)
+        p64 = {k: v.astype(np.float64) for k, v in params.items()}
+        ref_loss, ref_grads = oracle.forward_backward(cfg, p64, tok, tgt)
+        _FULL26.update(cfg=cfg, shapes=shapes, params=params, tok=tok, tgt=tgt, loss=ref_loss, grads=ref_grads)
+    return _FULL26
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_full_depth26_one_sequence_matches_oracle(dt):
+    """All 26 layers at the depth-26 widths, one Zipf(1.1) sequence of 2048: every gradient tensor."""
+    banner(f"full depth-26, B=1, Zipf ids, {dt}, against the oracle")
+    R = _full_depth26_reference()
+    cfg, shapes = R["cfg"], R["shapes"]
+    model = bwd_step_amd.Model(26, max_batch=1, dtype=dt)
+    flat = to_dev(pack(R["params"], shapes), dt)
+    loss, grads = run_step(model, flat, to_dev(R["tok"]), to_dev(R["tgt"]))
+    worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, R["loss"], R["grads"])
+    print(f"worst rel-L2 {worst}", flush=True)
+
+
+def test_nonfinite_loss_status():
+    """An infinite LM-head weight makes the loss non-finite: nc_check reports
+    NC_ERR_NONFINITE (5) and clears the word."""
+    banner("step with an infinite weight: non-finite loss status")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(TINY, 1, "bf16", seed=7)
+    lm_off = [o for n, o, _, _ in model.layout() if n == "W_lm"][0]
+    flat[lm_off + 3] = float("inf")
+    loss = torch.empty((), dtype=torch.float32, device="cuda")
+    grads = torch.empty(model.param_count, dtype=torch.float32, device="cuda")
+    model.forward_backward(flat, tok_d, tgt_d, loss, grads)
+    assert model.check() == 5
+    assert not math.isfinite(loss.item())
+    assert model.check() == 0
