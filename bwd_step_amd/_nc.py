@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libnc.so")
 NC_OK = 0
 NC_BF16 = 0
 NC_FP32 = 1
+DECODE_SCRATCH_BYTES = 32 << 20  # NC_DECODE_SCRATCH_BYTES in include/nc.h
 STATUS = {
     0: "NC_OK", 1: "NC_ERR_CONFIG", 2: "NC_ERR_NULL", 3: "NC_ERR_WORKSPACE",
     4: "NC_ERR_TOKEN_RANGE", 5: "NC_ERR_NONFINITE", 6: "NC_ERR_HIP",
@@ -70,6 +71,7 @@ SIGNATURES = {
     "nc_decode_workspace_bytes": (_u64, [_vp, _i, _i]),
     "nc_prefill": (_i, [_vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp]),
     "nc_decode": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _u64, _vp]),
+    "nc_decode_static": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
     "nc_check": (_i, [_vp]),
     "nc_profile_enable": (_i, [_vp, _i]),
     "nc_profile_read": (_i, [_vp, ctypes.POINTER(NcProfEntry), _i]),

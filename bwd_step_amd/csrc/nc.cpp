@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -597,6 +598,76 @@ DecodePlan decode_plan(const nc_config& c, int batch, int max_len) {
   p.total = o;
   return p;
 }
+
+// One decode step on the buffers of plan D inside w (device), with the
+// status word at `status`; the caller has checked every argument.
+int decode_run(nc_ctx* ctx, const DecodePlan& D, const void* params, const int32_t* tokens, const int32_t* pos,
+               int batch, void* cache, int max_len, char* w, int* status, float* logits) {
+  const nc_config& c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  const int d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff, V = c.vocab, dt = c.dtype;
+  const int Hk = c.n_kv_heads, nq = hh + 2 * Hk * hd;
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  float* x = (float*)(w + D.x);
+  float* cs = (float*)(w + D.cs);
+  const char* prm = (const char*)params;
+  const uint64_t le = kv_layer_elems(c, batch, max_len);
+  TRY(launch_rope_table(cs, max_len, hd, c.rope_base, s));
+  TRY(launch_embed_fwd(prm, tokens, x, batch, d, V, dt, status, s));
+  auto gemv = [&](const void* in, long ldin, const char* Wt, int N, int K, int epi, float* c32, void* clp, long ld,
+                  float norm_eps) {
+    SkinnyOut o;
+    o.c32 = c32;
+    o.c_lp = clp;
+    o.ld = ld;
+    return launch_skinny(in, ldin, Wt, K, batch, N, K, epi, o, dt, s, norm_eps);
+  };
+  // the RMSNorms before the QKV, MLP and LM-head products are fused into them (x fp32)
+  const float ne = c.norm_eps;
+  for (int l = 0; l < c.depth; ++l) {
+    const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
+    const char* Wo = prm + ctx->layout[2 + 4 * l].offset * es;
+    const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
+    const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
+    char* kc = (char*)cache + (size_t)l * 2 * le * es;
+    TRY(gemv(x, d, Wqkv, nq, d, EPI_LP, nullptr, w + D.qkv, nq, ne));
+    DecodeQkArgs q;
+    q.qkv = w + D.qkv; q.ldqkv = nq; q.qhat = w + D.qhat;
+    q.kc = kc; q.vc = kc + le * es; q.pos = pos; q.max_len = max_len; q.status = status;
+    TRY(launch_decode_qk(q, cs, batch, H, Hk, hd, c.norm_eps, dt, s));
+    TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, Hk, hd, max_len, (float*)(w + D.part_o),
+                           (float*)(w + D.part_ml), w + D.o, dt, s));
+    TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d, 0.f));
+    TRY(gemv(x, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F, ne));
+    TRY(gemv(w + D.g, F, W2, d, F, EPI_RESID, x, nullptr, d, 0.f));
+  }
+  return gemv(x, d, prm + ctx->layout.back().offset * es, V, d, EPI_F32, logits, nullptr, V, ne);
+}
+
+// Device scratch of nc_decode_static: one array per GPU, held until the
+// process ends.  Host code never uses the symbol's name as an address (in
+// host code it is only a stand-in); the address of each device's copy comes
+// from hipGetSymbolAddress, looked up once per device (with that device
+// current) and kept.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[NC_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+int decode_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return NC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return NC_ERR_HIP;
+    g_scratch[dev] = (char*)ptr;
+  }
+  *out = g_scratch[dev];
+  return NC_OK;
+}
 }  // namespace
 
 // =================================================================== C ABI
@@ -768,51 +839,27 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
               int max_len, void* workspace, uint64_t ws_bytes, float* logits) {
   if (!ctx) return NC_ERR_NULL;
   if (!params || !tokens || !pos || !cache || !workspace || !logits) return NC_ERR_NULL;
-  const nc_config& c = ctx->cfg;
   if (batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return NC_ERR_ARG;
   if ((uintptr_t)workspace & 255) return NC_ERR_ARG;
-  const DecodePlan D = decode_plan(c, batch, max_len);
+  const DecodePlan D = decode_plan(ctx->cfg, batch, max_len);
   if (ws_bytes < D.total) return NC_ERR_WORKSPACE;
-  hipStream_t s = ctx->stream;
-  const int d = c.d_model, H = c.n_heads, hd = c.head_dim, hh = H * hd, F = c.d_ff, V = c.vocab, dt = c.dtype;
-  const int Hk = c.n_kv_heads, nq = hh + 2 * Hk * hd;
-  const size_t es = dt == NC_BF16 ? 2 : 4;
-  char* w = (char*)workspace;
-  int* status = (int*)w;
-  float* x = (float*)(w + D.x);
-  float* cs = (float*)(w + D.cs);
-  const char* prm = (const char*)params;
-  const uint64_t le = kv_layer_elems(c, batch, max_len);
-  TRY(launch_rope_table(cs, max_len, hd, c.rope_base, s));
-  TRY(launch_embed_fwd(prm, tokens, x, batch, d, V, dt, status, s));
-  auto gemv = [&](const void* in, long ldin, const char* Wt, int N, int K, int epi, float* c32, void* clp, long ld,
-                  float norm_eps) {
-    SkinnyOut o;
-    o.c32 = c32;
-    o.c_lp = clp;
-    o.ld = ld;
-    return launch_skinny(in, ldin, Wt, K, batch, N, K, epi, o, dt, s, norm_eps);
-  };
-  // the RMSNorms before the QKV, MLP and LM-head products are fused into them (x fp32)
-  const float ne = c.norm_eps;
-  for (int l = 0; l < c.depth; ++l) {
-    const char* Wqkv = prm + ctx->layout[1 + 4 * l].offset * es;
-    const char* Wo = prm + ctx->layout[2 + 4 * l].offset * es;
-    const char* W1 = prm + ctx->layout[3 + 4 * l].offset * es;
-    const char* W2 = prm + ctx->layout[4 + 4 * l].offset * es;
-    char* kc = (char*)cache + (size_t)l * 2 * le * es;
-    TRY(gemv(x, d, Wqkv, nq, d, EPI_LP, nullptr, w + D.qkv, nq, ne));
-    DecodeQkArgs q;
-    q.qkv = w + D.qkv; q.ldqkv = nq; q.qhat = w + D.qhat;
-    q.kc = kc; q.vc = kc + le * es; q.pos = pos; q.max_len = max_len; q.status = status;
-    TRY(launch_decode_qk(q, cs, batch, H, Hk, hd, c.norm_eps, dt, s));
-    TRY(launch_decode_attn(w + D.qhat, q.kc, q.vc, pos, batch, H, Hk, hd, max_len, (float*)(w + D.part_o),
-                           (float*)(w + D.part_ml), w + D.o, dt, s));
-    TRY(gemv(w + D.o, hh, Wo, d, hh, EPI_RESID, x, nullptr, d, 0.f));
-    TRY(gemv(x, d, W1, F, d, EPI_RELU2, nullptr, w + D.g, F, ne));
-    TRY(gemv(w + D.g, F, W2, d, F, EPI_RESID, x, nullptr, d, 0.f));
-  }
-  return gemv(x, d, prm + ctx->layout.back().offset * es, V, d, EPI_F32, logits, nullptr, V, ne);
+  // the status word is the workspace's first word
+  return decode_run(ctx, D, params, tokens, pos, batch, cache, max_len, (char*)workspace, (int*)workspace, logits);
+}
+
+int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* pos, int batch,
+                     void* cache, int max_len, float* logits, int* status) {
+  if (!ctx) return NC_ERR_NULL;
+  if (!params || !tokens || !pos || !cache || !logits || !status) return NC_ERR_NULL;
+  if (batch < 1 || max_len < 1 || max_len > kMaxCacheLen) return NC_ERR_ARG;
+  const DecodePlan D = decode_plan(ctx->cfg, batch, max_len);
+  if (D.total > NC_DECODE_SCRATCH_BYTES) return NC_ERR_WORKSPACE;
+  char* w = nullptr;
+  TRY(decode_scratch(&w));
+  // this call's status word starts at zero (a kernel, not a memset: the call
+  // may be captured in a graph)
+  TRY(clear_status(status, ctx->stream));
+  return decode_run(ctx, D, params, tokens, pos, batch, cache, max_len, w, status, logits);
 }
 
 int nc_check(nc_ctx* ctx) {

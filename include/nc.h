@@ -226,6 +226,28 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, const int3
               float* logits);
 
 /*
+ * nc_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same step, with the workspace replaced by a static device array of
+ * NC_DECODE_SCRATCH_BYTES owned by the library (one per GPU, held until the
+ * process ends; its address is looked up on the first call on each device).
+ * Arguments as for nc_decode, except:
+ *   status: device int32, required; cleared at the start of the call, then
+ *           set to the status bits of this call (1: a position or id out of
+ *           range), the same codes nc_op_status decodes.
+ * The call allocates nothing and never synchronises.  Calls on one GPU share
+ * its array: calls that overlap on one GPU (other streams, other threads, a
+ * graph replayed while one runs) race and must not be issued.  Run it with
+ * the device of the context's stream current.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG, NC_ERR_WORKSPACE (the step needs more than
+ * NC_DECODE_SCRATCH_BYTES: nc_decode_workspace_bytes(ctx, batch, max_len)
+ * gives its need), NC_ERR_HIP (the array's address could not be found).
+ */
+#define NC_DECODE_SCRATCH_BYTES (32u << 20)
+int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, const int32_t* pos, int batch,
+                     void* cache, int max_len, float* logits, int* status);
+
+/*
  * Synchronise the context's stream, then read and clear the device status
  * word.  Returns NC_OK, NC_ERR_TOKEN_RANGE (an id outside the vocabulary of
  * "nanochat explainer", Tokenizer Training), NC_ERR_NONFINITE (the loss of
