@@ -204,7 +204,9 @@ def op_bench(args):
     elif args.op == "attention":
         B, H, T, hd = 16, 10, 2048, 128
         q, k, v, do = (torch.randn(B, T, H, hd, device=dev, generator=g).to(torch.bfloat16) for _ in range(4))
-        fn = lambda: ops.attention_fwd_bwd(q, k, v, do)  # noqa: E731
+        from bwd_step_amd import lib
+        ws = torch.zeros(int(lib().nc_attention_workspace_bytes(B, H, T, hd, 0)), dtype=torch.uint8, device=dev)
+        fn = lambda: ops.attention_fwd_bwd(q, k, v, do, ws=ws)  # noqa: E731
         flops = 3 * 4.0 * hd * B * H * T * (T + 1) / 2  # causal model FLOPs, fwd + 2x bwd
         name = "attention fwd+bwd (QK-norm, RoPE, causal) B16 H10 T2048 hd128"
     else:

@@ -489,198 +489,149 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
       : "memory");
 }
 
-// dQ: 128 queries per workgroup, 32 per wavefront (its qh and dO fragments
-// in registers).  Blocks of 64 keys (K and V tiles, 64 rows x 256 bytes with
-// the sw2 chunk swizzle) stream through four LDS stages, loaded two blocks
-// ahead (same scheme as the dK/dV kernel below).  A block is processed as two
-// halves of 32 keys: the dS arithmetic of one half is issued together with
-// the S / dP products of the next half, then the dQ products of the half.
-__global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
-  constexpr int HD = 128, KS = 8, HB = 4;
+// The stored dS of one (b, h), lane-major.  The dK/dV kernel holds -dS^T
+// of 32 keys (a key block kw) x 32 queries (a query block qw) in one
+// wavefront as two B-operand fragments per lane: fragment t of lane
+// l = li + 32 g holds key 32 kw + li and queries 32 qw + 16 t + 4 g + {0..3},
+// 32 qw + 16 t + 8 + 4 g + {0..3}.  Each fragment is stored whole, so chunk
+// (kw, qw, t) is 1 KB with lane l's 16 bytes at byte 16 l, and a store
+// instruction writes one contiguous KB.  Chunks are ordered kw, qw, t; a
+// (b, h) takes (Tp / 32)^2 * 2 KB = Tp^2 * 2 bytes.
+__device__ __forceinline__ uint32_t ds_chunk(long Tp, int kw, int qw, int t) {
+  return (uint32_t)((((long)kw * (Tp >> 5) + qw) * 2 + t) * 1024);
+}
+
+// D = rowsum(dO * O) of every (token, head), head_dim 128: 16 lanes per row
+// (16 bytes of each operand per lane, so four whole rows per wavefront
+// load), reduced across the 16 lanes; stored [b * H + h][t] for the dK/dV
+// kernel.
+__global__ void __launch_bounds__(256) attn_bwd_D128(AttnArgs p) {
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b T + t) H + h
+  const int l = threadIdx.x & 15;
+  const long rows = (long)p.B * p.T * p.H;
+  const long n = row / p.H;
+  const int h = (int)(row - n * p.H);
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>((const bf16*)p.o + n * p.ldo + h * 128 + l * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>((const bf16*)p.dout + n * p.lddo + h * 128 + l * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s = fmaf(bf16lo_to_f32(a[w]), bf16lo_to_f32(b[w]), s);
+      s = fmaf(bf16hi_to_f32(a[w]), bf16hi_to_f32(b[w]), s);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+  if (row < rows && l == 0) {
+    const long b = n / p.T, t = n - b * p.T;
+    p.Dbuf[((size_t)b * p.H + h) * p.T + t] = s;
+  }
+}
+
+// dQ from the stored dS: dQ_t = scale sum_j dS_tj kh_j, as dQ^T = K^T dS^T.
+// The A operand is transposed out of the K tile (tr_frag); the B operand
+// comes from the dS chunks with ds_read_b64_tr_b16 (ds_frag).  The dK/dV
+// kernel stored every causal chunk (zeros above the diagonal and past T),
+// so no mask is needed here.  128 queries per workgroup (32 per wavefront),
+// 64-key blocks through two LDS stages (a K tile, 64 rows x 256 bytes with
+// the sw2 swizzle, and the 16 dS chunks of 64 keys x 128 queries): 64 KB,
+// so two workgroups share a compute unit.  The kernel streams the stored
+// dS once from HBM, which bounds it.
+//
+// In LDS the chunks are ordered (kw, qw, t) within the tile and the 16-byte
+// pieces of chunk lane li + 32 g sit at slot 32 g + (li ^ 4 g): a 16-lane
+// transposed read then covers 4 keys x 16 queries in 8 distinct 16-byte
+// bank groups.
+__device__ __forceinline__ bf16x8 ds_frag(const bf16* S, int qwl, int kb, int lane) {
+  const int gi = lane >> 4, i = lane & 15;
+  const int r = i >> 2, q = i & 3;
+  const int gq = q & 1;  // the fragment half (g of the storing lane) that holds queries 4q .. 4q+3
+  const int k0 = kb + 4 * (gi >> 1) + r;
+  auto addr = [&](int kk) {
+    const int chunk = (kk >> 5) * 8 + qwl * 2 + (gi & 1);
+    const int slot = 32 * gq + ((kk & 31) ^ (4 * gq));
+    return (LDS_AS v4i16*)(S + chunk * 512 + slot * 8 + 4 * (q >> 1));
+  };
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(k0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(k0 + 8));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
+  constexpr int HD = 128, HB = 4;
   constexpr uint32_t kTile = 64 * HD * 2, kStage = 2 * kTile;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int T = p.T;
+  const long Tp = p.tpad;
   const int nqb = gridDim.x;
   const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
   const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn, the longest first
   const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, li = lane & 31;
+  const int g = lane >> 5;
   const int q0 = qb * 128;
-  const int qi = q0 + wv * 32 + li;  // this lane's query
+  const int qi = q0 + wv * 32 + (lane & 31);  // this lane's query
 
   const size_t tok0 = (size_t)b * T;
   const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
                               (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2));
-  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv,
-                              (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)(p.H / p.G) * HD) * 2));
+  const rsrc_t rs = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
   const long col = (long)(h / p.G) * HD;  // this query head's key/value head
   const int nkv = min(T - 1, q0 + 127) / 64 + 1;  // key blocks up to the diagonal
 
-  uint32_t toff_k[4], toff_v[4];
+  // K tile: per-lane byte offsets of this wavefront's 4 blocks (4 rows each)
+  // relative to the key block's first row.  dS: this wavefront loads chunks
+  // 4 wv .. 4 wv + 3 of the tile; LDS slot `lane` of a chunk takes the
+  // stored piece of lane (li ^ 4 g) + 32 g.
+  uint32_t toff_k[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wv * 4 + i) * 4 + (lane >> 4);
     const int cc = (lane & 15) ^ sw2(row);
     toff_k[i] = (uint32_t)(((long)row * p.ldk + col + cc * 8) * 2);
-    toff_v[i] = (uint32_t)(((long)row * p.ldv + col + cc * 8) * 2);
   }
-  // loads of key block j into stage st (8 per wavefront); rows past T and
-  // blocks past the last read 0
+  const uint32_t src_lane = (uint32_t)((((lane & 31) ^ (4 * g)) + 32 * g) * 16);
   auto load_block = [&](int st, int j) {
-    const int row0 = j < nkv ? j * 64 : T;
+    const int row0 = j * 64;
     const uint32_t sb = lds0 + (uint32_t)st * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = row0 + (wv * 4 + i) * 4 + (lane >> 4) < T;
+      const bool ok = row0 + (wv * 4 + i) * 4 + (lane >> 4) < T;  // keys past T read 0
       dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 4 + i) * 1024u);
-      dma16(rv, ok ? toff_v[i] + (uint32_t)(row0 * p.ldv * 2) : kOOB, sb + kTile + (uint32_t)(wv * 4 + i) * 1024u);
+      const int c = wv * 4 + i;  // chunk (kwl, qwl, t) = (c / 8, (c / 2) % 4, c % 2)
+      dma16(rs, src_lane + ds_chunk(Tp, 2 * j + (c >> 3), (q0 >> 5) + ((c >> 1) & 3), c & 1),
+            sb + kTile + (uint32_t)c * 1024u);
     }
   };
-  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory"); };
 
-  load_block(0, 0);
-  load_block(1, 1);
-  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  const bf16* dop = (const bf16*)p.dout + tok0 * p.lddo + h * HD;
-  bf16x8 qf[KS], df[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
-    df[s] = qi < T ? *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * p.lddo + s * 16 + g * 8) : bf16x8{};
-  }
-  const float nlse = qi < T ? -p.lse[(size_t)bh * T + qi] : 0.f;  // base 2
-  // D = rowsum(dO * O) of this lane's query (lanes l and l ^ 32 hold the two
-  // halves of the row), also written for the dK/dV kernel that runs next
-  float Dl = 0.f;
-  {
-    const bf16* op = (const bf16*)p.o + tok0 * p.ldo + h * HD;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 o8 = qi < T ? *reinterpret_cast<const bf16x8*>(op + (size_t)qi * p.ldo + s * 16 + g * 8) : bf16x8{};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Dl = fmaf(to_f32(df[s][e]), to_f32(o8[e]), Dl);
-    }
-    Dl += __shfl_xor(Dl, 32, 64);
-    if (g == 0 && qi < T) p.Dbuf[(size_t)bh * T + qi] = Dl;
-  }
-  const float c = p.scale_log2;
-  // dP^T accumulators start at -D (one value per lane: its query), so they
-  // end at dP - D and dS = P (dP - D) takes one multiply
-  f32x16 negD;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) negD[r] = -Dl;
   f32x16 dq[HB];
 #pragma unroll
   for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
 
-  // S^T and dP^T of one half (kk: 32 keys) of the block in stage st.  All 16
-  // fragment reads are issued in a scheduling region of their own, ahead of
-  // the MFMAs: with one wavefront per SIMD, a read placed next to the MFMA
-  // that consumes it stalls that MFMA for the whole LDS latency.
-  auto phase_a = [&](uint32_t st, int kk, f32x16& S, f32x16& Pd) {
-    const char* sb = smem + st * kStage;
+  load_block(0, 0);
+  for (int j = 0; j < nkv; ++j) {
+    // block j landed (its loads are the only ones in flight) and every
+    // wavefront is done with the stage the next loads overwrite
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 1 < nkv) load_block((j + 1) & 1, j + 1);
+    const char* sb = smem + (j & 1) * kStage;
     const bf16* Ks = (const bf16*)sb;
-    const bf16* Vs = (const bf16*)(sb + kTile);
-    bf16x8 fk[KS], fv[KS];
+    const bf16* Ss = (const bf16*)(sb + kTile);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      fk[s] = row_frag(Ks, kk * 32 + li, 2 * s + g);
-      fv[s] = row_frag(Vs, kk * 32 + li, 2 * s + g);
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 sf = ds_frag(Ss, wv, kk * 16, lane);
+#pragma unroll
+      for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 16, lane), sf, dq[x]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    S = f32x16{};
-    Pd = negD;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      S = mfma(fk[s], qf[s], S);
-      Pd = mfma(fv[s], df[s], Pd);
-    }
-  };
-  // dS^T = P (dP - D) of one half as bf16 B operands; MASKED: causal / length mask
-  auto phase_b = [&](auto masked, const f32x16& S, const f32x16& Pd, int kh, bf16x8* sf) {
-    constexpr bool MASKED = decltype(masked)::value;
-    f32x16 dS;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pr = ex2(fmaf(S[r], c, nlse));
-      if constexpr (MASKED) {
-        const int key = kh + acc_row(r, g);
-        pr = (key > qi || key >= T) ? 0.f : pr;
-      }
-      dS[r] = pr * Pd[r];
-    }
-    sf[0] = pack8(dS, 0);
-    sf[1] = pack8(dS, 1);
-  };
-  // dQ += dS K for one half of the block in stage st
-  auto phase_c = [&](uint32_t st, int kk, const bf16x8* sf) {
-    const bf16* Ks = (const bf16*)(smem + st * kStage);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 32 + t * 16, lane), sf[t], dq[x]);
-  };
-  // Instruction interleave of one section: LEAD LDS reads first, then NM
-  // groups of one MFMA, NDS LDS reads (for later MFMAs) and NVALU vector
-  // instructions.  The lead keeps the fragment reads several MFMAs ahead of
-  // their use, so with one wavefront per SIMD an MFMA does not wait out the
-  // LDS latency of its own operand.
-  auto interleave = [&](auto nm, auto lead, auto nds, auto nvalu) {
-    if constexpr (decltype(lead)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(lead)::value, 0);
-#pragma unroll
-    for (int i = 0; i < decltype(nm)::value; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
-      if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I2 = std::integral_constant<int, 2>;
-  using I6 = std::integral_constant<int, 6>;
-  using I8 = std::integral_constant<int, 8>;
-  using I16 = std::integral_constant<int, 16>;
-
-  f32x16 Sa, Pa;  // the pending half: S^T and dP^T done, arithmetic not yet
-  auto pass = [&](auto masked, int j) {
-    const uint32_t cur = (uint32_t)j & 3u, nxt = (uint32_t)(j + 1) & 3u;
-    load_block((j + 2) & 3, j + 2);
-    const int kbase = j * 64;
-    bf16x8 sf[2];
-    f32x16 Sb, Pb;
-    __builtin_amdgcn_sched_barrier(0);
-    phase_a(cur, 1, Sb, Pb);
-    phase_b(masked, Sa, Pa, kbase, sf);
-    interleave(I16{}, I0{}, I0{}, I6{});
-    phase_c(cur, 0, sf);
-    interleave(I8{}, I6{}, I2{}, I0{});
-    wait_block_and_sync();  // block j + 1
-    phase_a(nxt, 0, Sa, Pa);
-    phase_b(masked, Sb, Pb, kbase + 32, sf);
-    interleave(I16{}, I0{}, I0{}, I6{});
-    phase_c(cur, 1, sf);
-    interleave(I8{}, I6{}, I2{}, I0{});
-  };
-
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, qh and dO
-  phase_a(0, 0, Sa, Pa);
-  // The last two blocks meet the diagonal and a block j with (j + 1) * 64 > T
-  // (j >= T / 64) meets the end, so the masked passes are a suffix.  Two
-  // loops with one pass body each keep the accumulators in one place (one
-  // loop with both bodies behind a branch moved dQ between register files
-  // on every trip).
-  const int jm = max(0, min(nkv - 2, T / 64));
-  int j = 0;
-  for (; j < jm; ++j) pass(std::false_type{}, j);
-  for (; j < nkv; ++j) pass(std::true_type{}, j);
-  wait_vmem();  // the loads of the two blocks past the end still target LDS
+  }
+  wait_vmem();
 
   if (qi >= T) return;
-  const float sc = p.scale;
+  const float sc = -p.scale;  // the stored matrix is -dS
   float* dqp = p.dq32 + (tok0 + qi) * p.lddq + h * HD;
 #pragma unroll
   for (int x = 0; x < HB; ++x)
@@ -698,7 +649,9 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq128(AttnArgs p) {
 // half is issued together with the S / dP products of the next half, then
 // the dV / dK products of the half follow.  With -V in place of V the dP
 // accumulator starts at D and ends at D - dP, so P (D - dP) = -dS comes out
-// of one multiply; the sign is restored when dK is written.
+// of one multiply; the sign is restored when dK is written.  The bf16 -dS
+// (the B operand of the dK products) is also stored, transposed ([key]
+// [query]), for the dQ kernel, so S and dP are computed once per pair.
 //
 // LDS: one array of four 36-KB stages (qh tile, dO tile: 64 rows x 256 bytes
 // with the sw2 chunk swizzle; then four 1-KB vector slots: lse (base 2), D,
@@ -757,10 +710,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
     const int t = row0 + 4 * lane;
     dma16(rv, (lane < 16 && t < T) ? (uint32_t)t * 4u : kOOB, sb + 2 * kTile + (uint32_t)wv * 1024u);
   };
-  // Loads retire in issue order: with the 9 loads of the newest block still
-  // in flight, the previous block has landed.  The barrier publishes it and
-  // orders every wavefront's reads of older stages before the next loads.
-  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory"); };
+  // Vector memory operations retire in issue order.  At this wait the ones
+  // younger than the previous block's 9 loads are the 2 + 2 dS stores of the
+  // previous pass, the 9 loads of the newest block and the 2 dS stores of
+  // this pass's first half: with at most 15 in flight the previous block has
+  // landed.  The barrier publishes it and orders every wavefront's reads of
+  // older stages before the next loads.
+  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory"); };
+  // -dS^T of one half (32 queries from q, a multiple of 32): each lane's two
+  // fragments go out whole, one 1-KB chunk per fragment (ds_chunk)
+  const long Tp = p.tpad;
+  const rsrc_t rds = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
+  const uint32_t ds_lane = (uint32_t)lane * 16u;
+  auto store_ds = [&](const bf16x8* sf, int q) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sf[t]), rds, ds_lane,
+                                             (int)ds_chunk(Tp, wk >> 5, q >> 5, t), 0);
+  };
 
   load_block(0, 0);
   load_block(1, 1);
@@ -885,12 +852,14 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
     interleave(I4{}, I0{}, I6{});
     phase_c(cur, 0, pf, sf);
     interleave(I8{}, I2{}, I0{});
+    store_ds(sf, qbase);
     wait_block_and_sync();  // block j + 1
     phase_a(nxt, 0, Sa, Pa);
     phase_b(masked, Sb, Pb, cur, 1, qbase + 32, pf, sf);
     interleave(I4{}, I0{}, I6{});
     phase_c(cur, 1, pf, sf);
     interleave(I8{}, I2{}, I0{});
+    store_ds(sf, qbase + 32);
   };
 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, K and V
@@ -1304,9 +1273,12 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
     dim3 gk((p.T + 127) / 128, p.B * p.H);
     dim3 gq((p.T + 127) / 128, p.B * p.H);
     if (hd == 128) {
-      // the dQ kernel computes D = rowsum(dO * O) for the dK/dV kernel
-      attn_bwd_dq128<<<gq, 256, 0, s>>>(p);
+      // D, then dK/dV (which stores dS), then dQ from the stored dS
+      if (!p.dsT || p.tpad != attn_ds_pad(p.T)) return NC_ERR_WORKSPACE;
+      if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
+      attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
       attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
+      attn_bwd_dq_ds128<<<gq, 256, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
       attn_bwd_dkdv_mfma<64><<<gk, 256, 0, s>>>(p);

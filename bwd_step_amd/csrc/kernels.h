@@ -108,7 +108,22 @@ struct AttnArgs {
   int G = 1;  // query heads per key/value head: head h reads K/V head h / G (grouped-query attention)
               // dk32 / dv stay per query head (the caller sums each group)
   float scale = 0.f, scale_log2 = 0.f;      // set by the launchers
+  // bf16, head_dim 128: -dS^T of every (b, h) as a [tpad][tpad] matrix (key
+  // rows, query columns), written by the dK/dV kernel and read by dQ
+  void* dsT = nullptr;
+  long tpad = 0;  // attn_ds_pad(T)
 };
+// Rows (and columns) of each (b, h) block of the stored dS: T rounded up to
+// 128.  A block is addressed through one buffer resource (32-bit offsets), so
+// T is at most kMaxDsPad on that path.
+inline long attn_ds_pad(int T) { return ((long)T + 127) / 128 * 128; }
+constexpr long kMaxDsPad = 32640;
+// Bytes of the stored dS for the attention backward (0 where none is stored).
+inline uint64_t attn_ds_bytes(int B, int H, int T, int hd, int dtype) {
+  if (dtype != 0 || hd != 128) return 0;
+  const uint64_t tp = (uint64_t)attn_ds_pad(T);
+  return (uint64_t)B * H * tp * tp * 2;
+}
 int launch_attn_fwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s);
 // dk (fp32 [N, Hk*hd], ld ldk) and dv (element type, ld ldv) of the key/value

@@ -63,8 +63,8 @@ struct Plan {
   size_t layers_base;
   // step-global buffers
   size_t wT = 0;  // bf16: one weight matrix transposed, rewritten before each input-gradient product
-  size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, gq_dk, gq_dv, Dbuf, rope, logits, G, loss_rows, splitk,
-      embed_ws;
+  size_t x, z, rf, dx, dx_lp, tmp_d, du, dO, dqkv, dqk32, gq_dk, gq_dv, Dbuf, dsT, rope, logits, G, loss_rows,
+      splitk, embed_ws;
   uint64_t splitk_bytes = 0;
   size_t total;
 };
@@ -141,6 +141,8 @@ int validate(nc_config* c) {
   if (c->dtype != NC_BF16 && c->dtype != NC_FP32) return NC_ERR_CONFIG;
   if ((uint64_t)c->max_batch * c->seq_len > (1ull << 30)) return NC_ERR_CONFIG;
   if (c->dtype == NC_BF16 && c->head_dim != 64 && c->head_dim != 128) return NC_ERR_UNSUPPORTED;
+  // the bf16 head_dim-128 attention backward stores dS per (b, h) as one [Tp][Tp] block
+  if (c->dtype == NC_BF16 && c->head_dim == 128 && attn_ds_pad(c->seq_len) > kMaxDsPad) return NC_ERR_UNSUPPORTED;
   return NC_OK;
 }
 
@@ -170,6 +172,7 @@ Plan make_plan(const nc_config& c, int batch) {
   p.gq_dk = grouped ? take(N * hh * 4) : 0;
   p.gq_dv = grouped ? take(N * hh * es) : 0;
   p.Dbuf = take(N * H * 4);
+  p.dsT = take(attn_ds_bytes(batch, (int)H, c.seq_len, c.head_dim, c.dtype));  // the attention backward's dS
   p.rope = take((size_t)c.seq_len * c.head_dim * 4);
   const size_t chunk = (size_t)ce_chunk((int)N, (int)V, c.dtype);
   p.logits = take(ce_aux_bytes(chunk, V, c.dtype));
@@ -529,6 +532,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     a.dout = W + P.dO; a.lddo = hh;
     a.lse = (float*)(L + P.lse);
     a.Dbuf = (float*)(W + P.Dbuf);
+    a.dsT = W + P.dsT; a.tpad = attn_ds_pad(c.seq_len);
     a.dq32 = dqk32; a.lddq = hh + hk;
     a.B = batch; a.H = H; a.T = c.seq_len;
     a.G = H / Hk;
@@ -922,12 +926,13 @@ static size_t attn_ws_parts(int B, int H, int T, int hd, int dtype, size_t* off)
   off[7] = take(N * hh * 4);     // dqh fp32
   off[8] = take(N * hh * 4);     // dkh fp32
   off[9] = take((size_t)T * hd * 4);  // rope table
+  off[10] = take(attn_ds_bytes(B, H, T, hd, dtype));  // dS of the backward (bf16, head_dim 128)
   return o;
 }
 
 uint64_t nc_attention_workspace_bytes(int B, int H, int T, int hd, int dtype) {
   if (B < 1 || H < 1 || T < 1 || (hd != 16 && hd != 32 && hd != 64 && hd != 128)) return 0;
-  size_t off[10];
+  size_t off[11];
   return attn_ws_parts(B, H, T, hd, dtype, off);
 }
 
@@ -940,7 +945,8 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void
     return NC_ERR_ARG;
   if (dtype != NC_BF16 && dtype != NC_FP32) return NC_ERR_ARG;
   if (dtype == NC_BF16 && hd != 64 && hd != 128) return NC_ERR_UNSUPPORTED;
-  size_t off[10];
+  if (dtype == NC_BF16 && hd == 128 && attn_ds_pad(T) > kMaxDsPad) return NC_ERR_UNSUPPORTED;
+  size_t off[11];
   if (ws_bytes < attn_ws_parts(B, H, T, hd, dtype, off)) return NC_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)workspace;
@@ -960,6 +966,7 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void
   a.dq32 = (float*)(w + off[7]); a.lddq = hh;
   a.dk32 = (float*)(w + off[8]); a.lddk = hh;
   a.dv = dv; a.lddv = hh;
+  a.dsT = w + off[10]; a.tpad = attn_ds_pad(T);
   a.B = B; a.H = H; a.T = T;
   TRY(launch_attn_fwd(a, hd, dtype, s));
   TRY(launch_attn_bwd(a, hd, dtype, s));

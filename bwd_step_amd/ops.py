@@ -98,15 +98,19 @@ def gemm(A, a_kmajor, B, b_kmajor, M, N, K, C=None, beta=0):
     return C
 
 
-def attention_fwd_bwd(q, k, v, dout, rope_base=10000.0, eps=1e-6):
-    """q, k, v, dout: [B, T, H, hd] (bf16 or fp32). Returns (out, dq, dk, dv)."""
+def attention_fwd_bwd(q, k, v, dout, rope_base=10000.0, eps=1e-6, ws=None):
+    """q, k, v, dout: [B, T, H, hd] (bf16 or fp32). Returns (out, dq, dk, dv).
+
+    ws: an optional workspace of at least nc_attention_workspace_bytes (reused
+    across calls, e.g. by a benchmark loop); one is allocated otherwise."""
     torch = _t()
     B, T, H, hd = q.shape
     dt = _code(q)
     out = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nb = int(lib().nc_attention_workspace_bytes(B, H, T, hd, dt))
-    ws = _ws(nb)
+    if ws is None or ws.numel() < nb:
+        ws = _ws(nb)
     check(lib().nc_attention_fwd_bwd(_p(q), _p(k), _p(v), _p(dout), _p(out), _p(dq), _p(dk), _p(dv), B, H, T, hd,
                                      rope_base, eps, dt, _p(ws), nb, _s()), "nc_attention_fwd_bwd")
     return out, dq, dk, dv

@@ -66,7 +66,9 @@ typedef enum { NC_BF16 = 0, NC_FP32 = 1 } nc_dtype;
  * h / (n_heads / n_kv_heads), and the KV cache holds n_kv_heads heads.
  * Constraints: depth >= 1; head_dim in {16, 32, 64, 128} (the bf16 path:
  * 64 or 128); d_model, d_ff multiples of 64; vocab >= 64 and a multiple of
- * 64; seq_len >= 1; max_batch >= 1; n_kv_heads divides n_heads.
+ * 64; seq_len >= 1 (the bf16 path with head_dim 128: at most 32640, its
+ * attention backward keeps dS per sequence and head); max_batch >= 1;
+ * n_kv_heads divides n_heads.
  */
 typedef struct {
   int32_t depth;
@@ -359,7 +361,8 @@ int nc_optim_step(nc_ctx* ctx, const nc_optim_config* cfg, int step, const float
  * t * rope_base^(-2i/hd), t = position within the sequence.
  * Layout of q, k, v, dout, out, dq, dk, dv: (dt) [B, T, H, hd] contiguous.
  * hd must be 16, 32, 64 or 128.  Errors: NC_ERR_NULL, NC_ERR_ARG (sizes),
- * NC_ERR_UNSUPPORTED (hd not in {64, 128} on the bf16 path), NC_ERR_WORKSPACE.
+ * NC_ERR_UNSUPPORTED (hd not in {64, 128} on the bf16 path, or T > 32640
+ * with hd 128 on the bf16 path), NC_ERR_WORKSPACE.
  */
 uint64_t nc_attention_workspace_bytes(int B, int H, int T, int hd, int dtype);
 int nc_attention_fwd_bwd(const void* q, const void* k, const void* v,
