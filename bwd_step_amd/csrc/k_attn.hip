@@ -537,7 +537,8 @@ __global__ void __launch_bounds__(256) attn_bwd_D128(AttnArgs p) {
 // 64-key blocks through two LDS stages (a K tile, 64 rows x 256 bytes with
 // the sw2 swizzle, and the 16 dS chunks of 64 keys x 128 queries): 64 KB,
 // so two workgroups share a compute unit.  The kernel streams the stored
-// dS once from HBM, which bounds it.
+// dS once from HBM, which bounds it.  Its epilogue also runs the QK-norm +
+// RoPE backward of q, so it writes the gradient w.r.t. the pre-norm q.
 //
 // In LDS the chunks are ordered (kw, qw, t) within the tile and the 16-byte
 // pieces of chunk lane li + 32 g sit at slot 32 g + (li ^ 4 g): a 16-lane
@@ -630,15 +631,65 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
   }
   wait_vmem();
 
-  if (qi >= T) return;
+  // QK-norm + RoPE backward of this lane's query, head h: with dqh the
+  // gradient w.r.t. qh = R_t rho(q) and y = R_t^T qh = rho(q), the gradient
+  // w.r.t. q is r (dy - y mean(dy y)), dy = R_t^T dqh.  Lanes l and l ^ 32
+  // hold the two halves of the head row: element 32 x + 8 rg + 4 g + e is
+  // dq[x][4 rg + e], so the pair (i, i + 64) is (x, x + 2) of one lane and
+  // only the mean needs the partner lane.
+  const bool live = qi < T;
   const float sc = -p.scale;  // the stored matrix is -dS
-  float* dqp = p.dq32 + (tok0 + qi) * p.lddq + h * HD;
+  const size_t n = tok0 + (live ? qi : 0);
+  const int t = live ? qi : 0;
+  const bf16* vrow = (const bf16*)p.q + n * p.ldq + h * HD;
+  // dq[x] becomes dy of elements i (x < 2) and i + 64 (dq[x + 2]); ylo / yhi
+  // hold y of the same elements
+  f32x16 ylo[2], yhi[2];
+  float dot = 0.f;
 #pragma unroll
-  for (int x = 0; x < HB; ++x)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      f32x4 w{dq[x][rg * 4 + 0] * sc, dq[x][rg * 4 + 1] * sc, dq[x][rg * 4 + 2] * sc, dq[x][rg * 4 + 3] * sc};
-      *reinterpret_cast<f32x4*>(dqp + x * 32 + 8 * rg + 4 * g) = w;
+      const int i = 32 * x + 8 * rg + 4 * g;  // pairs i .. i + 3
+      const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
+      const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
+      const f32x4 cv{c01.x, c01.z, c23.x, c23.z}, sv{c01.y, c01.w, c23.y, c23.w};
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + i);
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + i + 64);
+      const f32x4 v0{bf16lo_to_f32(a0.x), bf16hi_to_f32(a0.x), bf16lo_to_f32(a0.y), bf16hi_to_f32(a0.y)};
+      const f32x4 v1{bf16lo_to_f32(a1.x), bf16hi_to_f32(a1.x), bf16lo_to_f32(a1.y), bf16hi_to_f32(a1.y)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        const float g0 = dq[x][r] * sc, g1 = dq[x + 2][r] * sc;
+        const float d0 = g0 * cv[e] + g1 * sv[e], d1 = g1 * cv[e] - g0 * sv[e];
+        const float y0 = v0[e] * cv[e] + v1[e] * sv[e], y1 = v1[e] * cv[e] - v0[e] * sv[e];
+        dq[x][r] = d0;
+        dq[x + 2][r] = d1;
+        ylo[x][r] = y0;
+        yhi[x][r] = y1;
+        dot = fmaf(d0, y0, fmaf(d1, y1, dot));
+      }
+    }
+  dot += __shfl_xor(dot, 32, 64);
+  dot *= 1.0f / 128.0f;
+  if (!live) return;
+  const float rr = p.rq[n * p.H + h];
+  bf16* out = (bf16*)p.dq_pre + n * p.lddq_pre + h * HD;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int i = 32 * x + 8 * rg + 4 * g;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        lo[e] = (dq[x][r] - ylo[x][r] * dot) * rr;
+        hi[e] = (dq[x + 2][r] - yhi[x][r] * dot) * rr;
+      }
+      *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w)};
+      *reinterpret_cast<u32x2*>(out + i + 64) = u32x2{pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
     }
 }
 
@@ -1275,6 +1326,7 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
     if (hd == 128) {
       // D, then dK/dV (which stores dS), then dQ from the stored dS
       if (!p.dsT || p.tpad != attn_ds_pad(p.T)) return NC_ERR_WORKSPACE;
+      if (!p.dq_pre || !p.rq || !p.cs) return NC_ERR_NULL;
       if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
       attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
       attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);

@@ -337,9 +337,9 @@ struct QkBwdArgs {
 
 template <class T, int HALF>
 __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const float* __restrict__ cs, int N,
-                                                              int H, int Tseq) {
+                                                              int H, int Tseq, int w0) {
   constexpr int LPV = QkLanes<HALF>::LPV, VPW = QkLanes<HALF>::VPW;
-  const int w = blockIdx.y;
+  const int w = w0 + blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
   const int i = (lane % LPV) * 4;
@@ -391,17 +391,19 @@ static int qk_fwd_dispatch(const QkArgs& a, const float* cs, int N, int H, int h
 }
 
 template <class T>
-static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, int hd, int Tseq, hipStream_t s) {
-  const int vecs = N * H;
+static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, int hd, int Tseq, hipStream_t s,
+                           bool k_only) {
+  const int vecs = N * (k_only ? a.heads[1] : H);
   if (vecs == 0) return 0;
   const int half = hd / 2;
   const int vpb = 4 * (64 / (half / 4));
-  dim3 grid((vecs + vpb - 1) / vpb, 2);
+  dim3 grid((vecs + vpb - 1) / vpb, k_only ? 1 : 2);
+  const int w0 = k_only ? 1 : 0;
   switch (half) {
-    case 64: qknorm_rope_bwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
-    case 32: qknorm_rope_bwd_kernel<T, 32><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
-    case 16: qknorm_rope_bwd_kernel<T, 16><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
-    case 8: qknorm_rope_bwd_kernel<T, 8><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq); break;
+    case 64: qknorm_rope_bwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 32: qknorm_rope_bwd_kernel<T, 32><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 16: qknorm_rope_bwd_kernel<T, 16><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 8: qknorm_rope_bwd_kernel<T, 8><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
     default: return 7;
   }
   NC_LAUNCH_CHECK();
@@ -425,7 +427,7 @@ int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int l
 int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s, int Hk) {
+                           hipStream_t s, int Hk, bool k_only) {
   QkBwdArgs a;
   a.heads[0] = H; a.heads[1] = Hk > 0 ? Hk : H;
   a.dv[0] = dq; a.dv[1] = dk;
@@ -435,7 +437,8 @@ int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk,
   a.r[0] = rq; a.r[1] = rk;
   a.du[0] = dq_out; a.du[1] = dk_out;
   a.ld_du[0] = ldq_out; a.ld_du[1] = ldk_out;
-  return dtype == 0 ? qk_bwd_dispatch<bf16>(a, cs, N, H, hd, T, s) : qk_bwd_dispatch<float>(a, cs, N, H, hd, T, s);
+  return dtype == 0 ? qk_bwd_dispatch<bf16>(a, cs, N, H, hd, T, s, k_only)
+                    : qk_bwd_dispatch<float>(a, cs, N, H, hd, T, s, k_only);
 }
 
 }  // namespace nc

@@ -80,10 +80,11 @@ int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s);
 int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
                            void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
                            int T, float eps, int dtype, hipStream_t s, int Hk = 0);
+// k_only: only the k tensor (the q part was finished by the attention backward)
 int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s, int Hk = 0);
+                           hipStream_t s, int Hk = 0, bool k_only = false);
 
 // ---- embedding
 int launch_embed_fwd(const void* E, const int32_t* tok, float* x, int N, int d, int V, int dtype, int* status,
@@ -112,6 +113,12 @@ struct AttnArgs {
   // rows, query columns), written by the dK/dV kernel and read by dQ
   void* dsT = nullptr;
   long tpad = 0;  // attn_ds_pad(T)
+  // bf16, head_dim 128: the dQ kernel finishes the QK-norm + RoPE backward
+  // of q itself and writes dq w.r.t. the pre-norm q (bf16) here instead of
+  // dq32: rq = 1/rms of q [N][H], cs = the RoPE table (cos, sin per pair)
+  void* dq_pre = nullptr; long lddq_pre = 0;
+  const float* rq = nullptr;
+  const float* cs = nullptr;
 };
 // Rows (and columns) of each (b, h) block of the stored dS: T rounded up to
 // 128.  A block is addressed through one buffer resource (32-bit offsets), so

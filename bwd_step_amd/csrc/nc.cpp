@@ -533,6 +533,14 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     a.lse = (float*)(L + P.lse);
     a.Dbuf = (float*)(W + P.Dbuf);
     a.dsT = W + P.dsT; a.tpad = attn_ds_pad(c.seq_len);
+    // bf16, head_dim 128: the dQ kernel finishes q's QK-norm + RoPE backward
+    // and writes dq straight into dqkv; the pass below then handles k only
+    const bool q_fused = dt == NC_BF16 && hd == 128;
+    if (q_fused) {
+      a.dq_pre = dqkv; a.lddq_pre = nq;
+      a.rq = (const float*)(L + P.rq);
+      a.cs = cs;
+    }
     a.dq32 = dqk32; a.lddq = hh + hk;
     a.B = batch; a.H = H; a.T = c.seq_len;
     a.G = H / Hk;
@@ -548,9 +556,10 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
       PROF(pf, PC_OTHER, 0, (double)N * hh * (4 + es) + (double)N * hk * (4 + es),
            launch_kv_group_sum((float*)(W + P.gq_dk), hh, W + P.gq_dv, hh, dqk32 + hh, hh + hk,
                                dqkv + (hh + hk) * es, nq, N, Hk, a.G, hd, dt, s));
-    PROF(pf, PC_QK_BWD, 0, (double)N * (hh + hk) * (4 + 2 * es) + (double)N * (H + Hk) * 4, launch_qknorm_rope_bwd(dqk32, hh + hk, dqk32 + hh, hh + hk, qkv, nq, qkv + hh * es, nq,
-                               (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
-                               hd, c.seq_len, dt, s, Hk));
+    PROF(pf, PC_QK_BWD, 0, (double)N * ((q_fused ? 0 : hh) + hk) * (4 + 2 * es) + (double)N * ((q_fused ? 0 : H) + Hk) * 4,
+         launch_qknorm_rope_bwd(dqk32, hh + hk, dqk32 + hh, hh + hk, qkv, nq, qkv + hh * es, nq,
+                                (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
+                                hd, c.seq_len, dt, s, Hk, q_fused));
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
     GemmCall b7 = mk(dqkv, nq, true, Wqkv, d, false, N, d, nq, dt);
@@ -968,10 +977,16 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void
   a.dv = dv; a.lddv = hh;
   a.dsT = w + off[10]; a.tpad = attn_ds_pad(T);
   a.B = B; a.H = H; a.T = T;
+  const bool q_fused = dtype == NC_BF16 && hd == 128;  // the dQ kernel writes dq itself
+  if (q_fused) {
+    a.dq_pre = dq; a.lddq_pre = hh;
+    a.rq = (const float*)(w + off[3]);
+    a.cs = cs;
+  }
   TRY(launch_attn_fwd(a, hd, dtype, s));
   TRY(launch_attn_bwd(a, hd, dtype, s));
   return launch_qknorm_rope_bwd(a.dq32, hh, a.dk32, hh, w + off[1], hh, w + off[2], hh, (float*)(w + off[3]),
-                                (float*)(w + off[4]), dq, hh, dk, hh, cs, N, H, hd, T, dtype, s);
+                                (float*)(w + off[4]), dq, hh, dk, hh, cs, N, H, hd, T, dtype, s, 0, q_fused);
 }
 
 static size_t ce_ws_parts(int N, int d, int V, int dtype, size_t* off) {
