@@ -13,8 +13,11 @@
 // workgroup owns a row: pass 1 keeps a per-thread online (max, sum), merged
 // across the workgroup; pass 2 re-reads the row (now L2/MALL-resident) and
 // writes G.  The mean loss is reduced over all rows in a fixed order.
-// bf16 path: the row statistics come from the LM-head GEMM epilogue instead
-// (per 128-column segment), and G overwrites the bf16 logits (ce_finish).
+// bf16 path (ce_finish): the LM-head product stores bf16 logits only; a
+// workgroup per row holds the row in registers (V <= 65536) or streams it
+// twice, takes max and sum exp from it, the target logit in fp32 as the dot
+// product of its hidden row with the target's weight row, and overwrites the
+// logits with G in place.
 #include "common.h"
 #include "kernels.h"
 
@@ -103,17 +106,53 @@ int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, l
   return 0;
 }
 
-// Finish a chunk from the partials of the LM-head GEMM epilogue (bf16 path):
-// a workgroup per row combines the (max, sum exp) pairs of its 128-column
-// segments into lse, writes loss_n = lse - l_{n, y_n} (fp32 target logit
-// from the epilogue), then overwrites the row's bf16 logits in place with
-// G_nv = (exp(l_nv - lse) - [v == y_n]) / count (zeros for a row that is
-// not counted).
-__global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict__ part, int nseg,
-                                                        const float* __restrict__ tlog,
+// Finish a chunk from its bf16 logits (bf16 path).  Per row, a workgroup of
+// 256 threads: max and sum exp(l - max) over the row (exp2 domain, the
+// hardware v_exp_f32), merged across the workgroup; the fp32 target logit
+// l_y = z . W[y] over the hidden width d; loss_n = lse - l_y; then the row's
+// logits become G_nv = (exp(l_nv - lse) - [v == y_n]) / count in place
+// (zeros for a row that is not counted).  REG: the row stays in registers
+// (thread t holds 8-element chunks t, t + 256, ..: V <= 2048 * kCeChunks);
+// otherwise it is read twice.
+constexpr int kCeChunks = 32;
+constexpr float kLog2eCe = 1.4426950408889634f;
+
+__device__ __forceinline__ void unpack8(const u32x4 w, float* v) {
+  v[0] = bf16lo_to_f32(w.x); v[1] = bf16hi_to_f32(w.x); v[2] = bf16lo_to_f32(w.y); v[3] = bf16hi_to_f32(w.y);
+  v[4] = bf16lo_to_f32(w.z); v[5] = bf16hi_to_f32(w.z); v[6] = bf16lo_to_f32(w.w); v[7] = bf16hi_to_f32(w.w);
+}
+
+// Workgroup-wide max / sum of one value per thread (256 threads).
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// Make the held row opaque between passes, so that each pass unpacks it
+// again instead of the compiler keeping 256 unpacked floats live.
+template <int N>
+__device__ __forceinline__ void opaque(u32x4 (&r)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));
+}
+
+template <bool REG>
+__global__ void __launch_bounds__(256) ce_finish_kernel(const bf16* __restrict__ z, long ldz,
+                                                        const bf16* __restrict__ W, long ldw, int d,
                                                         const int32_t* __restrict__ tgt, bf16* __restrict__ LG,
                                                         long ld, float* __restrict__ loss_rows, int V,
                                                         int* __restrict__ status) {
+  __shared__ float sh[4];
   const int row = blockIdx.x;
   bf16* g = LG + (size_t)row * ld;
   int y = tgt[row];
@@ -123,49 +162,112 @@ __global__ void __launch_bounds__(256) ce_finish_kernel(const float* __restrict_
     return;
   }
   const float inv_n = inv_count(blk_count(status));
-  const float* pr = part + (size_t)row * nseg * 2;
-  float m = -INFINITY, s = 0.f;
-  for (int k = threadIdx.x; k < nseg; k += 256) online_merge(m, s, pr[2 * k], pr[2 * k + 1]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-    online_merge(m, s, m2, s2);
-  }
   const bool y_ok = y < V;
   if (!y_ok) y = V - 1;
-  // the clamped target of an out-of-range id has no fp32 logit: read the
-  // stored one before the row is overwritten
-  const float ty = y_ok ? tlog[row] : to_f32(g[y]);
-  __shared__ float sm[4], ss[4];
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[wv] = m; ss[wv] = s; }
-  __syncthreads();
-  m = sm[0]; s = ss[0];
-  for (int w = 1; w < 4; ++w) online_merge(m, s, sm[w], ss[w]);
+  // (REG) the row, chunk k of thread t at column 8 (256 k + t)
+  [[maybe_unused]] u32x4 r[REG ? kCeChunks : 1];
+  if constexpr (REG) {
+#pragma unroll
+    for (int k = 0; k < kCeChunks; ++k) {
+      const int c = 8 * (256 * k + (int)threadIdx.x);
+      r[k] = c < V ? *reinterpret_cast<const u32x4*>(g + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // the target logit in fp32 (also for a clamped out-of-range id)
+  float dot = 0.f;
+  {
+    const bf16* zr = z + (size_t)row * ldz;
+    const bf16* wr = W + (size_t)y * ldw;
+    for (int c = threadIdx.x * 8; c < d; c += 2048) {
+      float a[8], b[8];
+      unpack8(*reinterpret_cast<const u32x4*>(zr + c), a);
+      unpack8(*reinterpret_cast<const u32x4*>(wr + c), b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(a[e], b[e], dot);
+    }
+  }
+  // max
+  float m = -INFINITY;
+  if constexpr (REG) {
+#pragma unroll
+    for (int k = 0; k < kCeChunks; ++k) {
+      if (8 * (256 * k + (int)threadIdx.x) < V) {
+        float v[8];
+        unpack8(r[k], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, v[e]);
+      }
+    }
+  } else {
+    for (int c = threadIdx.x * 8; c < V; c += 2048) {
+      float v[8];
+      unpack8(*reinterpret_cast<const u32x4*>(g + c), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, v[e]);
+    }
+  }
+  m = block_max(m, sh);
+  const float mo = -m * kLog2eCe;
+  // sum exp(l - m)
+  float s = 0.f;
+  if constexpr (REG) {
+    opaque(r);
+#pragma unroll
+    for (int k = 0; k < kCeChunks; ++k) {
+      if (8 * (256 * k + (int)threadIdx.x) < V) {
+        float v[8];
+        unpack8(r[k], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eCe, mo));
+      }
+    }
+  } else {
+    for (int c = threadIdx.x * 8; c < V; c += 2048) {
+      float v[8];
+      unpack8(*reinterpret_cast<const u32x4*>(g + c), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[e], kLog2eCe, mo));
+    }
+  }
+  s = block_sum(s, sh);
+  dot = block_sum(dot, sh);
   const float lse = m + logf(s);
   if (threadIdx.x == 0) {
-    loss_rows[row] = lse - ty;
+    loss_rows[row] = lse - dot;
     if (!y_ok) atomicOr(status, kStatusTokenRange);
   }
-  for (int c = threadIdx.x * 8; c < V; c += 2048) {
-    u32x4 w = *reinterpret_cast<const u32x4*>(g + c);
-    float v[8] = {bf16lo_to_f32(w.x), bf16hi_to_f32(w.x), bf16lo_to_f32(w.y), bf16hi_to_f32(w.y),
-                  bf16lo_to_f32(w.z), bf16hi_to_f32(w.z), bf16lo_to_f32(w.w), bf16hi_to_f32(w.w)};
+  // G in place
+  const float lo = -lse * kLog2eCe;
+  auto write_g = [&](int c, u32x4 w) {
+    float v[8];
+    unpack8(w, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (expf(v[e] - lse) - (c + e == y ? 1.f : 0.f)) * inv_n;
-    w.x = pack_bf16x2(v[0], v[1]);
-    w.y = pack_bf16x2(v[2], v[3]);
-    w.z = pack_bf16x2(v[4], v[5]);
-    w.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<u32x4*>(g + c) = w;
+    for (int e = 0; e < 8; ++e) v[e] = (__builtin_amdgcn_exp2f(fmaf(v[e], kLog2eCe, lo)) - (c + e == y ? 1.f : 0.f)) * inv_n;
+    *reinterpret_cast<u32x4*>(g + c) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  };
+  if constexpr (REG) {
+    opaque(r);
+#pragma unroll
+    for (int k = 0; k < kCeChunks; ++k) {
+      const int c = 8 * (256 * k + (int)threadIdx.x);
+      if (c < V) write_g(c, r[k]);
+    }
+  } else {
+    for (int c = threadIdx.x * 8; c < V; c += 2048) write_g(c, *reinterpret_cast<const u32x4*>(g + c));
   }
 }
 
-int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
-                     float* loss_rows, int rows, int V, int* status, hipStream_t s) {
+int launch_ce_finish(const void* z, long ldz, const void* W, long ldw, int d, const int32_t* tgt, void* logits_G,
+                     long ld, float* loss_rows, int rows, int V, int* status, hipStream_t s) {
   if (rows == 0) return 0;
-  if (V % 8 || ld % 8) return NC_ERR_ARG;
-  ce_finish_kernel<<<rows, 256, 0, s>>>(part, nseg, tlog, tgt, (bf16*)logits_G, ld, loss_rows, V, status);
+  if (V % 8 || ld % 8 || d % 8 || ldz % 8 || ldw % 8) return NC_ERR_ARG;
+  if (V <= 2048 * kCeChunks)
+    ce_finish_kernel<true><<<rows, 256, 0, s>>>((const bf16*)z, ldz, (const bf16*)W, ldw, d, tgt, (bf16*)logits_G,
+                                                ld, loss_rows, V, status);
+  else
+    ce_finish_kernel<false><<<rows, 256, 0, s>>>((const bf16*)z, ldz, (const bf16*)W, ldw, d, tgt, (bf16*)logits_G,
+                                                 ld, loss_rows, V, status);
   NC_LAUNCH_CHECK();
   return 0;
 }

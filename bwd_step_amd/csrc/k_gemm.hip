@@ -541,72 +541,6 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
       for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
   };
 
-  // Cross-entropy epilogue of the LM head: logits stored in bf16 and, for
-  // each row, the max and the sum of exp(l - max) over this wavefront's 128
-  // columns (the lanes l and l ^ 32 hold one row's columns), and the fp32
-  // logit of the target column.
-  auto epilogue_ce = [&](const Item& ci) {
-    constexpr float kLog2e = 1.4426950408889634f;
-    const int jw = ci.n0 + wn * TN;        // the wavefront's first column (N < 2^31)
-    const int jb = jw + 4 * (lane >> 5);   // column of acc[a][c][4 q + e] is jb + 32 c + 8 q + e
-    const bool full = ci.n0 + BN <= p.N;   // uniform: every column of the tile exists
-    // a moved-back tile (N a multiple of 128): a wavefront whose 128 columns
-    // precede nlo belongs to the previous tile and writes nothing
-    const bool cols_own = jw >= ci.nlo;
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-      const long i = ci.m0 + wm * TM + a * 32 + (lane & 31);
-      const bool row_ok = i < p.M && i >= ci.mlo && cols_own;
-      const int yc = (row_ok ? p.e.tgt[i] : -1) - jb;  // target column relative to jb
-      bf16* crow = (bf16*)p.e.c_lp + i * p.e.ld_lp + jb;
-      // pass 1: bf16 logits out, the fp32 target logit, the row maximum
-      float mraw = -INFINITY;
-#pragma unroll
-      for (int c = 0; c < FN; ++c) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = 32 * c + 8 * q;
-          const f32x4 v{acc[a][c][4 * q], acc[a][c][4 * q + 1], acc[a][c][4 * q + 2], acc[a][c][4 * q + 3]};
-          if (full) {
-            mraw = fmaxf(mraw, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (jb + j + e < p.N) mraw = fmaxf(mraw, v[e]);
-          }
-          if (row_ok && (full || jb + j < p.N)) store4(crow + j, v);
-          const unsigned dy = (unsigned)(yc - j);
-          if (row_ok && dy < 4u) p.e.tlog[i] = dy == 0 ? v.x : dy == 1 ? v.y : dy == 2 ? v.z : v.w;
-        }
-      }
-      // pass 2: sum of exp(l - max) in the log2 domain
-      const float m2 = mraw * kLog2e;
-      float s = 0.f;
-      if (mraw != -INFINITY) {
-#pragma unroll
-        for (int c = 0; c < FN; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (full || jb + 32 * c + 8 * (r >> 2) + (r & 3) < p.N)
-              s += __builtin_amdgcn_exp2f(fmaf(acc[a][c][r], kLog2e, -m2));
-      }
-      // merge with the partner lane holding the row's other columns
-      const float pm = __shfl_xor(m2, 32, 64), ps = __shfl_xor(s, 32, 64);
-      const float mn = fmaxf(m2, pm);
-      if (mn != -INFINITY) s = s * __builtin_amdgcn_exp2f(m2 - mn) + ps * __builtin_amdgcn_exp2f(pm - mn);
-      if (row_ok && lane < 32 && jw < p.N) {
-        float* pp = p.e.part + ((size_t)i * p.e.nseg + (size_t)(jw / TN)) * 2;
-        pp[0] = mn * (1.0f / kLog2e);  // natural-log max
-        pp[1] = s;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-      for (int c = 0; c < FN; ++c) acc[a][c] = f32x16{};
-  };
-
   if constexpr (P64) {
     // One 160 KB array of five 32 KB slots.  Half i of the sequence A(0) B(0)
     // A(1) B(1) ... goes to slot i mod 5: while pair P is computed from its
@@ -830,8 +764,6 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
         epilogue_lds(ci, slot_el(wv < 2 ? cs + 3 : cs + 4) + (wv & 1) * 8192);
       } else if constexpr (EPI == EPI_DRELU2) {
         epilogue_drelu2_lds(ci, slot_el(wv < 2 ? cs + 3 : cs + 4) + (wv & 1) * 8192);
-      } else if constexpr (EPI == EPI_CE) {
-        epilogue_ce(ci);
       } else {
         epilogue(ci);
       }
@@ -900,8 +832,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mfma_kernel(GemmParams p) {
     NC_STEP(1, 2, 0, na, nb, nx, 0, has_next)
     NC_STEP(2, 3, 1, na, nb, nx, 1, has_next)
     NC_STEP(3, 0, 2, na, nb, nx, 2, has_next)
-    if constexpr (EPI == EPI_CE) epilogue_ce(ci);
-    else if constexpr (EPI == EPI_DRELU2) epilogue_drelu2(ci);
+    if constexpr (EPI == EPI_DRELU2) epilogue_drelu2(ci);
     else epilogue(ci);
     if (!has_next) break;
     it = nit;
@@ -1049,16 +980,15 @@ static void launch_mfma_k(const GemmParams& p, bool ak, bool bk, bool p64, dim3 
 // already 512 bytes) with K a multiple of 64 of at least 640 and row
 // strides of at least K.  Its last tile-row and tile-column are moved back
 // inside the operands, so M and N are at least 256; N is a multiple of 8
-// (whole 16-byte column chunks in the staged epilogues), of 128 for the
-// cross-entropy epilogue (whole 128-column softmax segments per wavefront).
-static bool use_pairs(const GemmParams& p, bool ak, bool bk, int epi) {
+// (whole 16-byte column chunks in the staged epilogues).
+static bool use_pairs(const GemmParams& p, bool ak, bool bk) {
   return ak && bk && p.batch == 1 && !p.sym && p.K % 64 == 0 && p.K >= 640 && p.lda >= p.K && p.ldb >= p.K &&
-         p.M >= 256 && p.N >= 256 && p.N % (epi == EPI_CE ? 128 : 8) == 0;
+         p.M >= 256 && p.N >= 256 && p.N % 8 == 0;
 }
 template <int EPI, bool KTAIL>
 static int launch_mfma_b(const GemmParams& p, bool ak, bool bk, dim3 grid, hipStream_t s) {
   if (p.batch == 1 && !p.sym) {
-    launch_mfma_k<EPI, KTAIL, false>(p, ak, bk, !KTAIL && use_pairs(p, ak, bk, EPI), grid, s);
+    launch_mfma_k<EPI, KTAIL, false>(p, ak, bk, !KTAIL && use_pairs(p, ak, bk), grid, s);
     return 0;
   }
   if constexpr (EPI == EPI_LP || EPI == EPI_AXPBY || EPI == EPI_F32) {
@@ -1218,7 +1148,6 @@ int launch_gemm(const GemmCall& g, hipStream_t s) {
       case EPI_LP: rc = launch_mfma<EPI_LP>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_RELU2: rc = launch_mfma<EPI_RELU2>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_DRELU2: rc = launch_mfma<EPI_DRELU2>(p, g.a_k, g.b_k, grid, s); break;
-      case EPI_CE: rc = launch_mfma<EPI_CE>(p, g.a_k, g.b_k, grid, s); break;
       case EPI_AXPBY: rc = launch_mfma<EPI_AXPBY>(p, g.a_k, g.b_k, grid, s); break;
       default: return 8;
     }

@@ -10,7 +10,6 @@ namespace nc {
 // ---- GEMM epilogues
 enum { EPI_F32 = 0, EPI_RESID = 1, EPI_LP = 2, EPI_RELU2 = 3, EPI_DRELU2 = 4,
        EPI_F32_ACC = 5 /* internal to the GEMM: EPI_F32 with beta = 1 */,
-       EPI_CE = 6 /* logits: bf16 store + per-row softmax partials + target logit (bf16 path) */,
        EPI_AXPBY = 7 /* c_lp = alpha * aux + beta * acc, aux and c_lp in the element type */ };
 
 struct EpiArgs {
@@ -23,13 +22,6 @@ struct EpiArgs {
   long ld_lp = 0;
   const void* aux = nullptr;  // EPI_DRELU2: g
   long ld_aux = 0;
-  // EPI_CE: logits in c_lp (bf16, ld_lp); for each row and 128-column segment
-  // (max, sum exp(l - max)) in part[row][seg][2] (nseg segments per row); the
-  // fp32 logit of column tgt[row] in tlog[row]
-  const int32_t* tgt = nullptr;
-  float* part = nullptr;
-  float* tlog = nullptr;
-  int nseg = 0;
   // EPI_AXPBY: the two coefficients (aux is read at the output's position)
   float alpha = 0.f, beta_f = 1.f;
 };
@@ -149,10 +141,11 @@ __host__ __device__ inline int* blk_count(int* status) { return status + 4; }
 __host__ __device__ inline double* blk_loss_acc(int* status) { return reinterpret_cast<double*>(status + 8); }
 // count = number of y[i] >= 0 over n ids; loss accumulator = 0
 int launch_count_targets(const int32_t* y, long n, int* status, hipStream_t s);
-// Finish the cross-entropy of a chunk from the EPI_CE partials: loss_rows,
-// and G = (softmax - onehot) / count written over the bf16 logits in place.
-int launch_ce_finish(const float* part, int nseg, const float* tlog, const int32_t* tgt, void* logits_G, long ld,
-                     float* loss_rows, int rows, int V, int* status, hipStream_t s);
+// Finish the cross-entropy of a chunk from its bf16 logits (logits_G [rows]
+// [ld], overwritten in place by G = (softmax - onehot) / count) and the loss
+// rows; z [rows][ldz] and W [V][ldw] (bf16, width d) give the fp32 target logits.
+int launch_ce_finish(const void* z, long ldz, const void* W, long ldw, int d, const int32_t* tgt, void* logits_G,
+                     long ld, float* loss_rows, int rows, int V, int* status, hipStream_t s);
 int launch_ce_rows(const float* logits, long ldl, const int32_t* tgt, void* G, long ldg, float* loss_rows, int rows,
                    int V, int dtype, int* status, hipStream_t s);
 // loss accumulator += sum of the n loss rows (fixed order)

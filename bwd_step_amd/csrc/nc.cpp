@@ -41,11 +41,10 @@ inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 // Longest KV cache (positions) the inference entry points accept.
 constexpr int kMaxCacheLen = 1 << 16;
 
-// LM-head chunk scratch besides G: bf16 path, the GEMM epilogue's per-row
-// softmax partials (max, sum exp) over 128-column segments and the target
-// logits; fp32 path, the fp32 logits.
+// LM-head chunk scratch besides G: fp32 path, the fp32 logits (the bf16 path
+// writes its logits into G).
 size_t ce_aux_bytes(size_t chunk, size_t V, int dtype) {
-  if (dtype == NC_BF16) return chunk * ((V + 127) / 128) * 2 * 4 + al(chunk * 4);
+  if (dtype == NC_BF16) return 0;
   return chunk * V * 4;
 }
 
@@ -281,7 +280,6 @@ inline double gbytes(const GemmCall& g) {
     case EPI_RESID: out = 8.0 * mn; break;                     // fp32 residual read + write
     case EPI_LP: case EPI_RELU2: out = es * mn; break;
     case EPI_DRELU2: out = 2.0 * es * mn; break;               // g read, du written
-    case EPI_CE: out = 2.0 * mn + 8.0 * g.M * (double)g.e.nseg + 4.0 * g.M; break;
     default: break;
   }
   return es * ((double)g.M * g.K + (double)g.N * g.K) + out;
@@ -299,15 +297,14 @@ GemmCall mk(const void* A, long lda, bool ak, const void* B, long ldb, bool bk, 
 // LM head + cross-entropy over tokens in chunks: loss_rows, dz (fp32, [N,d]),
 // dW (fp32 [V,d]; overwritten or accumulated).  G and the scratch `aux`
 // (ce_aux_bytes) are chunk-sized.  bf16: the logits GEMM writes bf16 logits
-// into G with the softmax partials (EPI_CE), ce_finish turns them into G in
-// place; fp32: fp32 logits, then ce_rows.  wT (bf16, optional, V*d
+// into G, ce_finish turns them into G in place (with the fp32 target logits
+// from z and W); fp32: fp32 logits, then ce_rows.  wT (bf16, optional, V*d
 // elements): W is transposed into it once so that dz = G W reads both
 // operands k-contiguous.
 int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int V, float* loss_rows, float* dz,
               float* dW, int accumulate, int dtype, float* aux, void* G, float* splitk, uint64_t splitk_bytes,
               int* status, hipStream_t s, Prof* pf, void* wT = nullptr) {
   const size_t es = dtype == NC_BF16 ? 2 : 4;
-  const int nseg = (V + 127) / 128;
   const int chunk = ce_chunk(N, V, dtype);
   if (wT && dtype == NC_BF16) TRY(launch_transpose_bf16(W, V, d, d, wT, V, s));
   for (int c0 = 0; c0 < N; c0 += chunk) {
@@ -315,13 +312,10 @@ int lmhead_ce(const void* z, const void* W, const int32_t* y, int N, int d, int 
     const char* zc = (const char*)z + (size_t)c0 * d * es;
     GemmCall lg = mk(zc, d, true, W, d, true, rows, V, d, dtype);
     if (dtype == NC_BF16) {
-      float* part = aux;
-      float* tlog = aux + (size_t)chunk * nseg * 2;
-      lg.epi = EPI_CE; lg.e.c_lp = G; lg.e.ld_lp = V; lg.e.tgt = y + c0; lg.e.part = part; lg.e.tlog = tlog;
-      lg.e.nseg = nseg;
+      lg.epi = EPI_LP; lg.e.c_lp = G; lg.e.ld_lp = V;
       PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
-      PROF(pf, PC_CE, 0, (double)rows * V * 4 + (double)rows * nseg * 8,
-           launch_ce_finish(part, nseg, tlog, y + c0, G, V, loss_rows + c0, rows, V, status, s));
+      PROF(pf, PC_CE, 0, (double)rows * V * 4 + (double)rows * d * 4,
+           launch_ce_finish(zc, d, W, d, d, y + c0, G, V, loss_rows + c0, rows, V, status, s));
     } else {
       lg.epi = EPI_F32; lg.e.c32 = aux; lg.e.ldc = V; lg.e.beta = 0;
       PROF(pf, PC_GEMM, gflops(lg), gbytes(lg), launch_gemm(lg, s));
