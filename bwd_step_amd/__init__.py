@@ -162,6 +162,10 @@ class Model:
         """Synchronise and return the device status code (0 = ok)."""
         return int(lib().nc_check(self._h))
 
+    def poison_workspace(self, on=True):
+        """Debug: NaN-fill the workspace before each call (nc_debug_poison_workspace)."""
+        check(lib().nc_debug_poison_workspace(self._h, int(bool(on))), "nc_debug_poison_workspace")
+
     # ---- optimizer step (nc_optim_*)
     OPTIM_DEFAULTS = dict(lr_adamw=3e-3, lr_muon=0.02, beta1=0.9, beta2=0.95, eps=1e-8, momentum=0.95,
                           weight_decay=0.1, clip=1.0, final_frac=0.0, warmup_steps=1, total_steps=1, ns_steps=5)

@@ -532,26 +532,28 @@ __global__ void __launch_bounds__(256) attn_bwd_D128(AttnArgs p) {
 // dQ from the stored dS: dQ_t = scale sum_j dS_tj kh_j, as dQ^T = K^T dS^T.
 // The A operand is transposed out of the K tile (tr_frag); the B operand
 // comes from the dS chunks with ds_read_b64_tr_b16 (ds_frag).  The dK/dV
-// kernel stored every causal chunk (zeros above the diagonal and past T),
-// so no mask is needed here.  128 queries per workgroup (32 per wavefront),
-// 64-key blocks through two LDS stages (a K tile, 64 rows x 256 bytes with
-// the sw2 swizzle, and the 16 dS chunks of 64 keys x 128 queries): 64 KB,
-// so two workgroups share a compute unit.  The kernel streams the stored
-// dS once from HBM, which bounds it.  Its epilogue also runs the QK-norm +
+// kernel stored every chunk of its 128 keys from their first query on
+// (zeros above the diagonal and past T), so no mask is needed; a wavefront
+// only skips the key blocks past its last query.  256 queries per workgroup (8 wavefronts of
+// 32, two per SIMD), 64-key blocks through three LDS stages (a K tile, 64
+// rows x 256 bytes with the sw2 swizzle, and the 32 dS chunks of 64 keys x
+// 256 queries; 48 KB each), loaded two blocks ahead.  The kernel streams
+// the stored dS once and re-reads K once per 256 queries.  Its epilogue also runs the QK-norm +
 // RoPE backward of q, so it writes the gradient w.r.t. the pre-norm q.
 //
 // In LDS the chunks are ordered (kw, qw, t) within the tile and the 16-byte
-// pieces of chunk lane li + 32 g sit at slot 32 g + (li ^ 4 g): a 16-lane
-// transposed read then covers 4 keys x 16 queries in 8 distinct 16-byte
-// bank groups.
+// piece of chunk lane li + 32 g sits at slot 32 g + (li ^ (4 g + 8 t)): the
+// 32 lanes of each half of a transposed read then cover 64 distinct banks.
+template <int QW>  // 32-query blocks of the tile (chunks per 32 keys: 2 QW)
 __device__ __forceinline__ bf16x8 ds_frag(const bf16* S, int qwl, int kb, int lane) {
   const int gi = lane >> 4, i = lane & 15;
   const int r = i >> 2, q = i & 3;
   const int gq = q & 1;  // the fragment half (g of the storing lane) that holds queries 4q .. 4q+3
   const int k0 = kb + 4 * (gi >> 1) + r;
+  const int t = gi & 1;  // the 16-query half: chunk parity
   auto addr = [&](int kk) {
-    const int chunk = (kk >> 5) * 8 + qwl * 2 + (gi & 1);
-    const int slot = 32 * gq + ((kk & 31) ^ (4 * gq));
+    const int chunk = (kk >> 5) * (2 * QW) + qwl * 2 + t;
+    const int slot = 32 * gq + ((kk & 31) ^ (4 * gq + 8 * t));
     return (LDS_AS v4i16*)(S + chunk * 512 + slot * 8 + 4 * (q >> 1));
   };
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(k0));
@@ -559,10 +561,12 @@ __device__ __forceinline__ bf16x8 ds_frag(const bf16* S, int qwl, int kb, int la
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
-  constexpr int HD = 128, HB = 4;
-  constexpr uint32_t kTile = 64 * HD * 2, kStage = 2 * kTile;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+constexpr int kDqQueries = 256;  // queries per workgroup of the dQ kernel
+
+__global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
+  constexpr int HD = 128, HB = 4, QW = kDqQueries / 32;
+  constexpr uint32_t kTile = 64 * HD * 2, kStage = kTile + 64 * kDqQueries * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[3 * kStage];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   const int T = p.T;
@@ -574,7 +578,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;
-  const int q0 = qb * 128;
+  const int q0 = qb * kDqQueries;
   const int qi = q0 + wv * 32 + (lane & 31);  // this lane's query
 
   const size_t tok0 = (size_t)b * T;
@@ -582,29 +586,38 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
                               (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2));
   const rsrc_t rs = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
   const long col = (long)(h / p.G) * HD;  // this query head's key/value head
-  const int nkv = min(T - 1, q0 + 127) / 64 + 1;  // key blocks up to the diagonal
+  const int nkv = min(T - 1, q0 + kDqQueries - 1) / 64 + 1;  // key blocks up to the diagonal
 
-  // K tile: per-lane byte offsets of this wavefront's 4 blocks (4 rows each)
+  // K tile: per-lane byte offsets of this wavefront's 2 blocks (4 rows each)
   // relative to the key block's first row.  dS: this wavefront loads chunks
-  // 4 wv .. 4 wv + 3 of the tile; LDS slot `lane` of a chunk takes the
-  // stored piece of lane (li ^ 4 g) + 32 g.
-  uint32_t toff_k[4];
+  // 4 wv .. 4 wv + 3 of the tile; LDS slot `lane` of a chunk of parity t
+  // takes the stored piece of lane (li ^ (4 g + 8 t)) + 32 g.
+  uint32_t toff_k[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wv * 4 + i) * 4 + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int row = (wv * 2 + i) * 4 + (lane >> 4);
     const int cc = (lane & 15) ^ sw2(row);
     toff_k[i] = (uint32_t)(((long)row * p.ldk + col + cc * 8) * 2);
   }
-  const uint32_t src_lane = (uint32_t)((((lane & 31) ^ (4 * g)) + 32 * g) * 16);
+  const uint32_t src_lane[2] = {(uint32_t)((((lane & 31) ^ (4 * g)) + 32 * g) * 16),
+                                 (uint32_t)((((lane & 31) ^ (4 * g + 8)) + 32 * g) * 16)};
+  // the loads of key block j into stage st; blocks past the last read 0
   auto load_block = [&](int st, int j) {
+    const bool live = j < nkv;
     const int row0 = j * 64;
     const uint32_t sb = lds0 + (uint32_t)st * kStage;
 #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = live && row0 + (wv * 2 + i) * 4 + (lane >> 4) < T;  // keys past T read 0
+      dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 2 + i) * 1024u);
+    }
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = row0 + (wv * 4 + i) * 4 + (lane >> 4) < T;  // keys past T read 0
-      dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 4 + i) * 1024u);
-      const int c = wv * 4 + i;  // chunk (kwl, qwl, t) = (c / 8, (c / 2) % 4, c % 2)
-      dma16(rs, src_lane + ds_chunk(Tp, 2 * j + (c >> 3), (q0 >> 5) + ((c >> 1) & 3), c & 1),
+      // chunk (kwl, qwl, t) = (c / (2 QW), (c / 2) % QW, c % 2); c % 2 = i % 2.  A
+      // query block past the padded length reads 0 (its queries are past T).
+      const int c = wv * 4 + i;
+      const int qw = (q0 >> 5) + ((c >> 1) % QW);
+      dma16(rs, live && qw < (int)(Tp >> 5) ? src_lane[i & 1] + ds_chunk(Tp, 2 * j + c / (2 * QW), qw, c & 1) : kOOB,
             sb + kTile + (uint32_t)c * 1024u);
     }
   };
@@ -614,17 +627,25 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds128(AttnArgs p) {
   for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
 
   load_block(0, 0);
+  load_block(1, 1);
+  int cur = 0;  // stage of block j
   for (int j = 0; j < nkv; ++j) {
-    // block j landed (its loads are the only ones in flight) and every
-    // wavefront is done with the stage the next loads overwrite
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (j + 1 < nkv) load_block((j + 1) & 1, j + 1);
-    const char* sb = smem + (j & 1) * kStage;
+    // loads retire in issue order: with those of block j + 1 (6) still in
+    // flight, block j has landed; after the barrier every wavefront is done
+    // with block j - 1, whose stage the loads of block j + 2 take
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    load_block(cur == 0 ? 2 : cur - 1, j + 2);
+    const char* sb = smem + cur * kStage;
+    cur = cur == 2 ? 0 : cur + 1;
     const bf16* Ks = (const bf16*)sb;
     const bf16* Ss = (const bf16*)(sb + kTile);
+    // a key block wholly past this wavefront's last query adds nothing, and
+    // its chunks were never stored (the dK/dV workgroup of those keys starts
+    // at a later query): skip it
+    if (64 * j > q0 + 32 * wv + 31) continue;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 sf = ds_frag(Ss, wv, kk * 16, lane);
+      const bf16x8 sf = ds_frag<QW>(Ss, wv, kk * 16, lane);
 #pragma unroll
       for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 16, lane), sf, dq[x]);
     }
@@ -1330,7 +1351,7 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
       if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
       attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
       attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
-      attn_bwd_dq_ds128<<<gq, 256, 0, s>>>(p);
+      attn_bwd_dq_ds128<<<dim3((p.T + kDqQueries - 1) / kDqQueries, p.B * p.H), 512, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
       attn_bwd_dkdv_mfma<64><<<gk, 256, 0, s>>>(p);

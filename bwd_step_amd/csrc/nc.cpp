@@ -116,6 +116,7 @@ struct nc_ctx {
   char* ws = nullptr;
   uint64_t ws_bytes = 0;
   Prof prof;
+  bool poison = false;  // nc_debug_poison_workspace
 };
 
 namespace {
@@ -230,6 +231,22 @@ void build_layout(nc_ctx* x) {
 }
 
 __global__ void clear_status_kernel(int* s) { *s = 0; }
+
+// Debug: fill n 16-byte words with all-ones bytes (NaN as fp32 and bf16).
+__global__ void poison_kernel(uint4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+}
+
+// With poisoning on, every byte of the workspace past the status block is
+// made NaN before a call, so a kernel that read workspace memory it had not
+// written would change the result.
+int maybe_poison(nc_ctx* ctx, const Plan& P) {
+  if (!ctx->poison || P.total <= 256) return NC_OK;
+  const size_t n = (P.total - 256) / 16;
+  poison_kernel<<<2048, 256, 0, ctx->stream>>>((uint4*)(ctx->ws + 256), n);
+  return hipGetLastError() == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
 
 int clear_status(void* ws, hipStream_t s) {
   clear_status_kernel<<<1, 1, 0, s>>>((int*)ws);
@@ -759,6 +776,7 @@ int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens, 
   if (!ctx->ws) return NC_ERR_WORKSPACE;
   const Plan P = make_plan(ctx->cfg, batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  TRY(maybe_poison(ctx, P));
   TRY(launch_count_targets(targets, (long)batch * ctx->cfg.seq_len, (int*)(ctx->ws + P.status), ctx->stream));
   TRY(run_forward(ctx, P, params, tokens, batch, ctx->cfg.seq_len));
   return run_backward(ctx, P, params, tokens, targets, batch, loss, grads, accumulate, true);
@@ -773,6 +791,7 @@ int nc_forward_backward_accum(nc_ctx* ctx, const void* params, const int32_t* to
   const Plan P = make_plan(ctx->cfg, micro_batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
   const long T = ctx->cfg.seq_len;
+  TRY(maybe_poison(ctx, P));
   // one count over the whole step: every microbatch is scaled by 1 / (counted targets of the step)
   TRY(launch_count_targets(targets, (long)n_micro * micro_batch * T, (int*)(ctx->ws + P.status), ctx->stream));
   for (int m = 0; m < n_micro; ++m) {
@@ -791,6 +810,7 @@ int nc_forward_logits(nc_ctx* ctx, const void* params, const int32_t* tokens, in
   if (!ctx->ws) return NC_ERR_WORKSPACE;
   const Plan P = make_plan(ctx->cfg, batch);
   if (ctx->ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  TRY(maybe_poison(ctx, P));
   TRY(run_forward(ctx, P, params, tokens, batch, ctx->cfg.seq_len));
   const nc_config& c = ctx->cfg;
   const size_t es = c.dtype == NC_BF16 ? 2 : 4;
@@ -873,6 +893,13 @@ int nc_check(nc_ctx* ctx) {
   if (!ctx) return NC_ERR_NULL;
   if (!ctx->ws) return NC_ERR_WORKSPACE;
   return read_status(ctx->ws, ctx->stream);
+}
+
+int nc_debug_poison_workspace(nc_ctx* ctx, int on) {
+  if (!ctx) return NC_ERR_NULL;
+  if (on != 0 && on != 1) return NC_ERR_ARG;
+  ctx->poison = on != 0;
+  return NC_OK;
 }
 
 int nc_profile_enable(nc_ctx* ctx, int on) {

@@ -259,6 +259,18 @@ int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, con
 int nc_check(nc_ctx* ctx);
 
 /*
+ * Debugging aid (no passage of the pages: it checks this library's use of
+ * the caller's workspace).  With on = 1, nc_forward_backward,
+ * nc_forward_backward_accum and nc_forward_logits first fill the whole
+ * workspace except its 256-byte status block with all-ones bytes (NaN in
+ * fp32 and bf16), so any read of workspace memory not written earlier in the
+ * same call would change the results; they must come out bitwise identical
+ * to a run with on = 0.  Costs one fill pass per call.
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (on not 0 or 1).
+ */
+int nc_debug_poison_workspace(nc_ctx* ctx, int on);
+
+/*
  * Tracing: per-kernel-class GPU time.  When enabled, every launch made by
  * nc_forward_backward / nc_forward_logits is bracketed by HIP events on the
  * context's stream and credited to its class ("gemm", "attn_fwd",

@@ -72,6 +72,7 @@ RAGGED = oracle.derive_config(3, vocab=576, seq_len=100, d_model=192, n_heads=3,
 # ragged LM-head column tile (V = 1152: its last tile is moved back by one
 # 128-column softmax segment)
 MID = oracle.derive_config(2, vocab=1152, seq_len=136, d_model=640, n_heads=5, head_dim=128, d_ff=2560)
+LONG = oracle.derive_config(1, vocab=640, seq_len=600, d_model=256, n_heads=2, head_dim=128, d_ff=512)
 
 
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
@@ -260,3 +261,27 @@ def test_nonfinite_loss_status():
     assert model.check() == 5
     assert not math.isfinite(loss.item())
     assert model.check() == 0
+
+
+@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3), ("mid", 2), ("long", 1)])
+def test_poisoned_workspace_gives_identical_results(which, B):
+    """With the workspace NaN-filled before the step, loss and gradients are
+    bitwise those of a normal step: no kernel reads workspace memory it did
+    not write in the same call (mid: stored-dS columns past the sequence,
+    moved-back GEMM tiles; ragged: partial tiles everywhere; long: 600
+    tokens at head_dim 128, so the dQ kernel's 256-query tiles meet key
+    blocks whose dS chunks the dK/dV kernel never stores)."""
+    cfg = {"tiny": TINY, "ragged": RAGGED, "mid": MID, "long": LONG}[which]
+    banner(f"poisoned workspace, {which} bf16 B={B}")
+    model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, "bf16", seed=8)
+    l1, g1 = run_step(model, flat, tok_d, tgt_d)
+    logits = torch.empty(B, cfg.seq_len, cfg.vocab, dtype=torch.float32, device="cuda")
+    model.forward_logits(flat, tok_d, logits)
+    model.poison_workspace(True)
+    l2, g2 = run_step(model, flat, tok_d, tgt_d)
+    logits2 = torch.empty_like(logits)
+    model.forward_logits(flat, tok_d, logits2)
+    model.poison_workspace(False)
+    assert l1.item() == l2.item()
+    assert torch.equal(g1, g2)
+    assert torch.equal(logits, logits2)
