@@ -264,6 +264,8 @@ def main():
     ap.add_argument("--config", default="d20", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--resid-fp32", action="store_true",
+                    help="add the attention / MLP outputs to the residual stream in fp32 (nc_set_residual_fp32)")
     ap.add_argument("--op", choices=["attention", "lmhead", "copy", "optim", "decode"], default=None)
     ap.add_argument("--decode-batch", type=int, default=1, help="sequences per decode step (--op decode)")
     ap.add_argument("--context", type=int, default=1024, help="prompt length before the timed decode step")
@@ -286,6 +288,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     model = bwd_step_amd.Model(depth, vocab=65536, seq_len=2048, max_batch=B, dtype="bf16")
+    if args.resid_fp32:
+        model.set_residual_fp32(True)
     cfg = model.config
     T, V = cfg["seq_len"], cfg["vocab"]
     shapes = [(name, (rows, cols)) for name, _, rows, cols in model.layout()]
@@ -369,7 +373,7 @@ def main():
         kernels[name] = ent
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC.replace("depth-20", f"depth-{depth}"),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -388,6 +392,7 @@ def main():
             "seq_len": T,
             "depth": depth,
             "parallelism": "single GPU",
+            "residual_addend": "fp32" if args.resid_fp32 else "bf16",
         },
         "mfu": round(mfu, 4),
         "model_flops_per_token": fpt,

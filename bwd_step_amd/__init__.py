@@ -162,6 +162,11 @@ class Model:
         """Synchronise and return the device status code (0 = ok)."""
         return int(lib().nc_check(self._h))
 
+    def set_residual_fp32(self, on=True):
+        """bf16 path: add the attention / MLP outputs to the residual stream in
+        fp32 in the projection epilogue instead of as bf16 (nc_set_residual_fp32)."""
+        check(lib().nc_set_residual_fp32(self._h, int(bool(on))), "nc_set_residual_fp32")
+
     def poison_workspace(self, on=True):
         """Debug: NaN-fill the workspace before each call (nc_debug_poison_workspace)."""
         check(lib().nc_debug_poison_workspace(self._h, int(bool(on))), "nc_debug_poison_workspace")

@@ -74,6 +74,7 @@ SIGNATURES = {
     "nc_decode_static": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp]),
     "nc_check": (_i, [_vp]),
     "nc_debug_poison_workspace": (_i, [_vp, _i]),
+    "nc_set_residual_fp32": (_i, [_vp, _i]),
     "nc_profile_enable": (_i, [_vp, _i]),
     "nc_profile_read": (_i, [_vp, ctypes.POINTER(NcProfEntry), _i]),
     "nc_attention_workspace_bytes": (_u64, [_i, _i, _i, _i, _i]),

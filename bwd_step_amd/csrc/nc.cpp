@@ -117,6 +117,7 @@ struct nc_ctx {
   uint64_t ws_bytes = 0;
   Prof prof;
   bool poison = false;  // nc_debug_poison_workspace
+  bool resid_fp32 = false;  // nc_set_residual_fp32
 };
 
 namespace {
@@ -373,7 +374,8 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
   PROF(pf, PC_OTHER, 0, 0, launch_rope_table(cs, T, hd, c.rope_base, s));
   // bf16 path: the output projections store their sublayer output y in bf16
   // and the next RMSNorm adds it to the fp32 stream x (x += y, then the norm);
-  // fp32 path: the projections add into x in their epilogue.
+  // fp32 path, and bf16 with nc_set_residual_fp32: the projections add their
+  // fp32 accumulators into x in their epilogue.
   void* ybuf = W + P.dx_lp;
   const void* pend = nullptr;
   auto norm = [&](void* out, float* r) -> int {
@@ -388,7 +390,7 @@ int run_forward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* t
     return NC_OK;
   };
   auto proj_out = [&](GemmCall& g) {
-    if (dt == NC_BF16) {
+    if (dt == NC_BF16 && !ctx->resid_fp32) {
       g.epi = EPI_LP; g.e.c_lp = ybuf; g.e.ld_lp = d;
       pend = ybuf;
     } else {
@@ -899,6 +901,13 @@ int nc_debug_poison_workspace(nc_ctx* ctx, int on) {
   if (!ctx) return NC_ERR_NULL;
   if (on != 0 && on != 1) return NC_ERR_ARG;
   ctx->poison = on != 0;
+  return NC_OK;
+}
+
+int nc_set_residual_fp32(nc_ctx* ctx, int on) {
+  if (!ctx) return NC_ERR_NULL;
+  if (on != 0 && on != 1) return NC_ERR_ARG;
+  ctx->resid_fp32 = on != 0;
   return NC_OK;
 }
 

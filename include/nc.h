@@ -259,6 +259,20 @@ int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, con
 int nc_check(nc_ctx* ctx);
 
 /*
+ * Precision of the residual stream's addends on the bf16 path ("nanochat
+ * explainer", Modern architecture choices: each block's attention and MLP
+ * outputs are added to the residual stream).  The stream x is fp32 on both
+ * paths.  With on = 0 (the default) the attention and MLP output projections
+ * store their result rounded to bf16 and the next RMSNorm adds it to x; with
+ * on = 1 they add their fp32 accumulators into x in the product's epilogue,
+ * as the fp32 path always does.  Affects nc_forward_backward,
+ * nc_forward_backward_accum, nc_forward_logits and nc_prefill; no effect on
+ * an fp32 context or on nc_decode (which adds in fp32).
+ * Errors: NC_ERR_NULL, NC_ERR_ARG (on not 0 or 1).
+ */
+int nc_set_residual_fp32(nc_ctx* ctx, int on);
+
+/*
  * Debugging aid (no passage of the pages: it checks this library's use of
  * the caller's workspace).  With on = 1, nc_forward_backward,
  * nc_forward_backward_accum and nc_forward_logits first fill the whole

@@ -75,6 +75,8 @@ int main(void) {
   CHECK(nc_decode_static(ctx, &f, ids, ids, 64, &f, 65536, &f, ids) == NC_ERR_WORKSPACE);
   CHECK(nc_debug_poison_workspace(ctx, 2) == NC_ERR_ARG);
   CHECK(nc_debug_poison_workspace(ctx, 1) == NC_OK && nc_debug_poison_workspace(ctx, 0) == NC_OK);
+  CHECK(nc_set_residual_fp32(NULL, 1) == NC_ERR_NULL && nc_set_residual_fp32(ctx, 2) == NC_ERR_ARG);
+  CHECK(nc_set_residual_fp32(ctx, 1) == NC_OK && nc_set_residual_fp32(ctx, 0) == NC_OK);
   CHECK(nc_profile_enable(NULL, 1) == NC_ERR_NULL);
   nc_optim_config oc;
   memset(&oc, 0, sizeof(oc));

@@ -203,18 +203,28 @@ def _full_depth20_reference():
     return _FULL
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("dt", ["bf16", "fp32"])
-def test_full_depth20_one_sequence_matches_oracle(dt):
-    """All 20 layers at the real widths, one sequence of 2048: every gradient tensor."""
-    banner(f"full depth-20, B=1, {dt}, against the oracle")
-    R = _full_depth20_reference()
+def _full_depth_run(R, depth, mode):
+    """One step of the full-depth model on R's sequence; mode is "fp32", "bf16"
+    (sublayer outputs added to the fp32 residual stream as bf16) or
+    "bf16-resid32" (added as fp32 in the projection epilogue)."""
+    dt = "fp32" if mode == "fp32" else "bf16"
     cfg, shapes = R["cfg"], R["shapes"]
-    model = bwd_step_amd.Model(20, max_batch=1, dtype=dt)
+    model = bwd_step_amd.Model(depth, max_batch=1, dtype=dt)
+    if mode == "bf16-resid32":
+        model.set_residual_fp32(True)
     flat = to_dev(pack(R["params"], shapes), dt)
     loss, grads = run_step(model, flat, to_dev(R["tok"]), to_dev(R["tgt"]))
     worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, R["loss"], R["grads"])
-    print(f"worst rel-L2 {worst}", flush=True)
+    print(f"{mode}: loss rel err {abs(loss.item() - R['loss']) / R['loss']:.3g}, worst grad rel-L2 {worst}", flush=True)
+    return worst
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", ["bf16", "bf16-resid32", "fp32"])
+def test_full_depth20_one_sequence_matches_oracle(mode):
+    """All 20 layers at the real widths, one sequence of 2048: every gradient tensor."""
+    banner(f"full depth-20, B=1, {mode}, against the oracle")
+    _full_depth_run(_full_depth20_reference(), 20, mode)
 
 
 _FULL26 = {}
@@ -235,17 +245,15 @@ def _full_depth26_reference():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("dt", ["bf16", "fp32"])
-def test_full_depth26_one_sequence_matches_oracle(dt):
-    """All 26 layers at the depth-26 widths, one Zipf(1.1) sequence of 2048: every gradient tensor."""
-    banner(f"full depth-26, B=1, Zipf ids, {dt}, against the oracle")
-    R = _full_depth26_reference()
-    cfg, shapes = R["cfg"], R["shapes"]
-    model = bwd_step_amd.Model(26, max_batch=1, dtype=dt)
-    flat = to_dev(pack(R["params"], shapes), dt)
-    loss, grads = run_step(model, flat, to_dev(R["tok"]), to_dev(R["tgt"]))
-    worst = compare(cfg, dt, loss.item(), to_np(grads), shapes, R["loss"], R["grads"])
-    print(f"worst rel-L2 {worst}", flush=True)
+@pytest.mark.parametrize("mode", ["bf16", "bf16-resid32", "fp32"])
+def test_full_depth26_one_sequence_matches_oracle(mode):
+    """All 26 layers at the depth-26 widths, one Zipf(1.1) sequence of 2048:
+    every gradient tensor.  The bf16 addend of the residual stream is kept
+    only while its worst gradient error after 26 layers stays within 2e-2."""
+    banner(f"full depth-26, B=1, Zipf ids, {mode}, against the oracle")
+    worst = _full_depth_run(_full_depth26_reference(), 26, mode)
+    if mode == "bf16":
+        assert worst[0] <= 2e-2, worst
 
 
 def test_nonfinite_loss_status():
