@@ -8,12 +8,14 @@
 // increasing n, with no floating-point atomics, so the result is bitwise
 // reproducible.  Steps:
 //   1. a stable LSD radix sort (8-bit digits) of (id, position) pairs; each
-//      pass is a per-tile digit histogram, one exclusive scan, and a stable
-//      scatter whose in-tile ranks come from wavefront ballots;
+//      pass is a per-tile digit histogram, an exclusive scan (per digit over
+//      the tiles, plus each digit's base), and a stable scatter whose in-tile
+//      ranks come from wavefront ballots;
 //   2. the sorted positions are cut into pieces of kPiece entries; each piece
 //      sums dx over every run of equal ids inside it, in order, and stores the
-//      run's sum at the run's first sorted index;
-//   3. each vocabulary row binary-searches its segment [lo, hi) and adds the
+//      run's sum at the run's first sorted index; the first sorted index of
+//      every id, lo[v] (lo[V] = N), is written from the sorted ids;
+//   3. each vocabulary row takes its segment [lo[v], lo[v + 1]) and adds the
 //      partial sums that start at lo and at every piece boundary inside it.
 // Long segments (skewed ids) are thus split over many pieces and reduced in a
 // fixed order.
@@ -111,35 +113,69 @@ __global__ void __launch_bounds__(256) sort_hist_kernel(const int32_t* __restric
   hist[threadIdx.x * ntiles + blockIdx.x] = tot[threadIdx.x];
 }
 
-// Exclusive scan of n ints in place by one block of 1024 threads.
-__global__ void __launch_bounds__(1024) scan_kernel(int* __restrict__ a, int n) {
-  __shared__ int part[1024];
-  const int per = (n + 1023) / 1024;
-  const int b = threadIdx.x * per;
-  int s = 0;
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) s += a[b + i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
+// Offsets of the scatter from the per-tile digit counts hist[digit][tile]:
+// in place, hist[d][t] becomes the count of digit d in tiles before t, and
+// base[d] the count of all digits below d.  One block of 16 wavefronts; a
+// wavefront scans whole digit rows (four consecutive counts per lane, so the
+// loads are coalesced), then one wavefront scans the 256 digit totals.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(x, off, 64);
+    if (lane >= off) x += t;
   }
-  int run = threadIdx.x ? part[threadIdx.x - 1] : 0;
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) {
-      const int v = a[b + i];
-      a[b + i] = run;
-      run += v;
+  return x;
+}
+__global__ void __launch_bounds__(1024) scan_kernel(int* __restrict__ hist, int ntiles, int* __restrict__ base) {
+  __shared__ int tot[256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int d = wv; d < 256; d += 16) {
+    int* row = hist + (size_t)d * ntiles;
+    int run = 0;
+    for (int c0 = 0; c0 < ntiles; c0 += 256) {
+      int v[4];
+      int sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = c0 + 4 * lane + e;
+        v[e] = i < ntiles ? row[i] : 0;
+        sum += v[e];
+      }
+      const int incl = wave_incl_scan(sum, lane);
+      int ex = run + incl - sum;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = c0 + 4 * lane + e;
+        if (i < ntiles) row[i] = ex;
+        ex += v[e];
+      }
+      run += __shfl(incl, 63, 64);
     }
+    if (lane == 0) tot[d] = run;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int v[4];
+    int sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = tot[4 * lane + e];
+      sum += v[e];
+    }
+    int ex = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      base[4 * lane + e] = ex;
+      ex += v[e];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* __restrict__ keys_in,
                                                            const int32_t* __restrict__ vals_in,
                                                            const int32_t* __restrict__ tok, int N, int V, int shift,
-                                                           const int* __restrict__ offs, int ntiles,
+                                                           const int* __restrict__ offs,
+                                                           const int* __restrict__ base, int ntiles,
                                                            int32_t* __restrict__ keys_out,
                                                            int32_t* __restrict__ vals_out) {
   __shared__ int cnt[4 * 256];
@@ -158,7 +194,7 @@ __global__ void __launch_bounds__(256) sort_scatter_kernel(const int32_t* __rest
   const int digit = (key >> shift) & 255;
   const int rank = tile_rank(digit, valid, cnt, nullptr);
   if (valid) {
-    const int dst = offs[digit * ntiles + blockIdx.x] + rank;
+    const int dst = base[digit] + offs[digit * ntiles + blockIdx.x] + rank;
     keys_out[dst] = key;
     vals_out[dst] = val;
   }
@@ -194,24 +230,27 @@ __global__ void __launch_bounds__(256) piece_sum_kernel(const float* __restrict_
   }
 }
 
-__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
+// lo[v] = the first sorted index whose id is >= v, for v = 0 .. V (lo[V] =
+// N): thread i (0 <= i <= N) writes every v in (id[i - 1], id[i]] (with
+// id[-1] = -1, id[N] = V), so each v is written exactly once.
+__global__ void __launch_bounds__(256) seg_lo_kernel(const int32_t* __restrict__ skey, int N, int V,
+                                                     int32_t* __restrict__ lo) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i > N) return;
+  const int a = i == 0 ? -1 : skey[i - 1];
+  const int b = i == N ? V : skey[i];
+  for (int v = a + 1; v <= b; ++v) lo[v] = i;
 }
 
 // Wavefront per vocabulary row.
 __global__ void __launch_bounds__(256) row_combine_kernel(const float* __restrict__ partial,
-                                                          const int32_t* __restrict__ skey, int N, int d, int V,
+                                                          const int32_t* __restrict__ seg_lo, int d, int V,
                                                           float* __restrict__ dE, int accumulate) {
   const int v = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (v >= V) return;
-  const int lo = lower_bound_i32(skey, N, v);
-  const int hi = lower_bound_i32(skey, N, v + 1);
+  const int lo = seg_lo ? seg_lo[v] : 0;
+  const int hi = seg_lo ? seg_lo[v + 1] : 0;
   float* dst = dE + (size_t)v * d;
   for (int c = lane * 4; c < d; c += 256) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -232,8 +271,8 @@ static inline size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 uint64_t embed_bwd_ws_bytes(int N, int d, int V) {
   const int ntiles = (N + kSortTile - 1) / kSortTile;
-  (void)V;
-  return 4 * al256((size_t)N * 4) + al256((size_t)256 * ntiles * 4) + al256((size_t)N * d * 4);
+  return 4 * al256((size_t)N * 4) + al256((size_t)256 * ntiles * 4) + al256(256 * 4) + al256(((size_t)V + 1) * 4) +
+         al256((size_t)N * d * 4);
 }
 
 int launch_embed_bwd(const float* dx, const int32_t* tok, float* dE, int N, int d, int V, int accumulate, void* ws,
@@ -246,6 +285,8 @@ int launch_embed_bwd(const float* dx, const int32_t* tok, float* dE, int N, int 
   int32_t* kb = (int32_t*)p; p += al256((size_t)N * 4);
   int32_t* vb = (int32_t*)p; p += al256((size_t)N * 4);
   int* hist = (int*)p; p += al256((size_t)256 * ntiles * 4);
+  int* base = (int*)p; p += al256(256 * 4);
+  int32_t* seg_lo = (int32_t*)p; p += al256(((size_t)V + 1) * 4);
   float* partial = (float*)p;
   if (N > 0) {
     int bits = 1;
@@ -257,18 +298,19 @@ int launch_embed_bwd(const float* dx, const int32_t* tok, float* dE, int N, int 
     int32_t* vout = va;
     for (int ps = 0; ps < passes; ++ps) {
       sort_hist_kernel<<<ntiles, 256, 0, s>>>(kin, tok, N, V, 8 * ps, hist, ntiles);
-      scan_kernel<<<1, 1024, 0, s>>>(hist, 256 * ntiles);
-      sort_scatter_kernel<<<ntiles, 256, 0, s>>>(kin, vin, tok, N, V, 8 * ps, hist, ntiles, kout, vout);
+      scan_kernel<<<1, 1024, 0, s>>>(hist, ntiles, base);
+      sort_scatter_kernel<<<ntiles, 256, 0, s>>>(kin, vin, tok, N, V, 8 * ps, hist, base, ntiles, kout, vout);
       kin = kout;
       vin = vout;
       kout = (kout == ka) ? kb : ka;
       vout = (vout == va) ? vb : va;
     }
     piece_sum_kernel<<<(N + kPiece - 1) / kPiece, 256, 0, s>>>(dx, kin, vin, N, d, partial);
-    row_combine_kernel<<<(V + 3) / 4, 256, 0, s>>>(partial, kin, N, d, V, dE, accumulate);
+    seg_lo_kernel<<<(N + 1 + 255) / 256, 256, 0, s>>>(kin, N, V, seg_lo);
+    row_combine_kernel<<<(V + 3) / 4, 256, 0, s>>>(partial, seg_lo, d, V, dE, accumulate);
   } else if (!accumulate) {
     // no tokens: every row is absent
-    row_combine_kernel<<<(V + 3) / 4, 256, 0, s>>>(nullptr, nullptr, 0, d, V, dE, 0);
+    row_combine_kernel<<<(V + 3) / 4, 256, 0, s>>>(nullptr, nullptr, d, V, dE, 0);
   }
   NC_LAUNCH_CHECK();
   return 0;
