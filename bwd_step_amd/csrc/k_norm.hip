@@ -302,6 +302,11 @@ __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(QkArgs a, const fl
   const bool ok = vec < N * Hw;
   const int n = ok ? vec / Hw : 0, h = ok ? vec - (vec / Hw) * Hw : 0;
   const T* src = (const T*)a.in[w] + (size_t)n * a.ld_in[w] + h * (2 * HALF);
+  // the RoPE table entries first, so that their latency overlaps that of the
+  // row loads instead of following the reduction
+  const int t = n % Tseq;
+  const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
+  const f32x4 cs01 = csp[0], cs23 = csp[1];  // (cos, sin) of pairs i, i+1 | i+2, i+3
   f32x4 u0 = ok ? load4(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 u1 = ok ? load4(src + i + HALF) : f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = u0.x * u0.x + u0.y * u0.y + u0.z * u0.z + u0.w * u0.w + u1.x * u1.x + u1.y * u1.y + u1.z * u1.z +
@@ -310,14 +315,62 @@ __global__ void __launch_bounds__(256) qknorm_rope_fwd_kernel(QkArgs a, const fl
   for (int o = LPV / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float rr = 1.0f / sqrtf(ss / (float)(2 * HALF) + eps);
   if (!ok) return;
-  const int t = n % Tseq;
-  const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
-  const f32x4 cs01 = csp[0], cs23 = csp[1];  // (cos, sin) of pairs i, i+1 | i+2, i+3
   const f32x4 c{cs01.x, cs01.z, cs23.x, cs23.z}, sn{cs01.y, cs01.w, cs23.y, cs23.w};
   const f32x4 y0 = u0 * rr, y1 = u1 * rr;
   T* dst = (T*)a.out[w] + (size_t)n * a.ld_out[w] + h * (2 * HALF);
   store4(dst + i, y0 * c - y1 * sn);
   store4(dst + i + HALF, y0 * sn + y1 * c);
+  if (i == 0) a.r[w][vec] = rr;
+}
+
+// bf16 rows with HALF a multiple of 8: the same, with 8 pairs per lane so
+// that every row access is 16 bytes per lane (HALF / 8 lanes per vector).
+template <int HALF>
+__global__ void __launch_bounds__(256) qknorm_rope_fwd16_kernel(QkArgs a, const float* __restrict__ cs, int N, int H,
+                                                                int Tseq, float eps) {
+  constexpr int LPV = HALF / 8, VPW = 64 / LPV;
+  const int w = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int vec = (blockIdx.x * 4 + (threadIdx.x >> 6)) * VPW + lane / LPV;
+  const int i = (lane % LPV) * 8;
+  const int Hw = a.heads[w];
+  const bool ok = vec < N * Hw;
+  const int n = ok ? vec / Hw : 0, h = ok ? vec - (vec / Hw) * Hw : 0;
+  const bf16* src = (const bf16*)a.in[w] + (size_t)n * a.ld_in[w] + h * (2 * HALF);
+  const int t = n % Tseq;
+  const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
+  f32x4 cv[4];  // (cos, sin) of pairs i .. i + 7
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cv[e] = csp[e];
+  const u32x4 z{0u, 0u, 0u, 0u};
+  const u32x4 w0 = ok ? *reinterpret_cast<const u32x4*>(src + i) : z;
+  const u32x4 w1 = ok ? *reinterpret_cast<const u32x4*>(src + i + HALF) : z;
+  float u0[8], u1[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u0[2 * e] = bf16lo_to_f32(w0[e]);
+    u0[2 * e + 1] = bf16hi_to_f32(w0[e]);
+    u1[2 * e] = bf16lo_to_f32(w1[e]);
+    u1[2 * e + 1] = bf16hi_to_f32(w1[e]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(u0[e], u0[e], fmaf(u1[e], u1[e], ss));
+#pragma unroll
+  for (int o = LPV / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float rr = 1.0f / sqrtf(ss / (float)(2 * HALF) + eps);
+  if (!ok) return;
+  u32x4 o0, o1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x4 c2 = cv[e];  // pairs i + 2e (c2.x, c2.y) and i + 2e + 1 (c2.z, c2.w)
+    const float a0 = u0[2 * e] * rr, b0 = u1[2 * e] * rr, a1 = u0[2 * e + 1] * rr, b1 = u1[2 * e + 1] * rr;
+    o0[e] = pack_bf16x2(a0 * c2.x - b0 * c2.y, a1 * c2.z - b1 * c2.w);
+    o1[e] = pack_bf16x2(a0 * c2.y + b0 * c2.x, a1 * c2.w + b1 * c2.z);
+  }
+  bf16* dst = (bf16*)a.out[w] + (size_t)n * a.ld_out[w] + h * (2 * HALF);
+  *reinterpret_cast<u32x4*>(dst + i) = o0;
+  *reinterpret_cast<u32x4*>(dst + i + HALF) = o1;
   if (i == 0) a.r[w][vec] = rr;
 }
 
@@ -377,6 +430,16 @@ static int qk_fwd_dispatch(const QkArgs& a, const float* cs, int N, int H, int h
   const int vecs = N * H;
   if (vecs == 0) return 0;
   const int half = hd / 2;
+  if constexpr (sizeof(T) == 2) {
+    if (half == 64 || half == 32) {
+      const int vpb16 = 4 * (64 / (half / 8));
+      dim3 g16((vecs + vpb16 - 1) / vpb16, 2);
+      if (half == 64) qknorm_rope_fwd16_kernel<64><<<g16, 256, 0, s>>>(a, cs, N, H, Tseq, eps);
+      else qknorm_rope_fwd16_kernel<32><<<g16, 256, 0, s>>>(a, cs, N, H, Tseq, eps);
+      NC_LAUNCH_CHECK();
+      return 0;
+    }
+  }
   const int vpb = 4 * (64 / (half / 4));
   dim3 grid((vecs + vpb - 1) / vpb, 2);
   switch (half) {
