@@ -167,7 +167,9 @@ def attention_oracle(q, k, v, do, base, eps):
 
 
 @pytest.mark.parametrize("dt,hd", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 32)])
-@pytest.mark.parametrize("B,H,T", [(2, 2, 200), (1, 3, 64), (1, 1, 1)])
+# T = 300: a second, partial 256-query tile of the head_dim-128 dQ kernel;
+# T = 513: one key past a 512 boundary (a nearly empty last block everywhere)
+@pytest.mark.parametrize("B,H,T", [(2, 2, 200), (1, 3, 64), (1, 1, 1), (1, 2, 300), (1, 1, 513)])
 def test_attention_fwd_bwd(dt, hd, B, H, T):
     banner(f"attention {dt} hd={hd} B={B} H={H} T={T}")
     shp = (B, T, H, hd)
