@@ -76,9 +76,9 @@ LONG = oracle.derive_config(1, vocab=640, seq_len=600, d_model=256, n_heads=2, h
 
 
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
-@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3), ("mid", 2)])
+@pytest.mark.parametrize("which,B", [("tiny", 2), ("ragged", 3), ("mid", 2), ("long", 1)])
 def test_step_matches_oracle_small(dt, which, B):
-    cfg = {"tiny": TINY, "ragged": RAGGED, "mid": MID}[which]
+    cfg = {"tiny": TINY, "ragged": RAGGED, "mid": MID, "long": LONG}[which]
     banner(f"step {which} {dt} B={B}")
     model, shapes, params, flat, tok_d, tgt_d, tok, tgt = setup(cfg, B, dt)
     loss, grads = run_step(model, flat, tok_d, tgt_d)
