@@ -969,6 +969,348 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
     }
 }
 
+// dK, dV with two wavefronts per 32 keys: 512 threads, 128 keys per
+// workgroup.  Wavefronts p and p + 4 share a SIMD and own keys
+// k0 + 32 p .. + 31:
+//   the P wavefront (p) holds K: S = qh kh^T, P = exp2(S c - lse) (masked on
+//     the diagonal and past T), dV += P^T dO; it hands P (the bf16 B operand
+//     it built for dV) to its partner through LDS;
+//   the dS wavefront (p + 4) holds -V: its dP accumulator starts at D and
+//     ends at D - dP, -dS = P (D - dP) with the partner's P, dK' += (-dS)^T
+//     qh; it stores -dS for the dQ kernel (lane-major chunks, ds_chunk).
+// Each wavefront keeps one accumulator set (half of the single-wavefront
+// kernel's registers), so two share a SIMD and one's exponentials, products
+// or LDS waits overlap the other's matrix products.
+//
+// Blocks of 64 queries (qh, dO tiles; lse, D) stream through three LDS
+// stages; P goes through one of two exchange buffers.  One workgroup barrier
+// per block, X_j: between X_{j-1} and X_j every wavefront issues the loads of
+// block j + 1 (into the stage of block j - 2, whose last readers finished
+// before X_{j-1}), then the P wavefront runs S, P (writing P_j) and dV of
+// block j, the dS wavefront dS, dK of block j - 1 (reading P_{j-1}) and dP
+// of block j.  At X_j each wavefront has waited for its own
+// loads of block j + 1, so after it the whole block is in LDS; exchange
+// buffer j & 1 is rewritten two blocks later, after every reader of P_j
+// passed X_{j+1}.
+//
+// LDS (bytes): qh tiles of the three stages [0, 48K), dO tiles [48K, 96K)
+// (64 rows x 256 bytes, sw2 chunk swizzle), the lse and D vectors of stage st
+// at 96K + 2K st and 1K beyond, the exchange buffers from 102K (buffer x,
+// pair p, fragment f at 16K x + 4K p + 1K f, lane l's 16 bytes at 16 l).
+// Each wavefront keeps the per-lane byte offsets of its fragment reads in
+// registers and moves them to the next stage once per block (a uniform
+// delta), so a read is one register plus an immediate offset.
+constexpr uint32_t kPrTile = 64 * 128 * 2;
+constexpr uint32_t kPrQ = 0, kPrO = 3 * kPrTile, kPrV = 6 * kPrTile, kPrX = kPrV + 3 * 2048;
+constexpr uint32_t kPrBytes = kPrX + 2 * 16384;
+
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  __shared__ __attribute__((aligned(1024))) char smem[kPrBytes];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int T = p.T;
+  const int nkb = gridDim.x;
+  const int lin = xcd_block(blockIdx.x + nkb * blockIdx.y, nkb * gridDim.y);
+  const int kbk = lin % nkb;  // key blocks of one (b, h) in turn, the longest first
+  const int bh = lin / nkb, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pr = wv & 3;        // the pair, i.e. the 32 keys
+  const bool pwave = wv < 4;    // the P wavefront of its pair (else the dS wavefront)
+  const int g = lane >> 5, li = lane & 31;
+  const int k0 = kbk * 128;
+  const int wk = k0 + pr * 32;  // the pair's first key
+  const int kj = wk + li;       // this lane's key
+  const size_t tok0 = (size_t)b * T;
+  const rsrc_t rq = make_rsrc((const bf16*)p.q + tok0 * p.ldq,
+                              (uint32_t)(((size_t)(T - 1) * p.ldq + (size_t)p.H * HD) * 2));
+  const rsrc_t ro = make_rsrc((const bf16*)p.dout + tok0 * p.lddo,
+                              (uint32_t)(((size_t)(T - 1) * p.lddo + (size_t)p.H * HD) * 2));
+  // wavefront 0 loads lse (base 2), wavefront 1 D
+  const rsrc_t rv = make_rsrc(wv == 1 ? (const void*)(p.Dbuf + (size_t)bh * T) : (const void*)(p.lse + (size_t)bh * T),
+                              (uint32_t)T * 4u);
+  const long col = (long)h * HD;
+  const int qb0 = k0 / 64;
+  const int nb = (T + 63) / 64 - qb0;  // query blocks at or after the diagonal
+  const float c = p.scale_log2;
+
+  // this wavefront's loads of a block: slots wv and wv + 8 (4 rows each) of
+  // the qh and dO tiles; wavefronts 0 and 1 also load a vector
+  uint32_t toff_q[2], toff_o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (wv + 8 * i) * 4 + (lane >> 4);
+    const int cc = (lane & 15) ^ sw2(row);
+    toff_q[i] = (uint32_t)(((long)row * p.ldq + col + cc * 8) * 2);
+    toff_o[i] = (uint32_t)(((long)row * p.lddo + col + cc * 8) * 2);
+  }
+  auto load_block = [&](int j) {
+    const uint32_t st = (uint32_t)(j % 3);
+    const int row0 = j < nb ? (qb0 + j) * 64 : T;  // blocks past the last read 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t slot = st * kPrTile + (uint32_t)(wv + 8 * i) * 1024u;
+      const bool ok = row0 + (wv + 8 * i) * 4 + (lane >> 4) < T;
+      dma16(rq, ok ? toff_q[i] + (uint32_t)(row0 * p.ldq * 2) : kOOB, lds0 + kPrQ + slot);
+      dma16(ro, ok ? toff_o[i] + (uint32_t)(row0 * p.lddo * 2) : kOOB, lds0 + kPrO + slot);
+    }
+    if (wv < 2) {
+      const int t = row0 + 4 * lane;
+      dma16(rv, (lane < 16 && t < T) ? (uint32_t)t * 4u : kOOB, lds0 + kPrV + st * 2048u + (uint32_t)wv * 1024u);
+    }
+  };
+
+  // Per-lane LDS byte offsets (see above): row fragment s of tile row li
+  // (queries 0..31 of a block; +8 KB for 32..63) in this wavefront's row-read
+  // tile (qh for the P wavefront, dO for the dS wavefront), stage of block j;
+  // the two halves of transposed fragment x (reduction rows 0..15; +4 KB per
+  // 16 rows) in its other tile, stage of block j - 1; its exchange slot
+  // (buffer of block j for the P wavefront, of block j - 1 for the dS
+  // wavefront); its vector (lse or D of queries 4 g .., stage of block j).
+  uint32_t roff[KS], toff[HB][2], xoff, voff;
+  {
+    const uint32_t rbase = pwave ? kPrQ : kPrO, tbase = pwave ? kPrO : kPrQ + 2 * kPrTile;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) roff[s] = rbase + (uint32_t)(li * 256 + (((2 * s + g) ^ sw2(li)) << 4));
+    const int gi = lane >> 4, i = lane & 15, r = i >> 2, q = i & 3;
+#pragma unroll
+    for (int x = 0; x < HB; ++x)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int chunk = x * 4 + 2 * (gi & 1) + (q >> 1);
+        const int kr = 4 * (gi >> 1) + r + 8 * hh;
+        toff[x][hh] = tbase + (uint32_t)(kr * 256 + ((chunk ^ sw2(kr)) << 4) + 8 * (q & 1));
+      }
+    xoff = kPrX + (pwave ? 0u : 16384u) + (uint32_t)pr * 4096u + (uint32_t)lane * 16u;
+    voff = kPrV + (pwave ? 0u : 1024u) + 16u * (uint32_t)g;
+  }
+  // move to block j: by one stage (back to the first after the third), and
+  // the other exchange buffer.  The offsets pass through an empty asm, so
+  // the compiler neither re-derives them per read nor keeps base + immediate
+  // sums of its own.
+  auto advance = [&](int j) __attribute__((always_inline)) {
+    const uint32_t dst = (j % 3 == 0) ? (uint32_t)(-2 * (int)kPrTile) : kPrTile;  // row reads: stage of j
+    // transposed reads: stage of block j (P wavefront) or j - 1 (dS wavefront)
+    const uint32_t dtt = ((pwave ? j : j + 2) % 3 == 0) ? (uint32_t)(-2 * (int)kPrTile) : kPrTile;
+    const uint32_t dv = (j % 3 == 0) ? (uint32_t)(-2 * 2048) : 2048u;
+    // exchange buffer: of block j (P wavefront) or of block j - 1 (dS wavefront)
+    const uint32_t dx = ((pwave ? j : j + 1) & 1) ? 16384u : (uint32_t)-16384;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) roff[s] += dst;
+#pragma unroll
+    for (int x = 0; x < HB; ++x) { toff[x][0] += dtt; toff[x][1] += dtt; }
+    voff += dv;
+    xoff += dx;
+    asm volatile("" : "+v"(roff[0]), "+v"(roff[1]), "+v"(roff[2]), "+v"(roff[3]), "+v"(roff[4]), "+v"(roff[5]),
+                 "+v"(roff[6]), "+v"(roff[7]));
+    asm volatile("" : "+v"(toff[0][0]), "+v"(toff[0][1]), "+v"(toff[1][0]), "+v"(toff[1][1]), "+v"(toff[2][0]),
+                 "+v"(toff[2][1]), "+v"(toff[3][0]), "+v"(toff[3][1]), "+v"(xoff), "+v"(voff));
+  };
+  auto rowf = [&](uint32_t imm, int s) { return *reinterpret_cast<const bf16x8*>(smem + imm + roff[s]); };
+  auto trf = [&](uint32_t imm, int x) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(smem + imm + toff[x][0]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(smem + imm + toff[x][1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto vec4 = [&](uint32_t imm) { return *reinterpret_cast<const f32x4*>(smem + imm + voff); };
+
+  load_block(0);
+
+  if (pwave) {
+    // ------------------------------------------------------------ P wavefront
+    const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(kp + (size_t)kj * p.ldk + s * 16 + g * 8) : bf16x8{};
+    // wait for K here: the compiler does not see the waits of the asm below,
+    // and would otherwise wait for all loads (those of the next block too) at
+    // the first use of K inside the loop, every block
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(kf[s]));
+    f32x16 dv[HB];
+#pragma unroll
+    for (int x = 0; x < HB; ++x) dv[x] = f32x16{};
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // X_{-1}: block 0 landed
+    // one block: loads of block j + 1; S of both halves (fragment reads
+    // first, the two accumulation chains interleaved), P = exp2(S c - lse)
+    // written to the exchange buffer, dV += P^T dO
+    auto seg = [&](auto masked, int j) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
+      if (j > 0) advance(j);
+      load_block(j + 1);
+      bf16x8 fq[2][KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        fq[0][s] = rowf(0u, s);
+        fq[1][s] = rowf(8192u, s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 S[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        S[0] = mfma(fq[0][s], kf[s], S[0]);
+        S[1] = mfma(fq[1][s], kf[s], S[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int qbase = (qb0 + j) * 64;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        f32x16 P;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const f32x4 l4 = vec4((uint32_t)(mi * 32 + 8 * rb) * 4u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rb + e;
+            float pv = ex2(fmaf(S[mi][r], c, -l4[e]));
+            if constexpr (MASKED) {
+              const int q = qbase + mi * 32 + 8 * rb + 4 * g + e;
+              pv = (q < kj || q >= T) ? 0.f : pv;
+            }
+            P[r] = pv;
+          }
+        }
+        pf[2 * mi] = pack8(P, 0);
+        pf[2 * mi + 1] = pack8(P, 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<bf16x8*>(smem + (uint32_t)(2 * mi + t) * 1024u + xoff) = pf[2 * mi + t];
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int x = 0; x < HB; ++x)
+            dv[x] = mfma(trf((uint32_t)(mi * 32 + t * 16) * 256u, x), pf[2 * mi + t], dv[x]);
+      // X_j: the P writes are done and this wavefront's loads of block j + 1 landed
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // the first two blocks meet the diagonal, a block j with (qb0 + j + 1) *
+    // 64 > T meets the end: masked ranges are a prefix and a suffix
+    const int j_end = min(nb, max(2, T / 64 - qb0));
+    int j = 0;
+    for (; j < min(2, nb); ++j) seg(std::true_type{}, j);
+    for (; j < j_end; ++j) seg(std::false_type{}, j);
+    for (; j < nb; ++j) seg(std::true_type{}, j);
+    // the dS wavefront's last block (no loads: those of block nb + 1 read 0)
+    load_block(j + 1);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kj >= T) return;
+    bf16* dvq = (bf16*)p.dv + (tok0 + kj) * p.lddv + h * HD;
+#pragma unroll
+    for (int x = 0; x < HB; ++x)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 w;
+        w.x = pack_bf16x2(dv[x][rg * 4 + 0], dv[x][rg * 4 + 1]);
+        w.y = pack_bf16x2(dv[x][rg * 4 + 2], dv[x][rg * 4 + 3]);
+        *reinterpret_cast<u32x2*>(dvq + x * 32 + 8 * rg + 4 * g) = w;
+      }
+  } else {
+    // ----------------------------------------------------------- dS wavefront
+    const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
+    bf16x8 vn[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 v = kj < T ? *reinterpret_cast<const bf16x8*>(vp + (size_t)kj * p.ldv + s * 16 + g * 8) : bf16x8{};
+      vn[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);  // -V
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(vn[s]));  // wait for V here (see the P wavefront)
+    f32x16 dk[HB];
+#pragma unroll
+    for (int x = 0; x < HB; ++x) dk[x] = f32x16{};
+    f32x16 Pd[2];  // D - dP of the previous block, per half
+    const long Tp = p.tpad;
+    const rsrc_t rds = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
+    const uint32_t ds_lane = (uint32_t)lane * 16u;
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // X_{-1}: block 0 landed
+    // -dS = P (D - dP) of block jp from the partner's P, stored, then
+    // dK' += (-dS)^T qh
+    auto dsk = [&](int jp) __attribute__((always_inline)) {
+      const int qbase = (qb0 + jp) * 64;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        bf16x8 sf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(smem + (uint32_t)(2 * mi + t) * 1024u + xoff);
+          // fragment t holds accumulator registers 8 t .. 8 t + 7, two per dword
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = pack_bf16x2(bf16lo_to_f32(w[q]) * Pd[mi][8 * t + 2 * q],
+                               bf16hi_to_f32(w[q]) * Pd[mi][8 * t + 2 * q + 1]);
+          sf[t] = __builtin_bit_cast(bf16x8, o);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sf[t]), rds, ds_lane,
+                                                 (int)ds_chunk(Tp, wk >> 5, (qbase + 32 * mi) >> 5, t), 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int x = 0; x < HB; ++x) dk[x] = mfma(trf((uint32_t)(mi * 32 + t * 16) * 256u, x), sf[t], dk[x]);
+      }
+    };
+    int j = 0;
+    for (; j < nb; ++j) {
+      // one block: loads of block j + 1, dS and dK of block j - 1, D - dP of block j
+      if (j > 0) advance(j);
+      load_block(j + 1);
+      if (j > 0) dsk(j - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // D - dP of both halves: fragment and D reads first, then the two
+      // accumulation chains interleaved
+      bf16x8 fo[2][KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        fo[0][s] = rowf(0u, s);
+        fo[1][s] = rowf(8192u, s);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const f32x4 d4 = vec4((uint32_t)(mi * 32 + 8 * rb) * 4u);
+          Pd[mi][4 * rb + 0] = d4.x;
+          Pd[mi][4 * rb + 1] = d4.y;
+          Pd[mi][4 * rb + 2] = d4.z;
+          Pd[mi][4 * rb + 3] = d4.w;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        Pd[0] = mfma(fo[0][s], vn[s], Pd[0]);
+        Pd[1] = mfma(fo[1][s], vn[s], Pd[1]);
+      }
+      // X_j: this wavefront's loads of block j + 1 landed; the only vector
+      // memory operations issued after them are the 4 dS stores of block j - 1
+      if (j > 0) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    advance(j);
+    load_block(j + 1);
+    dsk(j - 1);
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    wait_vmem();
+    if (kj >= T) return;
+    const float sc = -p.scale;  // dK' = -dK
+    float* dkp = p.dk32 + (tok0 + kj) * p.lddk + h * HD;
+#pragma unroll
+    for (int x = 0; x < HB; ++x)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 w{dk[x][rg * 4 + 0] * sc, dk[x][rg * 4 + 1] * sc, dk[x][rg * 4 + 2] * sc, dk[x][rg * 4 + 3] * sc};
+        *reinterpret_cast<f32x4*>(dkp + x * 32 + 8 * rg + 4 * g) = w;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ backward: D
 template <class T>
 __global__ void __launch_bounds__(256) attn_bwd_pre(AttnArgs p, int hd) {
@@ -1350,7 +1692,11 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
       if (!p.dq_pre || !p.rq || !p.cs) return NC_ERR_NULL;
       if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
       attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
+#ifdef NC_DKDV_SINGLE
       attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
+#else
+      attn_bwd_dkdv_pair128<<<gk, 512, 0, s>>>(p);
+#endif
       attn_bwd_dq_ds128<<<dim3((p.T + kDqQueries - 1) / kDqQueries, p.B * p.H), 512, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
