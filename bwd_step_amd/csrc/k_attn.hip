@@ -1250,7 +1250,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sf[t]), rds, ds_lane,
-                                                 (int)ds_chunk(Tp, wk >> 5, (qbase + 32 * mi) >> 5, t), 0);
+                                                 (int)ds_chunk(Tp, wk >> 5, (qbase + 32 * mi) >> 5, t), 2);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
