@@ -236,201 +236,20 @@ __global__ void __launch_bounds__(256) attn_fwd_mfma(AttnArgs p) {
   if (g == 0) p.lse[(size_t)bh * T + qi] = mx + log2f(ltot);  // base 2
 }
 
-// ------------------------------------------------------------------ forward, head_dim 128
-// K and V tiles ([64 keys][128], 16 KB each) are staged with LDS-direct buffer
-// loads into two stages (separate LDS objects, so the compiler does not wait
-// on the in-flight stage).  K fragments for S^T = K Q^T are 16-byte reads of
-// an XOR-swizzled tile (chunk ^= key & 15).  V^T fragments for O^T = V^T P^T
-// come straight from the row-major V tile through ds_read_b64_tr_b16, whose
-// per-16-lane-group key offset is chosen to follow the key order that the
-// score accumulator already has; the V chunks are swizzled by sw_v(key & 3)
-// so that these reads are conflict free.  The kernel stays under 256
-// registers per lane so that two workgroups (eight wavefronts) share a
-// compute unit and one's softmax overlaps the other's MFMAs.
+// ------------------------------------------------------------------ head_dim 128 helpers
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// chunk swizzle of the forward's V tile: key & 3 -> XOR of the 16-byte chunk
+// index, so that the transposed reads of four consecutive keys are conflict free
 __device__ __forceinline__ int sw_v(int r) { return 4 * r + 2 * ((r >> 1) & 1); }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// One 1 KB block (4 key rows of 128) of a [64][128] tile; V tiles use the
-// transposed-read swizzle, K tiles the row swizzle.
-template <bool VTILE>
-__device__ __forceinline__ void kv_dma(rsrc_t rs, long ld, long col0, int key0, int T, bf16* lds, int blk,
-                                       int lane) {
-  const int row = blk * 4 + (lane >> 4);
-  const int pc = lane & 15;
-  const int c = VTILE ? (pc ^ sw_v(row & 3)) : (pc ^ (row & 15));
-  const int key = key0 + row;
-  const uint32_t off = key < T ? (uint32_t)(((long)key * ld + col0 + c * 8) * 2) : kOOB;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + blk * 512), 16, off, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 k_frag(const bf16* Ks, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(Ks + row * 128 + ((chunk ^ (row & 15)) << 3));
-}
-
-// V^T fragment: hd rows x*32 + (lane & 31), keys kb + {4g .. 4g+3, 8+4g .. 8+4g+3}, g = lane / 32.
-__device__ __forceinline__ bf16x8 vt_frag(const bf16* Vs, int x, int kb, int lane) {
-  const int gi = lane >> 4, i = lane & 15;
-  const int r = i >> 2, q = i & 3;
-  const int chunk = (x * 4 + 2 * (gi & 1) + (q >> 1)) ^ sw_v(r);
-  const int col = (chunk << 3) + 4 * (q & 1);
-  const int k0 = kb + 4 * (gi >> 1) + r;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(Vs + k0 * 128 + col));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(Vs + (k0 + 8) * 128 + col));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-
-__global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
-  constexpr int HD = 128, KS = 8, HB = 4;
-  __shared__ __attribute__((aligned(1024))) bf16 K0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 K1[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 V0[64 * HD];
-  __shared__ __attribute__((aligned(1024))) bf16 V1[64 * HD];
-
-  const int T = p.T;
-  const int nqb = gridDim.x;  // (T + 127) / 128
-  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
-  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn on one XCD, the longest first
-  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, li = lane & 31;
-  const int q0 = qb * 128;
-  const int qi = q0 + wv * 32 + li;
-  const size_t tok0 = (size_t)b * T;
-  const uint32_t kbytes = (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2);
-  const uint32_t vbytes = (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)(p.H / p.G) * HD) * 2);
-  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk, kbytes);
-  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv, vbytes);
-  const long colk = (long)(h / p.G) * HD;  // this query head's key/value head
-
-  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
-
-  f32x16 oacc[HB];
-#pragma unroll
-  for (int x = 0; x < HB; ++x) oacc[x] = f32x16{};
-  float mx = -INFINITY, lsum = 0.f;
-  const float c = p.scale_log2;
-
-  const int q_last = min(T - 1, q0 + 127);
-  const int nkv = q_last / 64 + 1;
-  const int wq_min = q0 + wv * 32, wq_max = wq_min + 31;
-
-  // stage block 0
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kv_dma<false>(rk, p.ldk, colk, 0, T, K0, wv * 4 + i, lane);
-    kv_dma<true>(rv, p.ldv, colk, 0, T, V0, wv * 4 + i, lane);
-  }
-  wait_vmem();
-  __syncthreads();
-
-  auto block = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn, int kb) {
-    const bool live = kb + 1 < nkv;
-    const int knext = (kb + 1) * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kv_dma<false>(rk, p.ldk, colk, live ? knext : T, T, Kn, wv * 4 + i, lane);
-      kv_dma<true>(rv, p.ldv, colk, live ? knext : T, T, Vn, wv * 4 + i, lane);
-    }
-    const int kbase = kb * 64;
-    if (kbase <= wq_max) {
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        sacc[kk] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sacc[kk] = mfma(k_frag(Ks, kk * 32 + li, 2 * s + g), qf[s], sacc[kk]);
-      }
-      const bool need_mask = (kbase + 63 > wq_min) || (kbase + 64 > T);
-      float lmax = -INFINITY;
-      if (need_mask) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + kk * 32 + acc_row(r, g);
-            if (key > qi || key >= T) sacc[kk][r] = -INFINITY;
-          }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, sacc[kk][r]);
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-      // Running max in the scaled log2 domain.  It is raised (and O and the
-      // sum rescaled) only when a score exceeds it by more than 8, so the
-      // weights below stay <= 2^8 and the costly rescale is rare; the final
-      // normalisation by the sum makes the result independent of the choice.
-      const float mcand = fmaxf(mx, lmax * c);
-      if (mcand > mx + 8.f) {
-        const float alpha = ex2(mx - mcand);
-        lsum *= alpha;
-#pragma unroll
-        for (int x = 0; x < HB; ++x) oacc[x] *= alpha;
-        mx = mcand;
-      }
-      const float moff = mx == -INFINITY ? 0.f : -mx;
-      float ps = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = ex2(fmaf(sacc[kk][r], c, moff));
-          sacc[kk][r] = e;
-          ps += e;
-        }
-      lsum += ps;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pf = pack8(sacc[kk], t);
-#pragma unroll
-          for (int x = 0; x < HB; ++x) oacc[x] = mfma(vt_frag(Vs, x, kk * 32 + t * 16, lane), pf, oacc[x]);
-        }
-    }
-  };
-
-  int kb = 0;
-  for (; kb + 1 < nkv; kb += 2) {
-    block(K0, V0, K1, V1, kb);
-    wait_vmem();
-    __syncthreads();
-    block(K1, V1, K0, V0, kb + 1);
-    wait_vmem();
-    __syncthreads();
-  }
-  if (kb < nkv) block(K0, V0, K1, V1, kb);
-  wait_vmem();  // the tail's no-op loads still target LDS
-
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  if (qi >= T) return;
-  const float inv = 1.0f / ltot;
-  bf16* op = (bf16*)p.o + (tok0 + qi) * p.ldo + h * HD;
-#pragma unroll
-  for (int x = 0; x < HB; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      u32x2 w;
-      w.x = pack_bf16x2(oacc[x][rg * 4 + 0] * inv, oacc[x][rg * 4 + 1] * inv);
-      w.y = pack_bf16x2(oacc[x][rg * 4 + 2] * inv, oacc[x][rg * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
-    }
-  if (g == 0) p.lse[(size_t)bh * T + qi] = mx + log2f(ltot);  // base 2
-}
 
 // ------------------------------------------------------------------ backward, head_dim 128
 // Tiles of 64 rows x 128 that are read both ways -- 16-byte row fragments
@@ -499,6 +318,213 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
 // (b, h) takes (Tp / 32)^2 * 2 KB = Tp^2 * 2 bytes.
 __device__ __forceinline__ uint32_t ds_chunk(long Tp, int kw, int qw, int t) {
   return (uint32_t)((((long)kw * (Tp >> 5) + qw) * 2 + t) * 1024);
+}
+
+// ------------------------------------------------------------------ forward, head_dim 128
+// Forward, head_dim 128: 128 queries per workgroup (4 wavefronts x 32, Q
+// fragments in registers), 64-key blocks of K and V through two LDS stages
+// (one array: K of stage 0 and 1, then V of stage 0 and 1, 16 KB each)
+// loaded one block ahead by inline-asm LDS-direct loads (a key past T reads
+// 0 through the buffer range check).  S^T = K Q^T with K fragments as 16-byte
+// reads of the row tile (chunk ^= key & 15); O^T = V^T P^T with V^T
+// fragments through ds_read_b64_tr_b16 from the row tile (chunks swizzled by
+// sw_v(key & 3)); both read without bank conflicts.  Every fragment address
+// is a per-lane register (moved to the block's stage once per block) plus an
+// immediate.  The row sum
+// of P is taken from the bf16 values that enter the product (v_dot2 with
+// ones), so the normalisation matches the numerator.  The kernel stays under
+// 256 registers per lane so that two workgroups (eight wavefronts) share a
+// compute unit and one's softmax overlaps the other's MFMAs.
+__global__ void __launch_bounds__(256, 2) attn_fwd128(AttnArgs p) {
+  constexpr int HD = 128, KS = 8, HB = 4;
+  constexpr uint32_t kTile = 64 * HD * 2, kVs = 2 * kTile;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTile];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+  const int T = p.T;
+  const int nqb = gridDim.x;  // (T + 127) / 128
+  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
+  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn on one XCD, the longest first
+  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, li = lane & 31;
+  const int q0 = qb * 128;
+  const int qi = q0 + wv * 32 + li;
+  const size_t tok0 = (size_t)b * T;
+  const uint32_t kbytes = (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2);
+  const uint32_t vbytes = (uint32_t)(((size_t)(T - 1) * p.ldv + (size_t)(p.H / p.G) * HD) * 2);
+  const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk, kbytes);
+  const rsrc_t rv = make_rsrc((const bf16*)p.v + tok0 * p.ldv, vbytes);
+  const long colk = (long)(h / p.G) * HD;  // this query head's key/value head
+
+  const bf16* qp = (const bf16*)p.q + tok0 * p.ldq + h * HD;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = qi < T ? *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * p.ldq + s * 16 + g * 8) : bf16x8{};
+  // wait for Q here: the compiler does not see the asm loads' waits and
+  // would otherwise wait for every load at the first use of Q in the loop
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qf[s]));
+
+  // this wavefront's loads of a block: 1-KB slots wv * 4 + i (key rows
+  // 4 slot .. + 3) of the K and V tiles; per-lane byte offsets relative to
+  // the block's first key.  A row at or past T lies past the buffer's range
+  // (the last row ends at the last head's column), so it reads 0.
+  uint32_t ko[4], vo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wv * 4 + i) * 4 + (lane >> 4);
+    const int pc = lane & 15;
+    ko[i] = (uint32_t)(((long)row * p.ldk + colk + ((pc ^ (row & 15)) << 3)) * 2);
+    vo[i] = (uint32_t)(((long)row * p.ldv + colk + ((pc ^ sw_v(row & 3)) << 3)) * 2);
+  }
+  auto load_kv = [&](uint32_t st, int key0) __attribute__((always_inline)) {
+    const uint32_t rk0 = (uint32_t)key0 * (uint32_t)p.ldk * 2u, rv0 = (uint32_t)key0 * (uint32_t)p.ldv * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t slot = st * kTile + (uint32_t)(wv * 4 + i) * 1024u;
+      dma16(rk, ko[i] + rk0, lds0 + slot);
+      dma16(rv, vo[i] + rv0, lds0 + kVs + slot);
+    }
+  };
+
+  // Per-lane LDS byte offsets of the fragment reads, formed once (opaque to
+  // the compiler so that it neither re-derives them nor hoists sums with the
+  // immediates): K fragment s of key row li (+8 KB for keys 32..63 of the
+  // block), V^T fragment x (keys 4 (gi >> 1) + r; +2 KB for the other eight
+  // of the 16-key step, +4 KB per step).
+  uint32_t kfo[KS], vfo[HB];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kfo[s] = (uint32_t)(li * 256 + (((2 * s + g) ^ (li & 15)) << 4));
+    asm volatile("" : "+v"(kfo[s]));
+  }
+  {
+    const int gi = lane >> 4, i = lane & 15, r = i >> 2, q = i & 3;
+#pragma unroll
+    for (int x = 0; x < HB; ++x) {
+      const int chunk = (x * 4 + 2 * (gi & 1) + (q >> 1)) ^ sw_v(r);
+      vfo[x] = kVs + (uint32_t)((4 * (gi >> 1) + r) * 256 + chunk * 16 + 8 * (q & 1));
+      asm volatile("" : "+v"(vfo[x]));
+    }
+  }
+  auto kfrag = [&](uint32_t imm, int s) { return *reinterpret_cast<const bf16x8*>(smem + imm + kfo[s]); };
+  auto vtfrag = [&](uint32_t imm, int x) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(smem + imm + vfo[x]));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(smem + imm + 2048u + vfo[x]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 oacc[HB];
+#pragma unroll
+  for (int x = 0; x < HB; ++x) oacc[x] = f32x16{};
+  float mx = -INFINITY, lsum = 0.f;
+  const float c = p.scale_log2;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+
+  const int q_last = min(T - 1, q0 + 127);
+  const int nkv = q_last / 64 + 1;
+  const int wq_min = q0 + wv * 32, wq_max = wq_min + 31;
+
+  load_kv(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // key block kb in stage kb & 1; the loads of block kb + 1 (or, past the
+  // last, of rows past T) go to the other stage.  The fragment offsets move
+  // to the block's stage by a uniform delta.
+  auto block = [&](int kb) __attribute__((always_inline)) {
+    const uint32_t st = (uint32_t)kb & 1u;
+    if (kb > 0) {
+      const uint32_t d = st ? kTile : (uint32_t)-(int)kTile;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kfo[s] += d;
+#pragma unroll
+      for (int x = 0; x < HB; ++x) vfo[x] += d;
+      asm volatile("" : "+v"(kfo[0]), "+v"(kfo[1]), "+v"(kfo[2]), "+v"(kfo[3]), "+v"(kfo[4]), "+v"(kfo[5]),
+                   "+v"(kfo[6]), "+v"(kfo[7]), "+v"(vfo[0]), "+v"(vfo[1]), "+v"(vfo[2]), "+v"(vfo[3]));
+    }
+    load_kv(st ^ 1u, kb + 1 < nkv ? (kb + 1) * 64 : T);
+    const int kbase = kb * 64;
+    if (kbase <= wq_max) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        sacc[kk] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc[kk] = mfma(kfrag(kk * 8192u, s), qf[s], sacc[kk]);
+      }
+      const bool need_mask = (kbase + 63 > wq_min) || (kbase + 64 > T);
+      float lmax = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + kk * 32 + acc_row(r, g);
+            if (key > qi || key >= T) sacc[kk][r] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, sacc[kk][r]);
+      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+      // Running max in the scaled log2 domain.  It is raised (and O and the
+      // sum rescaled) only when a score exceeds it by more than 8, so the
+      // weights below stay <= 2^8 and the costly rescale is rare; the final
+      // normalisation by the sum makes the result independent of the choice.
+      const float mcand = fmaxf(mx, lmax * c);
+      if (mcand > mx + 8.f) {
+        const float alpha = ex2(mx - mcand);
+        lsum *= alpha;
+#pragma unroll
+        for (int x = 0; x < HB; ++x) oacc[x] *= alpha;
+        mx = mcand;
+      }
+      const float moff = mx == -INFINITY ? 0.f : -mx;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kk][r] = ex2(fmaf(sacc[kk][r], c, moff));
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 pf = pack8(sacc[kk], t);
+          // (the pairs are taken with shufflevector: a bit_cast of a 32-bit
+          // lane to bf16x2 here selects the wrong register on this compiler)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), ones, lsum, false);
+#pragma unroll
+          for (int x = 0; x < HB; ++x)
+            oacc[x] = mfma(vtfrag((uint32_t)(kk * 32 + t * 16) * 256u, x), pf, oacc[x]);
+        }
+    }
+    // this wavefront's loads of block kb + 1 landed and every wavefront is
+    // done reading this block's stage
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  for (int kb = 0; kb < nkv; ++kb) block(kb);
+
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  if (qi >= T) return;
+  const float inv = 1.0f / ltot;
+  bf16* op = (bf16*)p.o + (tok0 + qi) * p.ldo + h * HD;
+#pragma unroll
+  for (int x = 0; x < HB; ++x)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 w;
+      w.x = pack_bf16x2(oacc[x][rg * 4 + 0] * inv, oacc[x][rg * 4 + 1] * inv);
+      w.y = pack_bf16x2(oacc[x][rg * 4 + 2] * inv, oacc[x][rg * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + x * 32 + 8 * rg + 4 * g) = w;
+    }
+  if (g == 0) p.lse[(size_t)bh * T + qi] = mx + log2f(ltot);  // base 2
 }
 
 // D = rowsum(dO * O) of every (token, head), head_dim 128: 16 lanes per row
