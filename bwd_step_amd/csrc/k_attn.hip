@@ -261,19 +261,6 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // aligned group of 4 rows bits 2-3 differ and bits 1-2 differ).
 __device__ __forceinline__ int sw2(int row) { return 4 * (row & 3) + (((row >> 2) & 3) ^ (2 * ((row >> 1) & 1))); }
 
-__device__ __forceinline__ void tile_dma(rsrc_t rs, long ld, long col0, int row0, int T, bf16* lds, int blk,
-                                         int lane) {
-  const int row = blk * 4 + (lane >> 4);
-  const int c = (lane & 15) ^ sw2(row);
-  const int t = row0 + row;
-  const uint32_t off = t < T ? (uint32_t)(((long)t * ld + col0 + c * 8) * 2) : kOOB;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + blk * 512), 16, off, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 row_frag(const bf16* S, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(S + row * 128 + ((chunk ^ sw2(row)) << 3));
-}
-
 // Transposed fragment: A-operand rows = columns x*32 + (lane & 31) of the
 // tile, reduction index = tile rows kb + {4g .. 4g+3, 8+4g .. 8+4g+3}.
 __device__ __forceinline__ bf16x8 tr_frag(const bf16* S, int x, int kb, int lane) {
@@ -737,261 +724,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
       }
       *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w)};
       *reinterpret_cast<u32x2*>(out + i + 64) = u32x2{pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
-    }
-}
-
-// dK, dV: 128 keys per workgroup, 32 per wavefront (its K and -V fragments in
-// registers).  Blocks of 64 queries (qh, dO and their lse and D) stream
-// through four LDS stages, loaded two blocks ahead.  A block is processed as
-// two halves of 32 queries, software-pipelined: the P / dS arithmetic of one
-// half is issued together with the S / dP products of the next half, then
-// the dV / dK products of the half follow.  With -V in place of V the dP
-// accumulator starts at D and ends at D - dP, so P (D - dP) = -dS comes out
-// of one multiply; the sign is restored when dK is written.  The bf16 -dS
-// (the B operand of the dK products) is also stored, transposed ([key]
-// [query]), for the dQ kernel, so S and dP are computed once per pair.
-//
-// LDS: one array of four 36-KB stages (qh tile, dO tile: 64 rows x 256 bytes
-// with the sw2 chunk swizzle; then four 1-KB vector slots: lse (base 2), D,
-// and copies of both, one slot loaded by each wavefront).
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv128(AttnArgs p) {
-  constexpr int HD = 128, KS = 8, HB = 4;
-  constexpr uint32_t kTile = 64 * HD * 2, kStage = 2 * kTile + 4096;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kStage];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-
-  const int T = p.T;
-  const int nkb = gridDim.x;
-  const int lin = xcd_block(blockIdx.x + nkb * blockIdx.y, nkb * gridDim.y);
-  const int kbk = lin % nkb;  // key blocks of one (b, h) in turn, the longest first
-  const int bh = lin / nkb, b = bh / p.H, h = bh % p.H;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5, li = lane & 31;
-  const int k0 = kbk * 128;
-  const int wk = k0 + wv * 32;  // the wavefront's first key
-  const int kj = wk + li;       // this lane's key
-  const size_t tok0 = (size_t)b * T;
-  const rsrc_t rq = make_rsrc((const bf16*)p.q + tok0 * p.ldq,
-                              (uint32_t)(((size_t)(T - 1) * p.ldq + (size_t)p.H * HD) * 2));
-  const rsrc_t ro = make_rsrc((const bf16*)p.dout + tok0 * p.lddo,
-                              (uint32_t)(((size_t)(T - 1) * p.lddo + (size_t)p.H * HD) * 2));
-  // wavefronts 0 and 2 load lse (base 2), 1 and 3 load D
-  const rsrc_t rv = make_rsrc((wv & 1) ? (const void*)(p.Dbuf + (size_t)bh * T) : (const void*)(p.lse + (size_t)bh * T),
-                              (uint32_t)T * 4u);
-  const long col = (long)h * HD;
-  const int qb0 = k0 / 64;
-  const int nb = (T + 63) / 64 - qb0;  // query blocks at or after the diagonal
-
-  // Per-lane byte offsets of this wavefront's tile loads (4 slots of 4 rows
-  // for each tile) relative to the block's first row, and of its vector load.
-  uint32_t toff_q[4], toff_o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wv * 4 + i) * 4 + (lane >> 4);
-    const int cc = (lane & 15) ^ sw2(row);
-    toff_q[i] = (uint32_t)(((long)row * p.ldq + col + cc * 8) * 2);
-    toff_o[i] = (uint32_t)(((long)row * p.lddo + col + cc * 8) * 2);
-  }
-  // loads of query block j into stage st (9 per wavefront); rows past T and
-  // blocks past the last read 0
-  auto load_block = [&](int st, int j) {
-    const int row0 = j < nb ? (qb0 + j) * 64 : T;
-    const uint32_t sb = lds0 + (uint32_t)st * kStage;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + (wv * 4 + i) * 4 + (lane >> 4);
-      const bool ok = row < T;
-      dma16(rq, ok ? toff_q[i] + (uint32_t)(row0 * p.ldq * 2) : kOOB, sb + (uint32_t)(wv * 4 + i) * 1024u);
-      dma16(ro, ok ? toff_o[i] + (uint32_t)(row0 * p.lddo * 2) : kOOB, sb + kTile + (uint32_t)(wv * 4 + i) * 1024u);
-    }
-    const int t = row0 + 4 * lane;
-    dma16(rv, (lane < 16 && t < T) ? (uint32_t)t * 4u : kOOB, sb + 2 * kTile + (uint32_t)wv * 1024u);
-  };
-  // Vector memory operations retire in issue order.  At this wait the ones
-  // younger than the previous block's 9 loads are the 2 + 2 dS stores of the
-  // previous pass, the 9 loads of the newest block and the 2 dS stores of
-  // this pass's first half: with at most 15 in flight the previous block has
-  // landed.  The barrier publishes it and orders every wavefront's reads of
-  // older stages before the next loads.
-  auto wait_block_and_sync = [&]() { asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory"); };
-  // -dS^T of one half (32 queries from q, a multiple of 32): each lane's two
-  // fragments go out whole, one 1-KB chunk per fragment (ds_chunk)
-  const long Tp = p.tpad;
-  const rsrc_t rds = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
-  const uint32_t ds_lane = (uint32_t)lane * 16u;
-  auto store_ds = [&](const bf16x8* sf, int q) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sf[t]), rds, ds_lane,
-                                             (int)ds_chunk(Tp, wk >> 5, q >> 5, t), 0);
-  };
-
-  load_block(0, 0);
-  load_block(1, 1);
-  const bf16* kp = (const bf16*)p.k + tok0 * p.ldk + (h / p.G) * HD;
-  const bf16* vp = (const bf16*)p.v + tok0 * p.ldv + (h / p.G) * HD;
-  bf16x8 kf[KS], vn[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kf[s] = kj < T ? *reinterpret_cast<const bf16x8*>(kp + (size_t)kj * p.ldk + s * 16 + g * 8) : bf16x8{};
-    const bf16x8 v = kj < T ? *reinterpret_cast<const bf16x8*>(vp + (size_t)kj * p.ldv + s * 16 + g * 8) : bf16x8{};
-    vn[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) ^ 0x80008000u);  // -V
-  }
-  f32x16 dk[HB], dv[HB];
-#pragma unroll
-  for (int x = 0; x < HB; ++x) { dk[x] = f32x16{}; dv[x] = f32x16{}; }
-  const float c = p.scale_log2;
-
-  // S and D - dP of one half (mi) of the block in stage st.  The fragment and
-  // D reads are issued in a scheduling region of their own, ahead of the
-  // MFMAs, so that no MFMA waits out the LDS latency of its own operand.
-  auto phase_a = [&](uint32_t st, int mi, f32x16& S, f32x16& Pd) {
-    const char* sb = smem + st * kStage;
-    const bf16* Qs = (const bf16*)sb;
-    const bf16* Os = (const bf16*)(sb + kTile);
-    const float* Ds = (const float*)(sb + 2 * kTile) + 256;
-    bf16x8 fq[KS], fo[KS];
-    f32x4 d4[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) d4[rb] = *reinterpret_cast<const f32x4*>(Ds + mi * 32 + 8 * rb + 4 * g);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      fq[s] = row_frag(Qs, mi * 32 + li, 2 * s + g);
-      fo[s] = row_frag(Os, mi * 32 + li, 2 * s + g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      // accumulator registers 4 rb .. 4 rb + 3 hold four consecutive queries
-      Pd[4 * rb + 0] = d4[rb].x;
-      Pd[4 * rb + 1] = d4[rb].y;
-      Pd[4 * rb + 2] = d4[rb].z;
-      Pd[4 * rb + 3] = d4[rb].w;
-    }
-    S = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      S = mfma(fq[s], kf[s], S);
-      Pd = mfma(fo[s], vn[s], Pd);
-    }
-  };
-  // P = exp2(S c - lse) and -dS = P (D - dP) of one half, as bf16 B operands;
-  // MASKED: apply the causal / length mask (passes that meet the diagonal or T)
-  auto phase_b = [&](auto masked, const f32x16& S, const f32x16& Pd, uint32_t st, int mi, int qh, bf16x8* pf,
-                     bf16x8* sf) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const float* Ls = (const float*)(smem + st * kStage + 2 * kTile);
-    f32x16 P, dS;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + mi * 32 + 8 * rb + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rb + e;
-        float pr = ex2(fmaf(S[r], c, -l4[e]));
-        if constexpr (MASKED) {
-          const int q = qh + 8 * rb + 4 * g + e;
-          pr = (q < kj || q >= T) ? 0.f : pr;
-        }
-        P[r] = pr;
-        dS[r] = pr * Pd[r];
-      }
-    }
-    pf[0] = pack8(P, 0);
-    pf[1] = pack8(P, 1);
-    sf[0] = pack8(dS, 0);
-    sf[1] = pack8(dS, 1);
-  };
-  // dV += P^T dO and dK' += (-dS)^T qh for one half of the block in stage st
-  auto phase_c = [&](uint32_t st, int mi, const bf16x8* pf, const bf16x8* sf) {
-    const char* sb = smem + st * kStage;
-    const bf16* Qs = (const bf16*)sb;
-    const bf16* Os = (const bf16*)(sb + kTile);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int x = 0; x < HB; ++x) {
-        dv[x] = mfma(tr_frag(Os, x, mi * 32 + t * 16, lane), pf[t], dv[x]);
-        dk[x] = mfma(tr_frag(Qs, x, mi * 32 + t * 16, lane), sf[t], dk[x]);
-      }
-  };
-  // Instruction interleave of one pipelined section of 16 MFMAs: LEAD LDS
-  // reads first, then per MFMA NDS LDS reads (for later MFMAs) and NVALU
-  // vector instructions, so that the reads run ahead of their MFMAs.
-  auto interleave = [&](auto lead, auto nds, auto nvalu) {
-    if constexpr (decltype(lead)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(lead)::value, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (decltype(nds)::value > 0) __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);
-      if constexpr (decltype(nvalu)::value > 0) __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I2 = std::integral_constant<int, 2>;
-  using I4 = std::integral_constant<int, 4>;
-  using I6 = std::integral_constant<int, 6>;
-  using I8 = std::integral_constant<int, 8>;
-
-  // One pass over block j (in stage j mod 4): its second half, then the first
-  // half of block j + 1, whose loads are waited for in the middle.
-  f32x16 Sa, Pa;  // the pending half: S and D - dP, products done, arithmetic not yet
-  auto pass = [&](auto masked, int j) {
-    const uint32_t cur = (uint32_t)j & 3u, nxt = (uint32_t)(j + 1) & 3u;
-    load_block((j + 2) & 3, j + 2);
-    const int qbase = (qb0 + j) * 64;
-    bf16x8 pf[2], sf[2];
-    f32x16 Sb, Pb;
-    __builtin_amdgcn_sched_barrier(0);
-    phase_a(cur, 1, Sb, Pb);
-    phase_b(masked, Sa, Pa, cur, 0, qbase, pf, sf);
-    interleave(I4{}, I0{}, I6{});
-    phase_c(cur, 0, pf, sf);
-    interleave(I8{}, I2{}, I0{});
-    store_ds(sf, qbase);
-    wait_block_and_sync();  // block j + 1
-    phase_a(nxt, 0, Sa, Pa);
-    phase_b(masked, Sb, Pb, cur, 1, qbase + 32, pf, sf);
-    interleave(I4{}, I0{}, I6{});
-    phase_c(cur, 1, pf, sf);
-    interleave(I8{}, I2{}, I0{});
-    store_ds(sf, qbase + 32);
-  };
-
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1, K and V
-  phase_a(0, 0, Sa, Pa);
-  // The first two blocks meet the diagonal and a block j with
-  // (qb0 + j + 1) * 64 > T (j >= T / 64 - qb0) meets the end: masked passes
-  // are a prefix and a suffix, each range run by a loop of its own so that
-  // the accumulators stay in one register file.
-  const int j_end = min(nb, max(2, T / 64 - qb0));
-  int j = 0;
-  for (; j < min(2, nb); ++j) pass(std::true_type{}, j);
-  for (; j < j_end; ++j) pass(std::false_type{}, j);
-  for (; j < nb; ++j) pass(std::true_type{}, j);
-  wait_vmem();  // the loads of the two blocks past the end still target LDS
-
-  if (kj >= T) return;
-  const float sc = -p.scale;  // dK' = -dK
-  float* dkp = p.dk32 + (tok0 + kj) * p.lddk + h * HD;
-#pragma unroll
-  for (int x = 0; x < HB; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      f32x4 w{dk[x][rg * 4 + 0] * sc, dk[x][rg * 4 + 1] * sc, dk[x][rg * 4 + 2] * sc, dk[x][rg * 4 + 3] * sc};
-      *reinterpret_cast<f32x4*>(dkp + x * 32 + 8 * rg + 4 * g) = w;
-    }
-  bf16* dvp = (bf16*)p.dv + (tok0 + kj) * p.lddv + h * HD;
-#pragma unroll
-  for (int x = 0; x < HB; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      u32x2 w;
-      w.x = pack_bf16x2(dv[x][rg * 4 + 0], dv[x][rg * 4 + 1]);
-      w.y = pack_bf16x2(dv[x][rg * 4 + 2], dv[x][rg * 4 + 3]);
-      *reinterpret_cast<u32x2*>(dvp + x * 32 + 8 * rg + 4 * g) = w;
     }
 }
 
@@ -1718,11 +1450,7 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
       if (!p.dq_pre || !p.rq || !p.cs) return NC_ERR_NULL;
       if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
       attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
-#ifdef NC_DKDV_SINGLE
-      attn_bwd_dkdv128<<<gk, 256, 0, s>>>(p);
-#else
       attn_bwd_dkdv_pair128<<<gk, 512, 0, s>>>(p);
-#endif
       attn_bwd_dq_ds128<<<dim3((p.T + kDqQueries - 1) / kDqQueries, p.B * p.H), 512, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
