@@ -118,6 +118,17 @@ struct nc_ctx {
   Prof prof;
   bool poison = false;  // nc_debug_poison_workspace
   bool resid_fp32 = false;  // nc_set_residual_fp32
+  // Backward: the weight-gradient products run on a second stream (created
+  // on first use, default priority), ordered against the main stream by
+  // events, so that they fill the compute units the input-gradient chain
+  // leaves idle.  Serial while the per-launch profiler is on.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_main = nullptr, ev_b2 = nullptr, ev_b4 = nullptr, ev_b6 = nullptr, ev_b8 = nullptr, ev_all = nullptr;
+  ~nc_ctx() {
+    for (hipEvent_t e : {ev_main, ev_b2, ev_b4, ev_b6, ev_b8, ev_all})
+      if (e) (void)hipEventDestroy(e);
+    if (side) (void)hipStreamDestroy(side);
+  }
 };
 
 namespace {
@@ -252,6 +263,36 @@ int maybe_poison(nc_ctx* ctx, const Plan& P) {
 int clear_status(void* ws, hipStream_t s) {
   clear_status_kernel<<<1, 1, 0, s>>>((int*)ws);
   return hipGetLastError() == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+
+// The second stream of the backward and its events (see nc_ctx).
+int ensure_side(nc_ctx* x) {
+  if (x->side) return NC_OK;
+  hipStream_t st = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return NC_ERR_HIP;
+  for (hipEvent_t* e : {&x->ev_main, &x->ev_b2, &x->ev_b4, &x->ev_b6, &x->ev_b8, &x->ev_all})
+    if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(st);
+      return NC_ERR_HIP;
+    }
+  x->side = st;
+  return NC_OK;
+}
+// Work enqueued on `to` after this call starts only once the work enqueued
+// on `from` so far has finished (nothing when both are one stream).
+int order_after(hipEvent_t e, hipStream_t from, hipStream_t to) {
+  if (from == to) return NC_OK;
+  if (hipEventRecord(e, from) != hipSuccess) return NC_ERR_HIP;
+  return hipStreamWaitEvent(to, e, 0) == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+// Record e on `from` now; a later wait_for(e, to) orders `to` after it.
+int mark(hipEvent_t e, hipStream_t from, hipStream_t to) {
+  if (from == to) return NC_OK;
+  return hipEventRecord(e, from) == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+int wait_for(hipEvent_t e, hipStream_t from, hipStream_t to) {
+  if (from == to) return NC_OK;
+  return hipStreamWaitEvent(to, e, 0) == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
 int read_status(void* ws, hipStream_t s) {
@@ -485,7 +526,21 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     }
     return NC_OK;
   };
+  // Weight gradients (dW = dy^T x: W_2, W_1, W_o, W_qkv) go to the second
+  // stream s2.  Each reads a saved activation and a gradient buffer that the
+  // main stream rewrites later: dx_lp (read by dW_2, then dW_o; rewritten by
+  // the two RMSNorm backwards), du (dW_1; rewritten by the next layer's
+  // MLP input gradient) and dqkv (dW_qkv; rewritten by the next layer's
+  // attention backward), so the main stream waits for the product that
+  // reads a buffer before it rewrites it.  The split-K workspace is used on
+  // s2 only (after the LM head, which precedes the first fork).
+  hipStream_t s2 = s;
+  if (!pf->on) {
+    TRY(ensure_side(ctx));
+    s2 = ctx->side;
+  }
   for (int l = c.depth - 1; l >= 0; --l) {
+    const bool first = l == c.depth - 1;
     char* L = W + P.layers_base + (size_t)l * P.layer_stride;
     const Desc& dqkv_d = ctx->layout[1 + 4 * l];
     const Desc& do_d = ctx->layout[2 + 4 * l];
@@ -503,16 +558,26 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     // MLP: du = (dx W_2) * 2 relu(u), with relu(u) = sqrt(g); dW_2 = dx^T g; dm = du W_1; dW_1 = du^T m
     // bf16: the product reads W_2 transposed, so that both operands are
     // k-contiguous (the pair loop and its staged ReLU²-backward epilogue)
+    // dW_2 (s2) reads dx_lp as the main stream has it now
+    TRY(order_after(ctx->ev_main, s, s2));
+    GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
+    b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
+    PROF(pf, PC_GEMM, gflops(b2), gbytes(b2), launch_gemm(b2, s2));
+    TRY(mark(ctx->ev_b2, s2, s));
     GemmCall b1 = mk(dx_lp, d, true, W2, F, false, N, F, d, dt);
     if (dt == NC_BF16) {
       TRY(launch_transpose_bf16(W2, d, F, F, W + P.wT, d, s));
       b1 = mk(dx_lp, d, true, W + P.wT, d, true, N, F, d, dt);
     }
     b1.epi = EPI_DRELU2; b1.e.c_lp = W + P.du; b1.e.ld_lp = F; b1.e.aux = L + P.g; b1.e.ld_aux = F;
+    if (!first) TRY(wait_for(ctx->ev_b4, s2, s));  // the previous layer's dW_1 has read du
     PROF(pf, PC_GEMM, gflops(b1), gbytes(b1), launch_gemm(b1, s));
-    GemmCall b2 = mk(dx_lp, d, false, L + P.g, F, false, d, F, N, dt);
-    b2.epi = EPI_F32; b2.e.c32 = grads + d2_d.offset; b2.e.ldc = F; b2.e.beta = beta; b2.splitk_ws = splitk; b2.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b2), gbytes(b2), launch_gemm(b2, s));
+    // dW_1 (s2) reads du
+    TRY(order_after(ctx->ev_main, s, s2));
+    GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
+    b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk; b4.splitk_bytes = P.splitk_bytes;
+    PROF(pf, PC_GEMM, gflops(b4), gbytes(b4), launch_gemm(b4, s2));
+    TRY(mark(ctx->ev_b4, s2, s));
     GemmCall b3 = mk(W + P.du, F, true, W1, d, false, N, d, F, dt);
     if (dt == NC_BF16) {
       TRY(launch_transpose_bf16(W1, F, d, d, W + P.wT, F, s));
@@ -520,9 +585,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     }
     dgrad_out(b3);
     PROF(pf, PC_GEMM, gflops(b3), gbytes(b3), launch_gemm(b3, s));
-    GemmCall b4 = mk(W + P.du, F, false, L + P.m, d, false, F, d, N, dt);
-    b4.epi = EPI_F32; b4.e.c32 = grads + d1_d.offset; b4.e.ldc = d; b4.e.beta = beta; b4.splitk_ws = splitk; b4.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b4), gbytes(b4), launch_gemm(b4, s));
+    TRY(wait_for(ctx->ev_b2, s2, s));  // dW_2 has read dx_lp
     TRY(norm_bwd(L + P.m, (float*)(L + P.r2)));
 
     // attention output projection: dO = dx W_o; dW_o = dx^T O
@@ -532,10 +595,13 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
       b5 = mk(dx_lp, d, true, W + P.wT, d, true, N, hh, d, dt);
     }
     b5.epi = EPI_LP; b5.e.c_lp = W + P.dO; b5.e.ld_lp = hh;
-    PROF(pf, PC_GEMM, gflops(b5), gbytes(b5), launch_gemm(b5, s));
+    // dW_o (s2) reads the new dx_lp
+    TRY(order_after(ctx->ev_main, s, s2));
     GemmCall b6 = mk(dx_lp, d, false, L + P.O, hh, false, d, hh, N, dt);
     b6.epi = EPI_F32; b6.e.c32 = grads + do_d.offset; b6.e.ldc = hh; b6.e.beta = beta; b6.splitk_ws = splitk; b6.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b6), gbytes(b6), launch_gemm(b6, s));
+    PROF(pf, PC_GEMM, gflops(b6), gbytes(b6), launch_gemm(b6, s2));
+    TRY(mark(ctx->ev_b6, s2, s));
+    PROF(pf, PC_GEMM, gflops(b5), gbytes(b5), launch_gemm(b5, s));
 
     AttnArgs a;
     a.q = qkv; a.ldq = nq;
@@ -564,6 +630,7 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
       a.dk32 = (float*)(W + P.gq_dk); a.lddk = hh;
       a.dv = W + P.gq_dv; a.lddv = hh;
     }
+    if (!first) TRY(wait_for(ctx->ev_b8, s2, s));  // the previous layer's dW_qkv has read dqkv
     PROF(pf, PC_ATTN_BWD, 8.0 * hd * pairs, 0, launch_attn_bwd(a, hd, dt, s));
     if (a.G > 1)
       PROF(pf, PC_OTHER, 0, (double)N * hh * (4 + es) + (double)N * hk * (4 + es),
@@ -574,7 +641,12 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
                                 (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
                                 hd, c.seq_len, dt, s, Hk, q_fused));
 
-    // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a
+    // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a (s2, reads dqkv)
+    TRY(order_after(ctx->ev_main, s, s2));
+    GemmCall b8 = mk(dqkv, nq, false, L + P.a1, d, false, nq, d, N, dt);
+    b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
+    PROF(pf, PC_GEMM, gflops(b8), gbytes(b8), launch_gemm(b8, s2));
+    TRY(mark(ctx->ev_b8, s2, s));
     GemmCall b7 = mk(dqkv, nq, true, Wqkv, d, false, N, d, nq, dt);
     if (dt == NC_BF16) {
       TRY(launch_transpose_bf16(Wqkv, nq, d, d, W + P.wT, nq, s));
@@ -582,11 +654,13 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     }
     dgrad_out(b7);
     PROF(pf, PC_GEMM, gflops(b7), gbytes(b7), launch_gemm(b7, s));
-    GemmCall b8 = mk(dqkv, nq, false, L + P.a1, d, false, nq, d, N, dt);
-    b8.epi = EPI_F32; b8.e.c32 = grads + dqkv_d.offset; b8.e.ldc = d; b8.e.beta = beta; b8.splitk_ws = splitk; b8.splitk_bytes = P.splitk_bytes;
-    PROF(pf, PC_GEMM, gflops(b8), gbytes(b8), launch_gemm(b8, s));
+    TRY(wait_for(ctx->ev_b6, s2, s));  // dW_o has read dx_lp
     TRY(norm_bwd(L + P.a1, (float*)(L + P.r1)));
   }
+  // every weight gradient is complete before the main stream goes on (the
+  // caller's next work, a next microbatch's forward rewriting the saved
+  // activations they read)
+  TRY(order_after(ctx->ev_all, s2, s));
   PROF(pf, PC_EMB_BWD, 0, (double)N * d * 4 + (double)V * d * 4 * (accumulate ? 2 : 1) + N * 4.0,
        launch_embed_bwd(dx, tokens, grads, N, d, V, accumulate, W + P.embed_ws, s));
   return NC_OK;

@@ -151,6 +151,11 @@ int nc_set_workspace(nc_ctx* ctx, void* dev_ptr, uint64_t bytes);
  *             accumulate = 0 overwrites it, accumulate = 1 adds to it.
  * Saved activations live in the workspace, which must hold
  * nc_workspace_bytes(ctx, batch) bytes.  Not re-entrant: one context per stream.
+ * The backward runs its weight-gradient products on a second stream that
+ * the context creates on first use (default priority, ordered against the
+ * context's stream by events; the context's stream waits for it before the
+ * call returns), so the results are ordered on the context's stream as
+ * usual.  NC_ERR_HIP if that stream or its events cannot be created.
  */
 int nc_forward_backward(nc_ctx* ctx, const void* params, const int32_t* tokens,
                         const int32_t* targets, int batch, float* loss,
