@@ -13,17 +13,21 @@
 // with the partner lane (lane ^ 32).  Scores are computed transposed
 // (S^T = K Q^T, A operand from an LDS K tile, B operand = Q held in
 // registers) and the output as O^T = V^T P^T, whose B operand is exactly the
-// score accumulator converted to bf16; V^T comes from an LDS tile that is
-// transposed in registers while it is staged.  The key order inside one MFMA
+// score accumulator converted to bf16; V^T comes from the row-major V tile
+// through transposed LDS reads (head_dim 128) or from a tile transposed in
+// registers while it is staged (head_dim 64).  The key order inside one MFMA
 // reduction step is permuted identically in both operands, which leaves the
 // sum unchanged.
 //
 // Forward: 128 queries per workgroup (4 wavefronts x 32), 64-key blocks,
-// online softmax in the exp2 domain; lse is saved.  Backward: dK/dV kernel
-// with 128 keys per workgroup looping over 64-query blocks (P recomputed from
-// lse), and a separate dQ kernel with 128 queries per workgroup looping over
-// 64-key blocks; no floating-point atomics, so results are reproducible.
-// Workgroups with the most causal work are launched first.
+// online softmax in the exp2 domain; lse is saved.  Backward, head_dim 128:
+// D = rowsum(dO * O), then a dK/dV kernel (128 keys per workgroup, two
+// wavefronts per 32 keys, looping over 64-query blocks with P recomputed
+// from lse) that also stores -dS, then a dQ kernel from the stored dS (256
+// queries per workgroup); head_dim 64: dK/dV and dQ kernels that each
+// recompute P (128 keys or queries per workgroup).  No floating-point
+// atomics, so results are reproducible.  Workgroups with the most causal
+// work are launched first.
 //
 // fp32 debug path: one wavefront per query (forward, dQ) or per key (dK/dV),
 // plain loops over the causal range.
@@ -736,9 +740,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
 //   the dS wavefront (p + 4) holds -V: its dP accumulator starts at D and
 //     ends at D - dP, -dS = P (D - dP) with the partner's P, dK' += (-dS)^T
 //     qh; it stores -dS for the dQ kernel (lane-major chunks, ds_chunk).
-// Each wavefront keeps one accumulator set (half of the single-wavefront
-// kernel's registers), so two share a SIMD and one's exponentials, products
-// or LDS waits overlap the other's matrix products.
+// Each wavefront keeps one accumulator set (dV or dK, with K or -V: about
+// half of what one wavefront holding both needs), so two share a SIMD and
+// one's exponentials, products or LDS waits overlap the other's matrix
+// products.
 //
 // Blocks of 64 queries (qh, dO tiles; lse, D) stream through three LDS
 // stages; P goes through one of two exchange buffers.  One workgroup barrier
