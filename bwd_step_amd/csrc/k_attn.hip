@@ -751,10 +751,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
 // block j + 1 (into the stage of block j - 2, whose last readers finished
 // before X_{j-1}), then the P wavefront runs S, P (writing P_j) and dV of
 // block j, the dS wavefront dS, dK of block j - 1 (reading P_{j-1}) and dP
-// of block j.  At X_j each wavefront has waited for its own
-// loads of block j + 1, so after it the whole block is in LDS; exchange
-// buffer j & 1 is rewritten two blocks later, after every reader of P_j
-// passed X_{j+1}.
+// of block j.  At X_j each wavefront has waited for its own loads of block
+// j + 1, so after it the whole block is in LDS; exchange buffer j & 1 is
+// rewritten two blocks later, after every reader of P_j passed X_{j+1}.
 //
 // LDS (bytes): qh tiles of the three stages [0, 48K), dO tiles [48K, 96K)
 // (64 rows x 256 bytes, sw2 chunk swizzle), the lse and D vectors of stage st
