@@ -80,6 +80,19 @@ def model_flops_per_token(c):
     return mat + att
 
 
+def palm_flops_per_token(c):
+    """The same FLOPs in the convention of the PaLM paper's MFU (Chowdhery et
+    al., 2022, appendix B), used by many training reports: 6 N for the
+    matmul parameters N (every weight but the token embedding) plus 12 * L *
+    H * hd * T for attention, i.e. every query against all T keys, with no
+    causal halving.  Reported beside the causal count, never in its place."""
+    d, H, hd, F = c["d_model"], c["n_heads"], c["head_dim"], c["d_ff"]
+    V, L, T = c["vocab"], c["depth"], c["seq_len"]
+    hh = H * hd
+    n_mat = L * (3 * hh * d + d * hh + 2 * F * d) + V * d
+    return 6.0 * n_mat + 12.0 * L * H * hd * T
+
+
 def cpu_baseline(c, seed=0):
     """Time the float64 oracle on this host on a bounded sample of the workload.
 
@@ -396,6 +409,8 @@ def main():
         },
         "mfu": round(mfu, 4),
         "model_flops_per_token": fpt,
+        "mfu_palm_convention": round(tok_s * palm_flops_per_token(cfg) / PEAK_BF16_FLOPS, 4),
+        "palm_flops_per_token": palm_flops_per_token(cfg),
         "loss": round(loss.item(), 5),
         "roofline": {
             "kernel": "gemm_mfma_kernel (all GEMM launches of the step, incl. split-K reduce)",

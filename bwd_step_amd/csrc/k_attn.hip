@@ -23,8 +23,8 @@
 // online softmax in the exp2 domain; lse is saved.  Backward, head_dim 128:
 // D = rowsum(dO * O), then a dK/dV kernel (128 keys per workgroup, two
 // wavefronts per 32 keys, looping over 64-query blocks with P recomputed
-// from lse) that also stores -dS, then a dQ kernel from the stored dS (256
-// queries per workgroup); head_dim 64: dK/dV and dQ kernels that each
+// from lse) that also stores -dS, then a dQ kernel from the stored dS (two
+// 256-query tiles per workgroup); head_dim 64: dK/dV and dQ kernels that each
 // recompute P (128 keys or queries per workgroup).  No floating-point
 // atomics, so results are reproducible.  Workgroups with the most causal
 // work are launched first.
@@ -299,6 +299,20 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
       : "memory");
 }
 
+// The same load with the non-temporal policy (data read once, streamed).
+__device__ __forceinline__ void dma16_nt(rsrc_t rs, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+
 // The stored dS of one (b, h), lane-major.  The dK/dV kernel holds -dS^T
 // of 32 keys (a key block kw) x 32 queries (a query block qw) in one
 // wavefront as two B-operand fragments per lane: fragment t of lane
@@ -551,12 +565,15 @@ __global__ void __launch_bounds__(256) attn_bwd_D128(AttnArgs p) {
 // comes from the dS chunks with ds_read_b64_tr_b16 (ds_frag).  The dK/dV
 // kernel stored every chunk of its 128 keys from their first query on
 // (zeros above the diagonal and past T), so no mask is needed; a wavefront
-// only skips the key blocks past its last query.  256 queries per workgroup (8 wavefronts of
-// 32, two per SIMD), 64-key blocks through three LDS stages (a K tile, 64
-// rows x 256 bytes with the sw2 swizzle, and the 32 dS chunks of 64 keys x
-// 256 queries; 48 KB each), loaded two blocks ahead.  The kernel streams
-// the stored dS once and re-reads K once per 256 queries.  Its epilogue also runs the QK-norm +
-// RoPE backward of q, so it writes the gradient w.r.t. the pre-norm q.
+// only skips the key blocks past its last query.  Tiles of 256 queries (8
+// wavefronts of 32, two per SIMD), 64-key blocks through three LDS stages (a
+// K tile, 64 rows x 256 bytes with the sw2 swizzle, and the 32 dS chunks of
+// 64 keys x 256 queries; 48 KB each), loaded two blocks ahead.  A workgroup
+// runs two tiles of one (b, h), i and n - 1 - i, so all workgroups have equal
+// work and those of one (b, h) read the same K blocks together from their
+// XCD's L2; the stored dS, read once, is loaded with the non-temporal
+// policy.  The epilogue of each tile also runs the QK-norm + RoPE backward
+// of q, so it writes the gradient w.r.t. the pre-norm q.
 //
 // In LDS the chunks are ordered (kw, qw, t) within the tile and the 16-byte
 // piece of chunk lane li + 32 g sits at slot 32 g + (li ^ (4 g + 8 t)): the
@@ -579,6 +596,7 @@ __device__ __forceinline__ bf16x8 ds_frag(const bf16* S, int qwl, int kb, int la
 }
 
 constexpr int kDqQueries = 256;  // queries per workgroup of the dQ kernel
+constexpr bool kDqDsNt = true;    // stored dS read with the non-temporal policy
 
 __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
   constexpr int HD = 128, HB = 4, QW = kDqQueries / 32;
@@ -588,22 +606,23 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
 
   const int T = p.T;
   const long Tp = p.tpad;
-  const int nqb = gridDim.x;
-  const int lin = xcd_block(blockIdx.x + nqb * blockIdx.y, nqb * gridDim.y);
-  const int qb = nqb - 1 - lin % nqb;  // query blocks of one (b, h) in turn, the longest first
-  const int bh = lin / nqb, b = bh / p.H, h = bh % p.H;
+  // Workgroup pi of a (b, h) takes query tiles ntile - 1 - pi and pi (the
+  // longer first), so every workgroup has the same number of key blocks and
+  // the workgroups of one (b, h), started together on one XCD, walk the same
+  // K blocks at the same time (shared in its L2).
+  const int ntile = (T + kDqQueries - 1) / kDqQueries;
+  const int npg = gridDim.x;  // (ntile + 1) / 2
+  const int lin = xcd_block(blockIdx.x + npg * blockIdx.y, npg * gridDim.y);
+  const int pi = lin % npg;
+  const int bh = lin / npg, b = bh / p.H, h = bh % p.H;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;
-  const int q0 = qb * kDqQueries;
-  const int qi = q0 + wv * 32 + (lane & 31);  // this lane's query
-
   const size_t tok0 = (size_t)b * T;
   const rsrc_t rk = make_rsrc((const bf16*)p.k + tok0 * p.ldk,
                               (uint32_t)(((size_t)(T - 1) * p.ldk + (size_t)(p.H / p.G) * HD) * 2));
   const rsrc_t rs = make_rsrc((const bf16*)p.dsT + (size_t)bh * Tp * Tp, (uint32_t)(Tp * Tp * 2));
   const long col = (long)(h / p.G) * HD;  // this query head's key/value head
-  const int nkv = min(T - 1, q0 + kDqQueries - 1) / 64 + 1;  // key blocks up to the diagonal
 
   // K tile: per-lane byte offsets of this wavefront's 2 blocks (4 rows each)
   // relative to the key block's first row.  dS: this wavefront loads chunks
@@ -618,117 +637,130 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
   }
   const uint32_t src_lane[2] = {(uint32_t)((((lane & 31) ^ (4 * g)) + 32 * g) * 16),
                                  (uint32_t)((((lane & 31) ^ (4 * g + 8)) + 32 * g) * 16)};
-  // the loads of key block j into stage st; blocks past the last read 0
-  auto load_block = [&](int st, int j) {
-    const bool live = j < nkv;
-    const int row0 = j * 64;
-    const uint32_t sb = lds0 + (uint32_t)st * kStage;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = live && row0 + (wv * 2 + i) * 4 + (lane >> 4) < T;  // keys past T read 0
-      dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 2 + i) * 1024u);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qb = pass == 0 ? ntile - 1 - pi : pi;
+    if (pass == 1) {
+      if (qb == ntile - 1 - pi) break;  // the middle tile of an odd count runs once
+      // every wavefront is done with the last stage of the first tile
+      __syncthreads();
     }
+    const int q0 = qb * kDqQueries;
+    const int qi = q0 + wv * 32 + (lane & 31);  // this lane's query
+    const int nkv = min(T - 1, q0 + kDqQueries - 1) / 64 + 1;  // key blocks up to the diagonal
+    // the loads of key block j into stage st; blocks past the last read 0
+    auto load_block = [&](int st, int j) {
+      const bool live = j < nkv;
+      const int row0 = j * 64;
+      const uint32_t sb = lds0 + (uint32_t)st * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // chunk (kwl, qwl, t) = (c / (2 QW), (c / 2) % QW, c % 2); c % 2 = i % 2.  A
-      // query block past the padded length reads 0 (its queries are past T).
-      const int c = wv * 4 + i;
-      const int qw = (q0 >> 5) + ((c >> 1) % QW);
-      dma16(rs, live && qw < (int)(Tp >> 5) ? src_lane[i & 1] + ds_chunk(Tp, 2 * j + c / (2 * QW), qw, c & 1) : kOOB,
-            sb + kTile + (uint32_t)c * 1024u);
+      for (int i = 0; i < 2; ++i) {
+        const bool ok = live && row0 + (wv * 2 + i) * 4 + (lane >> 4) < T;  // keys past T read 0
+        dma16(rk, ok ? toff_k[i] + (uint32_t)(row0 * p.ldk * 2) : kOOB, sb + (uint32_t)(wv * 2 + i) * 1024u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // chunk (kwl, qwl, t) = (c / (2 QW), (c / 2) % QW, c % 2); c % 2 = i % 2.  A
+        // query block past the padded length reads 0 (its queries are past T).
+        const int c = wv * 4 + i;
+        const int qw = (q0 >> 5) + ((c >> 1) % QW);
+        const uint32_t off = live && qw < (int)(Tp >> 5) ? src_lane[i & 1] + ds_chunk(Tp, 2 * j + c / (2 * QW), qw, c & 1) : kOOB;
+        if constexpr (kDqDsNt) dma16_nt(rs, off, sb + kTile + (uint32_t)c * 1024u);
+        else dma16(rs, off, sb + kTile + (uint32_t)c * 1024u);
+      }
+    };
+
+    f32x16 dq[HB];
+#pragma unroll
+    for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
+
+    load_block(0, 0);
+    load_block(1, 1);
+    int cur = 0;  // stage of block j
+    for (int j = 0; j < nkv; ++j) {
+      // loads retire in issue order: with those of block j + 1 (6) still in
+      // flight, block j has landed; after the barrier every wavefront is done
+      // with block j - 1, whose stage the loads of block j + 2 take
+      asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+      load_block(cur == 0 ? 2 : cur - 1, j + 2);
+      const char* sb = smem + cur * kStage;
+      cur = cur == 2 ? 0 : cur + 1;
+      const bf16* Ks = (const bf16*)sb;
+      const bf16* Ss = (const bf16*)(sb + kTile);
+      // a key block wholly past this wavefront's last query adds nothing, and
+      // its chunks were never stored (the dK/dV workgroup of those keys starts
+      // at a later query): skip it
+      if (64 * j > q0 + 32 * wv + 31) continue;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 sf = ds_frag<QW>(Ss, wv, kk * 16, lane);
+#pragma unroll
+        for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 16, lane), sf, dq[x]);
+      }
     }
-  };
+    wait_vmem();
 
-  f32x16 dq[HB];
+    // QK-norm + RoPE backward of this lane's query, head h: with dqh the
+    // gradient w.r.t. qh = R_t rho(q) and y = R_t^T qh = rho(q), the gradient
+    // w.r.t. q is r (dy - y mean(dy y)), dy = R_t^T dqh.  Lanes l and l ^ 32
+    // hold the two halves of the head row: element 32 x + 8 rg + 4 g + e is
+    // dq[x][4 rg + e], so the pair (i, i + 64) is (x, x + 2) of one lane and
+    // only the mean needs the partner lane.
+    const bool live = qi < T;
+    const float sc = -p.scale;  // the stored matrix is -dS
+    const size_t n = tok0 + (live ? qi : 0);
+    const int t = live ? qi : 0;
+    const bf16* vrow = (const bf16*)p.q + n * p.ldq + h * HD;
+    // dq[x] becomes dy of elements i (x < 2) and i + 64 (dq[x + 2]); ylo / yhi
+    // hold y of the same elements
+    f32x16 ylo[2], yhi[2];
+    float dot = 0.f;
 #pragma unroll
-  for (int x = 0; x < HB; ++x) dq[x] = f32x16{};
-
-  load_block(0, 0);
-  load_block(1, 1);
-  int cur = 0;  // stage of block j
-  for (int j = 0; j < nkv; ++j) {
-    // loads retire in issue order: with those of block j + 1 (6) still in
-    // flight, block j has landed; after the barrier every wavefront is done
-    // with block j - 1, whose stage the loads of block j + 2 take
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-    load_block(cur == 0 ? 2 : cur - 1, j + 2);
-    const char* sb = smem + cur * kStage;
-    cur = cur == 2 ? 0 : cur + 1;
-    const bf16* Ks = (const bf16*)sb;
-    const bf16* Ss = (const bf16*)(sb + kTile);
-    // a key block wholly past this wavefront's last query adds nothing, and
-    // its chunks were never stored (the dK/dV workgroup of those keys starts
-    // at a later query): skip it
-    if (64 * j > q0 + 32 * wv + 31) continue;
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 sf = ds_frag<QW>(Ss, wv, kk * 16, lane);
+      for (int rg = 0; rg < 4; ++rg) {
+        const int i = 32 * x + 8 * rg + 4 * g;  // pairs i .. i + 3
+        const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
+        const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
+        const f32x4 cv{c01.x, c01.z, c23.x, c23.z}, sv{c01.y, c01.w, c23.y, c23.w};
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + i);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + i + 64);
+        const f32x4 v0{bf16lo_to_f32(a0.x), bf16hi_to_f32(a0.x), bf16lo_to_f32(a0.y), bf16hi_to_f32(a0.y)};
+        const f32x4 v1{bf16lo_to_f32(a1.x), bf16hi_to_f32(a1.x), bf16lo_to_f32(a1.y), bf16hi_to_f32(a1.y)};
 #pragma unroll
-      for (int x = 0; x < HB; ++x) dq[x] = mfma(tr_frag(Ks, x, kk * 16, lane), sf, dq[x]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          const float g0 = dq[x][r] * sc, g1 = dq[x + 2][r] * sc;
+          const float d0 = g0 * cv[e] + g1 * sv[e], d1 = g1 * cv[e] - g0 * sv[e];
+          const float y0 = v0[e] * cv[e] + v1[e] * sv[e], y1 = v1[e] * cv[e] - v0[e] * sv[e];
+          dq[x][r] = d0;
+          dq[x + 2][r] = d1;
+          ylo[x][r] = y0;
+          yhi[x][r] = y1;
+          dot = fmaf(d0, y0, fmaf(d1, y1, dot));
+        }
+      }
+    dot += __shfl_xor(dot, 32, 64);
+    dot *= 1.0f / 128.0f;
+    if (live) {
+      const float rr = p.rq[n * p.H + h];
+      bf16* out = (bf16*)p.dq_pre + n * p.lddq_pre + h * HD;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int i = 32 * x + 8 * rg + 4 * g;
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            lo[e] = (dq[x][r] - ylo[x][r] * dot) * rr;
+            hi[e] = (dq[x + 2][r] - yhi[x][r] * dot) * rr;
+          }
+          *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w)};
+          *reinterpret_cast<u32x2*>(out + i + 64) = u32x2{pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
+        }
     }
   }
-  wait_vmem();
-
-  // QK-norm + RoPE backward of this lane's query, head h: with dqh the
-  // gradient w.r.t. qh = R_t rho(q) and y = R_t^T qh = rho(q), the gradient
-  // w.r.t. q is r (dy - y mean(dy y)), dy = R_t^T dqh.  Lanes l and l ^ 32
-  // hold the two halves of the head row: element 32 x + 8 rg + 4 g + e is
-  // dq[x][4 rg + e], so the pair (i, i + 64) is (x, x + 2) of one lane and
-  // only the mean needs the partner lane.
-  const bool live = qi < T;
-  const float sc = -p.scale;  // the stored matrix is -dS
-  const size_t n = tok0 + (live ? qi : 0);
-  const int t = live ? qi : 0;
-  const bf16* vrow = (const bf16*)p.q + n * p.ldq + h * HD;
-  // dq[x] becomes dy of elements i (x < 2) and i + 64 (dq[x + 2]); ylo / yhi
-  // hold y of the same elements
-  f32x16 ylo[2], yhi[2];
-  float dot = 0.f;
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int i = 32 * x + 8 * rg + 4 * g;  // pairs i .. i + 3
-      const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
-      const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
-      const f32x4 cv{c01.x, c01.z, c23.x, c23.z}, sv{c01.y, c01.w, c23.y, c23.w};
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + i);
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + i + 64);
-      const f32x4 v0{bf16lo_to_f32(a0.x), bf16hi_to_f32(a0.x), bf16lo_to_f32(a0.y), bf16hi_to_f32(a0.y)};
-      const f32x4 v1{bf16lo_to_f32(a1.x), bf16hi_to_f32(a1.x), bf16lo_to_f32(a1.y), bf16hi_to_f32(a1.y)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rg + e;
-        const float g0 = dq[x][r] * sc, g1 = dq[x + 2][r] * sc;
-        const float d0 = g0 * cv[e] + g1 * sv[e], d1 = g1 * cv[e] - g0 * sv[e];
-        const float y0 = v0[e] * cv[e] + v1[e] * sv[e], y1 = v1[e] * cv[e] - v0[e] * sv[e];
-        dq[x][r] = d0;
-        dq[x + 2][r] = d1;
-        ylo[x][r] = y0;
-        yhi[x][r] = y1;
-        dot = fmaf(d0, y0, fmaf(d1, y1, dot));
-      }
-    }
-  dot += __shfl_xor(dot, 32, 64);
-  dot *= 1.0f / 128.0f;
-  if (!live) return;
-  const float rr = p.rq[n * p.H + h];
-  bf16* out = (bf16*)p.dq_pre + n * p.lddq_pre + h * HD;
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int i = 32 * x + 8 * rg + 4 * g;
-      f32x4 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rg + e;
-        lo[e] = (dq[x][r] - ylo[x][r] * dot) * rr;
-        hi[e] = (dq[x + 2][r] - yhi[x][r] * dot) * rr;
-      }
-      *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w)};
-      *reinterpret_cast<u32x2*>(out + i + 64) = u32x2{pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
-    }
 }
 
 // dK, dV with two wavefronts per 32 keys: 512 threads, 128 keys per
@@ -1455,7 +1487,7 @@ int launch_attn_bwd(AttnArgs p, int hd, int dtype, hipStream_t s) {
       if (p.tpad > kMaxDsPad) return NC_ERR_UNSUPPORTED;  // one (b, h) block of dS must stay below 2 GiB
       attn_bwd_D128<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(p);
       attn_bwd_dkdv_pair128<<<gk, 512, 0, s>>>(p);
-      attn_bwd_dq_ds128<<<dim3((p.T + kDqQueries - 1) / kDqQueries, p.B * p.H), 512, 0, s>>>(p);
+      attn_bwd_dq_ds128<<<dim3(((p.T + kDqQueries - 1) / kDqQueries + 1) / 2, p.B * p.H), 512, 0, s>>>(p);
     } else if (hd == 64) {
       attn_bwd_pre<bf16><<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(p, hd);
       attn_bwd_dkdv_mfma<64><<<gk, 256, 0, s>>>(p);
