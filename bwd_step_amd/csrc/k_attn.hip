@@ -1094,6 +1094,17 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
     wait_vmem();
     if (kj >= T) return;
     const float sc = -p.scale;  // dK' = -dK
+    if (p.dk_lp) {
+      bf16* dkp = (bf16*)p.dk_lp + (tok0 + kj) * p.lddk_lp + h * HD;
+#pragma unroll
+      for (int x = 0; x < HB; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          *reinterpret_cast<u32x2*>(dkp + x * 32 + 8 * rg + 4 * g) =
+              u32x2{pack_bf16x2(dk[x][rg * 4 + 0] * sc, dk[x][rg * 4 + 1] * sc),
+                    pack_bf16x2(dk[x][rg * 4 + 2] * sc, dk[x][rg * 4 + 3] * sc)};
+      return;
+    }
     float* dkp = p.dk32 + (tok0 + kj) * p.lddk + h * HD;
 #pragma unroll
     for (int x = 0; x < HB; ++x)
