@@ -23,8 +23,9 @@
 // online softmax in the exp2 domain; lse is saved.  Backward, head_dim 128:
 // D = rowsum(dO * O), then a dK/dV kernel (128 keys per workgroup, two
 // wavefronts per 32 keys, looping over 64-query blocks with P recomputed
-// from lse) that also stores -dS, then a dQ kernel from the stored dS (two
-// 256-query tiles per workgroup); head_dim 64: dK/dV and dQ kernels that each
+// from lse) that also stores -dS and finishes the QK-norm + RoPE backward of
+// k, then a dQ kernel from the stored dS (two 256-query tiles per workgroup)
+// that finishes that of q; head_dim 64: dK/dV and dQ kernels that each
 // recompute P (128 keys or queries per workgroup).  No floating-point
 // atomics, so results are reproducible.  Workgroups with the most causal
 // work are launched first.
@@ -787,6 +788,12 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_ds128(AttnArgs p) {
 // j + 1, so after it the whole block is in LDS; exchange buffer j & 1 is
 // rewritten two blocks later, after every reader of P_j passed X_{j+1}.
 //
+// With dk_lp and rk (bf16, no key groups) the dS wavefront ends with the
+// QK-norm + RoPE backward of its keys: after the last block the P wavefront
+// writes K (kh) into the exchange buffers, now free, and the dS wavefront
+// rotates dkh and kh back, forms the norm backward with its partner lane
+// and writes the gradient w.r.t. the pre-norm k.
+//
 // LDS (bytes): qh tiles of the three stages [0, 48K), dO tiles [48K, 96K)
 // (64 rows x 256 bytes, sw2 chunk swizzle), the lse and D vectors of stage st
 // at 96K + 2K st and 1K beyond, the exchange buffers from 102K (buffer x,
@@ -828,6 +835,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
   const int qb0 = k0 / 64;
   const int nb = (T + 63) / 64 - qb0;  // query blocks at or after the diagonal
   const float c = p.scale_log2;
+  // the dS wavefront also finishes the QK-norm + RoPE backward of k
+  const bool k_fused = p.dk_lp && p.rk && p.cs && p.G == 1;
 
   // this wavefront's loads of a block: slots wv and wv + 8 (4 rows each) of
   // the qh and dO tiles; wavefronts 0 and 1 also load a vector
@@ -993,6 +1002,16 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
     // the dS wavefront's last block (no loads: those of block nb + 1 read 0)
     load_block(j + 1);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (k_fused) {
+      // K for the dS partner's QK-norm + RoPE backward, through the exchange
+      // buffers (read for the last time before the barrier above): pair pr,
+      // key row li (256 bytes), 16-byte chunk c of the row at slot c ^ (li & 15)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<bf16x8*>(smem + kPrX + (uint32_t)pr * 8192u + (uint32_t)li * 256u +
+                                   ((uint32_t)((2 * s + g) ^ (li & 15)) << 4)) = kf[s];
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     if (kj >= T) return;
     bf16* dvq = (bf16*)p.dv + (tok0 + kj) * p.lddv + h * HD;
 #pragma unroll
@@ -1092,8 +1111,77 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
     dsk(j - 1);
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     wait_vmem();
-    if (kj >= T) return;
     const float sc = -p.scale;  // dK' = -dK
+    if (k_fused) {
+      // QK-norm + RoPE backward of this lane's key (as the dQ kernel does for
+      // q): with dkh the gradient w.r.t. kh = R_t rho(k) and y = R_t^T kh,
+      // the gradient w.r.t. k is r (dy - y mean(dy y)), dy = R_t^T dkh.
+      // Element 32 x + 8 rg + 4 g + e is dk[x][4 rg + e]; the pair (i, i + 64)
+      // is (x, x + 2) of one lane and the mean needs the partner lane.  kh
+      // comes from the P partner through LDS.
+      const bool live = kj < T;
+      const int t = live ? kj : 0;
+      const float rr = live ? p.rk[(tok0 + t) * p.H + h] : 0.f;
+      f32x4 cv[2][4], sv[2][4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int i = 32 * x + 8 * rg + 4 * g;
+          const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
+          const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
+          cv[x][rg] = f32x4{c01.x, c01.z, c23.x, c23.z};
+          sv[x][rg] = f32x4{c01.y, c01.w, c23.y, c23.w};
+        }
+      asm volatile("s_barrier" ::: "memory");  // the P partner's K is in LDS
+      const char* krow = smem + kPrX + (uint32_t)pr * 8192u + (uint32_t)li * 256u;
+      float dot = 0.f;
+      f32x16 ylo[2], yhi[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int c0 = 4 * x + rg, c1 = 4 * (x + 2) + rg;  // chunks of elements i and i + 64
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(krow + ((uint32_t)(c0 ^ (li & 15)) << 4) + 8 * g);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(krow + ((uint32_t)(c1 ^ (li & 15)) << 4) + 8 * g);
+          const f32x4 v0{bf16lo_to_f32(a0.x), bf16hi_to_f32(a0.x), bf16lo_to_f32(a0.y), bf16hi_to_f32(a0.y)};
+          const f32x4 v1{bf16lo_to_f32(a1.x), bf16hi_to_f32(a1.x), bf16lo_to_f32(a1.y), bf16hi_to_f32(a1.y)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            const float cc = cv[x][rg][e], ss = sv[x][rg][e];
+            const float g0 = dk[x][r] * sc, g1 = dk[x + 2][r] * sc;
+            const float d0 = g0 * cc + g1 * ss, d1 = g1 * cc - g0 * ss;
+            const float y0 = v0[e] * cc + v1[e] * ss, y1 = v1[e] * cc - v0[e] * ss;
+            dk[x][r] = d0;
+            dk[x + 2][r] = d1;
+            ylo[x][r] = y0;
+            yhi[x][r] = y1;
+            dot = fmaf(d0, y0, fmaf(d1, y1, dot));
+          }
+        }
+      dot += __shfl_xor(dot, 32, 64);
+      dot *= 1.0f / 128.0f;
+      if (!live) return;
+      bf16* out = (bf16*)p.dk_lp + (tok0 + kj) * p.lddk_lp + h * HD;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int i = 32 * x + 8 * rg + 4 * g;
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            lo[e] = (dk[x][r] - ylo[x][r] * dot) * rr;
+            hi[e] = (dk[x + 2][r] - yhi[x][r] * dot) * rr;
+          }
+          *reinterpret_cast<u32x2*>(out + i) = u32x2{pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w)};
+          *reinterpret_cast<u32x2*>(out + i + 64) = u32x2{pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)};
+        }
+      return;
+    }
+    if (kj >= T) return;
     if (p.dk_lp) {
       bf16* dkp = (bf16*)p.dk_lp + (tok0 + kj) * p.lddk_lp + h * HD;
 #pragma unroll

@@ -374,12 +374,11 @@ __global__ void __launch_bounds__(256) qknorm_rope_fwd16_kernel(QkArgs a, const 
   if (i == 0) a.r[w][vec] = rr;
 }
 
-// Backward: dv (gradient w.r.t. the rotated normalised vector, fp32 or, for
-// TG = bf16, bf16), v the saved rotated normalised vector, r its saved 1/rms.
-// du = r (dy - y mean(dy y)) with dy = R^T dv and y = R^T v.  du may be dv
-// itself (bf16): each lane reads its elements before it writes them.
+// Backward: dv (fp32, gradient w.r.t. the rotated normalised vector), v the
+// saved rotated normalised vector, r its saved 1/rms.  du = r (dy - y mean(dy y))
+// with dy = R^T dv and y = R^T v.
 struct QkBwdArgs {
-  const void* dv[2];
+  const float* dv[2];
   int ld_dv[2];
   const void* v[2];
   int ld_v[2];
@@ -389,7 +388,7 @@ struct QkBwdArgs {
   int heads[2];
 };
 
-template <class T, int HALF, class TG = float>
+template <class T, int HALF>
 __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const float* __restrict__ cs, int N,
                                                               int H, int Tseq, int w0) {
   constexpr int LPV = QkLanes<HALF>::LPV, VPW = QkLanes<HALF>::VPW;
@@ -404,11 +403,11 @@ __global__ void __launch_bounds__(256) qknorm_rope_bwd_kernel(QkBwdArgs a, const
   const f32x4* csp = reinterpret_cast<const f32x4*>(cs + 2 * (t * HALF + i));
   const f32x4 cs01 = csp[0], cs23 = csp[1];
   const f32x4 c{cs01.x, cs01.z, cs23.x, cs23.z}, sn{cs01.y, cs01.w, cs23.y, cs23.w};
-  const TG* gp = (const TG*)a.dv[w] + (size_t)n * a.ld_dv[w] + h * (2 * HALF);
+  const float* gp = a.dv[w] + (size_t)n * a.ld_dv[w] + h * (2 * HALF);
   const T* vv = (const T*)a.v[w] + (size_t)n * a.ld_v[w] + h * (2 * HALF);
   const f32x4 z{0.f, 0.f, 0.f, 0.f};
-  const f32x4 g0 = ok ? load4(gp + i) : z;
-  const f32x4 g1 = ok ? load4(gp + i + HALF) : z;
+  const f32x4 g0 = ok ? *reinterpret_cast<const f32x4*>(gp + i) : z;
+  const f32x4 g1 = ok ? *reinterpret_cast<const f32x4*>(gp + i + HALF) : z;
   const f32x4 v0 = ok ? load4(vv + i) : z, v1 = ok ? load4(vv + i + HALF) : z;
   // R^T: rotation by -phi
   const f32x4 dy0 = g0 * c + g1 * sn, dy1 = g1 * c - g0 * sn;
@@ -454,7 +453,7 @@ static int qk_fwd_dispatch(const QkArgs& a, const float* cs, int N, int H, int h
   return 0;
 }
 
-template <class T, class TG = float>
+template <class T>
 static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, int hd, int Tseq, hipStream_t s,
                            bool k_only) {
   const int vecs = N * (k_only ? a.heads[1] : H);
@@ -464,10 +463,10 @@ static int qk_bwd_dispatch(const QkBwdArgs& a, const float* cs, int N, int H, in
   dim3 grid((vecs + vpb - 1) / vpb, k_only ? 1 : 2);
   const int w0 = k_only ? 1 : 0;
   switch (half) {
-    case 64: qknorm_rope_bwd_kernel<T, 64, TG><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
-    case 32: qknorm_rope_bwd_kernel<T, 32, TG><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
-    case 16: qknorm_rope_bwd_kernel<T, 16, TG><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
-    case 8: qknorm_rope_bwd_kernel<T, 8, TG><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 64: qknorm_rope_bwd_kernel<T, 64><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 32: qknorm_rope_bwd_kernel<T, 32><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 16: qknorm_rope_bwd_kernel<T, 16><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
+    case 8: qknorm_rope_bwd_kernel<T, 8><<<grid, 256, 0, s>>>(a, cs, N, H, Tseq, w0); break;
     default: return 7;
   }
   NC_LAUNCH_CHECK();
@@ -488,10 +487,10 @@ int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int l
                     : qk_fwd_dispatch<float>(a, cs, N, H, hd, T, eps, s);
 }
 
-int launch_qknorm_rope_bwd(const float* dq, int lddq, const void* dk, int lddk, const void* qh, int ldq,
+int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s, int Hk, bool k_only, bool dk_bf16) {
+                           hipStream_t s, int Hk, bool k_only) {
   QkBwdArgs a;
   a.heads[0] = H; a.heads[1] = Hk > 0 ? Hk : H;
   a.dv[0] = dq; a.dv[1] = dk;
@@ -501,11 +500,6 @@ int launch_qknorm_rope_bwd(const float* dq, int lddq, const void* dk, int lddk, 
   a.r[0] = rq; a.r[1] = rk;
   a.du[0] = dq_out; a.du[1] = dk_out;
   a.ld_du[0] = ldq_out; a.ld_du[1] = ldk_out;
-  if (dk_bf16) {
-    // the k gradient in bf16 (written so by the attention backward): k only
-    if (dtype != 0 || !k_only) return NC_ERR_UNSUPPORTED;
-    return qk_bwd_dispatch<bf16, bf16>(a, cs, N, H, hd, T, s, k_only);
-  }
   return dtype == 0 ? qk_bwd_dispatch<bf16>(a, cs, N, H, hd, T, s, k_only)
                     : qk_bwd_dispatch<float>(a, cs, N, H, hd, T, s, k_only);
 }

@@ -72,12 +72,11 @@ int launch_rope_table(float* cs, int T, int hd, float base, hipStream_t s);
 int launch_qknorm_rope_fwd(const void* q_in, int ldq_in, const void* k_in, int ldk_in, void* q_out, int ldq_out,
                            void* k_out, int ldk_out, float* rq, float* rk, const float* cs, int N, int H, int hd,
                            int T, float eps, int dtype, hipStream_t s, int Hk = 0);
-// k_only: only the k tensor (the q part was finished by the attention backward);
-// dk_bf16 (with k_only, bf16): dk is bf16, and dk_out may be dk itself
-int launch_qknorm_rope_bwd(const float* dq, int lddq, const void* dk, int lddk, const void* qh, int ldq,
+// k_only: only the k tensor (the q part was finished by the attention backward)
+int launch_qknorm_rope_bwd(const float* dq, int lddq, const float* dk, int lddk, const void* qh, int ldq,
                            const void* kh, int ldk, const float* rq, const float* rk, void* dq_out, int ldq_out,
                            void* dk_out, int ldk_out, const float* cs, int N, int H, int hd, int T, int dtype,
-                           hipStream_t s, int Hk = 0, bool k_only = false, bool dk_bf16 = false);
+                           hipStream_t s, int Hk = 0, bool k_only = false);
 
 // ---- embedding
 int launch_embed_fwd(const void* E, const int32_t* tok, float* x, int N, int d, int V, int dtype, int* status,
@@ -113,8 +112,11 @@ struct AttnArgs {
   const float* rq = nullptr;
   const float* cs = nullptr;
   // bf16, head_dim 128: the dK/dV kernel writes dk (w.r.t. the rotated k)
-  // in bf16 here instead of dk32
+  // in bf16 here instead of dk32; with rk as well (1/rms of k [N][H], no
+  // key groups) it finishes the QK-norm + RoPE backward of k itself and
+  // writes the gradient w.r.t. the pre-norm k there (cs as for q)
   void* dk_lp = nullptr; long lddk_lp = 0;
+  const float* rk = nullptr;
 };
 // Rows (and columns) of each (b, h) block of the stored dS: T rounded up to
 // 128.  A block is addressed through one buffer resource (32-bit offsets), so

@@ -613,7 +613,8 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     a.Dbuf = (float*)(W + P.Dbuf);
     a.dsT = W + P.dsT; a.tpad = attn_ds_pad(c.seq_len);
     // bf16, head_dim 128: the dQ kernel finishes q's QK-norm + RoPE backward
-    // and writes dq straight into dqkv; the pass below then handles k only
+    // and writes dq straight into dqkv (the pass below then handles k, unless
+    // the dK/dV kernel does as well)
     const bool q_fused = dt == NC_BF16 && hd == 128;
     if (q_fused) {
       a.dq_pre = dqkv; a.lddq_pre = nq;
@@ -623,12 +624,13 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
     a.dq32 = dqk32; a.lddq = hh + hk;
     a.B = batch; a.H = H; a.T = c.seq_len;
     a.G = H / Hk;
-    // with q finished by the dQ kernel and no key groups, dk goes to the k
-    // columns of dqkv in bf16 and the QK-norm + RoPE backward runs in place
+    // with q finished by the dQ kernel and no key groups, the dK/dV kernel
+    // finishes k's QK-norm + RoPE backward too and writes the gradient w.r.t.
+    // the pre-norm k (bf16) into the k columns of dqkv: no separate pass
     const bool k_lp = q_fused && a.G == 1;
     if (a.G == 1) {
       a.dk32 = dqk32 + hh; a.lddk = hh + hk;
-      if (k_lp) { a.dk_lp = dqkv + hh * es; a.lddk_lp = nq; }
+      if (k_lp) { a.dk_lp = dqkv + hh * es; a.lddk_lp = nq; a.rk = (const float*)(L + P.rk); }
       a.dv = dqkv + (hh + hk) * es; a.lddv = nq;
     } else {  // per query head first, then the sums over each group
       a.dk32 = (float*)(W + P.gq_dk); a.lddk = hh;
@@ -640,11 +642,11 @@ int run_backward(nc_ctx* ctx, const Plan& P, const void* params, const int32_t* 
       PROF(pf, PC_OTHER, 0, (double)N * hh * (4 + es) + (double)N * hk * (4 + es),
            launch_kv_group_sum((float*)(W + P.gq_dk), hh, W + P.gq_dv, hh, dqk32 + hh, hh + hk,
                                dqkv + (hh + hk) * es, nq, N, Hk, a.G, hd, dt, s));
-    PROF(pf, PC_QK_BWD, 0, (double)N * ((q_fused ? 0 : hh) + hk) * ((k_lp ? 2 : 4) + 2 * es) + (double)N * ((q_fused ? 0 : H) + Hk) * 4,
-         launch_qknorm_rope_bwd(dqk32, hh + hk, k_lp ? (const void*)(dqkv + hh * es) : (const void*)(dqk32 + hh),
-                                k_lp ? nq : hh + hk, qkv, nq, qkv + hh * es, nq,
-                                (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
-                                hd, c.seq_len, dt, s, Hk, q_fused, k_lp));
+    if (!k_lp)
+      PROF(pf, PC_QK_BWD, 0, (double)N * ((q_fused ? 0 : hh) + hk) * (4 + 2 * es) + (double)N * ((q_fused ? 0 : H) + Hk) * 4,
+           launch_qknorm_rope_bwd(dqk32, hh + hk, dqk32 + hh, hh + hk, qkv, nq, qkv + hh * es, nq,
+                                  (float*)(L + P.rq), (float*)(L + P.rk), dqkv, nq, dqkv + hh * es, nq, cs, N, H,
+                                  hd, c.seq_len, dt, s, Hk, q_fused));
 
     // QKV projection: da = dqkv W_qkv; dW_qkv = dqkv^T a (s2, reads dqkv)
     TRY(order_after(ctx->ev_main, s, s2));
@@ -1091,15 +1093,15 @@ int nc_attention_fwd_bwd(const void* q, const void* k, const void* v, const void
     a.dq_pre = dq; a.lddq_pre = hh;
     a.rq = (const float*)(w + off[3]);
     a.cs = cs;
-    // dk (w.r.t. the rotated k) in bf16 straight into dk; the QK-norm + RoPE
-    // backward then runs on it in place
+    // and the dK/dV kernel that of k, writing dk w.r.t. the pre-norm k
     a.dk_lp = dk; a.lddk_lp = hh;
+    a.rk = (const float*)(w + off[4]);
   }
   TRY(launch_attn_fwd(a, hd, dtype, s));
   TRY(launch_attn_bwd(a, hd, dtype, s));
-  return launch_qknorm_rope_bwd(a.dq32, hh, q_fused ? (const void*)dk : (const void*)a.dk32, hh, w + off[1], hh,
-                                w + off[2], hh, (float*)(w + off[3]), (float*)(w + off[4]), dq, hh, dk, hh, cs, N, H,
-                                hd, T, dtype, s, 0, q_fused, q_fused);
+  if (q_fused) return NC_OK;
+  return launch_qknorm_rope_bwd(a.dq32, hh, a.dk32, hh, w + off[1], hh, w + off[2], hh, (float*)(w + off[3]),
+                                (float*)(w + off[4]), dq, hh, dk, hh, cs, N, H, hd, T, dtype, s, 0, q_fused);
 }
 
 static size_t ce_ws_parts(int N, int d, int V, int dtype, size_t* off) {
