@@ -1108,6 +1108,26 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
     }
     advance(j);
     load_block(j + 1);
+    // the RoPE-table entries and 1/rms of this lane's key for the fused
+    // QK-norm + RoPE backward below, loaded under the last block's dK product
+    // (the wait after it covers them)
+    const bool live = kj < T;
+    const int t = live ? kj : 0;
+    float rr = 0.f;
+    f32x4 cv[2][4], sv[2][4];
+    if (k_fused) {
+      rr = live ? p.rk[(tok0 + t) * p.H + h] : 0.f;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int i = 32 * x + 8 * rg + 4 * g;
+          const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
+          const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
+          cv[x][rg] = f32x4{c01.x, c01.z, c23.x, c23.z};
+          sv[x][rg] = f32x4{c01.y, c01.w, c23.y, c23.w};
+        }
+    }
     dsk(j - 1);
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     wait_vmem();
@@ -1119,20 +1139,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair128(AttnArgs p) {
       // Element 32 x + 8 rg + 4 g + e is dk[x][4 rg + e]; the pair (i, i + 64)
       // is (x, x + 2) of one lane and the mean needs the partner lane.  kh
       // comes from the P partner through LDS.
-      const bool live = kj < T;
-      const int t = live ? kj : 0;
-      const float rr = live ? p.rk[(tok0 + t) * p.H + h] : 0.f;
-      f32x4 cv[2][4], sv[2][4];
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int i = 32 * x + 8 * rg + 4 * g;
-          const f32x4 c01 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i));
-          const f32x4 c23 = *reinterpret_cast<const f32x4*>(p.cs + 2 * ((size_t)t * 64 + i) + 4);
-          cv[x][rg] = f32x4{c01.x, c01.z, c23.x, c23.z};
-          sv[x][rg] = f32x4{c01.y, c01.w, c23.y, c23.w};
-        }
       asm volatile("s_barrier" ::: "memory");  // the P partner's K is in LDS
       const char* krow = smem + kPrX + (uint32_t)pr * 8192u + (uint32_t)li * 256u;
       float dot = 0.f;
